@@ -1,0 +1,453 @@
+/*
+ * CPU oracle for the CSA2 hierarchical sparse attention step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
+ * HIP path is checked against.  It shares no code, header, table or constant
+ * with the HIP library; only the tests, the smoke check and the benchmark's CPU
+ * baseline may load it.
+ *
+ * Sources (DeepSeek-V4.1-Flash write-ups):
+ *   [P2] fupanwang.com article, section "三个方向一起压小缓存" (the three layer
+ *        modes, the hierarchical sparse indexer and its figure caption, the FP4
+ *        indexer, OCP MXFP4 main KV, FP8 sliding-window KV); section
+ *        "后 20 层干脆共用一份 KV" (128-token sliding window).
+ *   [P3] dreamax.pages.dev notes, CSA2 paragraph (Full / Reindex / Reuse).
+ * Numeric rules the pages leave open are fixed as follows (each is one of the
+ * readings listed in the design notes):
+ *   - indexer score = one 128-d dot product of the FP4 query and key, with each
+ *     32-element block summed exactly (integers in half-units) and the four
+ *     scaled block sums added in fp32 in block order ((v0+v1)+v2)+v3;
+ *   - blocks are 8 aligned positions; a block's score is the maximum over its
+ *     visible positions; blocks and positions rank by (score desc, id asc);
+ *   - the pool keeps min(n_pool, #blocks) blocks; top-k keeps min(k, #pool);
+ *     outputs are ascending and padded with -1;
+ *   - attention: one softmax over the selected latent rows and the window rows,
+ *     value = key, scale sm_scale, computed in double, stored as float.
+ *   - scores compare by their IEEE-754 total order (-0 below +0).
+ *
+ * Pins: every function here is checked in tests/ against brute force, closed
+ * forms, library routines or published format tables (see the test docstrings).
+ */
+#include "csa2_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* O1-O2: E2M1 and E8M0 (OCP Microscaling Formats v1.0)               */
+/* ------------------------------------------------------------------ */
+
+/* E2M1 code -> value.  bit3 sign, bits 2..1 exponent (bias 1), bit0 mantissa. */
+static const double kE2M1[16] = {
+    0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+    -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0};
+
+double orc_e2m1_value(unsigned code) { return kE2M1[code & 15u]; }
+
+/* E2M1 code -> value in half-units (value * 2), an integer in [-12, 12]. */
+static int e2m1_half_units(unsigned code) { return (int)(kE2M1[code & 15u] * 2.0); }
+
+/* E8M0 byte -> 2^(byte-127); 0xFF is NaN. */
+double orc_e8m0_scale(unsigned byte) {
+    if ((byte & 255u) == 255u) return NAN;
+    return ldexp(1.0, (int)(byte & 255u) - 127);
+}
+
+/* FP8 E4M3 (OCP E4M3FN): bias 7, 3 mantissa bits, S.1111.111 is NaN, no inf. */
+double orc_e4m3_value(unsigned code) {
+    code &= 255u;
+    double sign = (code & 0x80u) ? -1.0 : 1.0;
+    unsigned e = (code >> 3) & 15u, m = code & 7u;
+    if (e == 15u && m == 7u) return NAN;
+    if (e == 0u) return sign * ldexp((double)m, -9);          /* subnormal: m/8 * 2^-6 */
+    return sign * ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+}
+
+/* O3: MXFP4 encode of one 32-element block (rule E = floor(log2 amax) - 2). */
+void orc_mxfp4_encode_block(const double* x, uint8_t* codes16, uint8_t* scale) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i)
+        if (fabs(x[i]) > amax) amax = fabs(x[i]);
+    if (amax == 0.0) {
+        for (int i = 0; i < 16; ++i) codes16[i] = 0;
+        *scale = 0;
+        return;
+    }
+    int E = ilogb(amax) - 2;
+    if (E < -127) E = -127;
+    if (E > 127) E = 127;
+    *scale = (uint8_t)(E + 127);
+    for (int i = 0; i < 32; ++i) {
+        double y = x[i] / ldexp(1.0, E);
+        /* nearest of the 8 non-negative E2M1 values; on a tie take the even
+           mantissa (code bit 0 clear); beyond 6 saturate */
+        int best = 0;
+        for (int c = 1; c < 8; ++c) {
+            double dc = fabs(fabs(y) - kE2M1[c]), db = fabs(fabs(y) - kE2M1[best]);
+            if (dc < db || (dc == db && (c % 2) == 0)) best = c;
+        }
+        if (fabs(y) >= 6.0) best = 7;
+        unsigned code = (unsigned)best;
+        if (y < 0.0 && best != 0) code |= 8u;
+        if (i % 2 == 0) codes16[i / 2] = (uint8_t)code;
+        else codes16[i / 2] = (uint8_t)(codes16[i / 2] | (code << 4));
+    }
+}
+
+/* O4: E4M3 encode, round to nearest even over the table of finite values. */
+uint8_t orc_e4m3_encode(double x) {
+    if (isnan(x)) return 0x7F;
+    if (x >= 448.0) return 0x7E;
+    if (x <= -448.0) return 0xFE;
+    int best = -1;
+    double bestd = 0.0;
+    for (int c = 0; c < 256; ++c) {
+        double v = orc_e4m3_value((unsigned)c);
+        if (isnan(v)) continue;
+        if ((signbit(v) != 0) != (signbit(x) != 0)) continue;   /* same sign only */
+        double d = fabs(x - v);
+        if (best < 0 || d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return (uint8_t)best;
+}
+
+/* ------------------------------------------------------------------ */
+/* O5: indexer score                                                  */
+/* ------------------------------------------------------------------ */
+float orc_score(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks) {
+    float v[4];
+    for (int b = 0; b < 4; ++b) {
+        int isum = 0;                                 /* exact, |isum| <= 32*144 */
+        for (int i = 32 * b; i < 32 * b + 32; ++i) {
+            unsigned cq = (i % 2 == 0) ? (qc[i / 2] & 15u) : (qc[i / 2] >> 4);
+            unsigned ck = (i % 2 == 0) ? (kc[i / 2] & 15u) : (kc[i / 2] >> 4);
+            isum += e2m1_half_units(cq) * e2m1_half_units(ck);
+        }
+        /* (hq/2 * 2^(eq-127)) * (hk/2 * 2^(ek-127)) summed = isum * 2^(eq+ek-256) */
+        int e = (int)qs[b] + (int)ks[b] - 256;
+        v[b] = ldexpf((float)isum, e);
+    }
+    volatile float s = v[0] + v[1];
+    s = s + v[2];
+    s = s + v[3];
+    return s;
+}
+
+/* ------------------------------------------------------------------ */
+/* ordering helpers                                                   */
+/* ------------------------------------------------------------------ */
+/* IEEE-754 total order of a float as an unsigned key (larger key = larger). */
+uint32_t orc_order_key(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+typedef struct { uint32_t key; int64_t id; } ranked_t;
+
+/* (key desc, id asc) */
+static int cmp_rank(const void* a, const void* b) {
+    const ranked_t* x = (const ranked_t*)a;
+    const ranked_t* y = (const ranked_t*)b;
+    if (x->key != y->key) return x->key > y->key ? -1 : 1;
+    if (x->id != y->id) return x->id < y->id ? -1 : 1;
+    return 0;
+}
+
+static int cmp_i64(const void* a, const void* b) {
+    int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+    return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+/* Keep the first k of the ranked list, emit their ids ascending, pad with -1. */
+static void emit_first_k_ascending(ranked_t* r, int64_t n, int64_t k, int32_t* out, int64_t out_len) {
+    qsort(r, (size_t)n, sizeof(ranked_t), cmp_rank);
+    int64_t keep = k < n ? k : n;
+    int64_t* ids = (int64_t*)malloc(sizeof(int64_t) * (size_t)(keep > 0 ? keep : 1));
+    for (int64_t i = 0; i < keep; ++i) ids[i] = r[i].id;
+    qsort(ids, (size_t)keep, sizeof(int64_t), cmp_i64);
+    for (int64_t i = 0; i < out_len; ++i) out[i] = i < keep ? (int32_t)ids[i] : -1;
+    free(ids);
+}
+
+/* ------------------------------------------------------------------ */
+/* simple thread pool over rows                                       */
+/* ------------------------------------------------------------------ */
+typedef void (*row_fn)(void* ctx, int64_t row);
+typedef struct { row_fn fn; void* ctx; int64_t n; int64_t next; pthread_mutex_t mu; } pool_t;
+
+static void* pool_worker(void* arg) {
+    pool_t* p = (pool_t*)arg;
+    for (;;) {
+        pthread_mutex_lock(&p->mu);
+        int64_t r = p->next++;
+        pthread_mutex_unlock(&p->mu);
+        if (r >= p->n) break;
+        p->fn(p->ctx, r);
+    }
+    return NULL;
+}
+
+static void parallel_rows(row_fn fn, void* ctx, int64_t n, int threads) {
+    pool_t p;
+    p.fn = fn; p.ctx = ctx; p.n = n; p.next = 0;
+    pthread_mutex_init(&p.mu, NULL);
+    if (threads < 1) threads = 1;
+    if (threads > 256) threads = 256;
+    if (threads > n) threads = (int)(n > 0 ? n : 1);
+    pthread_t tid[256];
+    int started = 0;
+    for (int t = 1; t < threads; ++t)
+        if (pthread_create(&tid[started], NULL, pool_worker, &p) == 0) ++started;
+    pool_worker(&p);
+    for (int t = 0; t < started; ++t) pthread_join(tid[t], NULL);
+    pthread_mutex_destroy(&p.mu);
+}
+
+/* ------------------------------------------------------------------ */
+/* O5-O8: Full layer                                                   */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const uint8_t *qc, *qs, *kc, *ks;
+    const int32_t* n_visible;
+    int M; int64_t N_max; int n_pool; int k;
+    float* scores; float* block_max; int32_t* pool_blocks; int32_t* idx;
+    int64_t nblk_max;
+    int global_topk;
+} full_ctx;
+
+static void full_row(void* vctx, int64_t r) {
+    full_ctx* c = (full_ctx*)vctx;
+    int64_t seq = r / c->M;
+    int64_t nv = c->n_visible[r];
+    const uint8_t* qc = c->qc + r * 64;
+    const uint8_t* qs = c->qs + r * 4;
+    const uint8_t* kc = c->kc + seq * c->N_max * 64;
+    const uint8_t* ks = c->ks + seq * c->N_max * 4;
+    /* O5: every visible position */
+    float* s = (float*)malloc(sizeof(float) * (size_t)(nv > 0 ? nv : 1));
+    for (int64_t j = 0; j < nv; ++j) s[j] = orc_score(qc, qs, kc + j * 64, ks + j * 4);
+    if (c->scores)
+        for (int64_t j = 0; j < nv; ++j) c->scores[r * c->N_max + j] = s[j];
+    /* O6: block b = positions [8b, 8b+8) that are visible; max by total order */
+    int64_t nblk = (nv + 7) / 8;
+    ranked_t* blocks = (ranked_t*)malloc(sizeof(ranked_t) * (size_t)(nblk > 0 ? nblk : 1));
+    for (int64_t b = 0; b < nblk; ++b) {
+        uint32_t best = 0;
+        float bestf = 0.f;
+        for (int64_t j = 8 * b; j < 8 * b + 8 && j < nv; ++j) {
+            if (j == 8 * b || orc_order_key(s[j]) > best) { best = orc_order_key(s[j]); bestf = s[j]; }
+        }
+        blocks[b].key = best;
+        blocks[b].id = b;
+        if (c->block_max) c->block_max[r * c->nblk_max + b] = bestf;
+    }
+    /* O7: pool = first min(n_pool, nblk) blocks by (max desc, id asc) */
+    int32_t* pool = c->pool_blocks + r * c->n_pool;
+    emit_first_k_ascending(blocks, nblk, c->n_pool, pool, c->n_pool);
+    if (c->idx && c->k > 0) {
+        /* O8: top-k over the pool's visible positions by (score desc, pos asc).
+           With global_topk set, rank every visible position instead (the two are
+           equal for a Full layer when the pool keeps >= k blocks). */
+        ranked_t* cand = (ranked_t*)malloc(sizeof(ranked_t) * (size_t)(nv > 0 ? nv : 1));
+        int64_t nc = 0;
+        if (c->global_topk) {
+            for (int64_t j = 0; j < nv; ++j) { cand[nc].key = orc_order_key(s[j]); cand[nc].id = j; ++nc; }
+        } else {
+            for (int i = 0; i < c->n_pool; ++i) {
+                if (pool[i] < 0) continue;
+                for (int64_t j = 8 * (int64_t)pool[i]; j < 8 * (int64_t)pool[i] + 8 && j < nv; ++j) {
+                    cand[nc].key = orc_order_key(s[j]);
+                    cand[nc].id = j;
+                    ++nc;
+                }
+            }
+        }
+        emit_first_k_ascending(cand, nc, c->k, c->idx + r * c->k, c->k);
+        free(cand);
+    }
+    free(blocks);
+    free(s);
+}
+
+int orc_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                   const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
+                   int n_pool, int k, float* scores, float* block_max, int32_t* pool_blocks,
+                   int32_t* idx, int global_topk, int threads) {
+    if (B < 0 || M < 0 || N_max < 0 || n_pool < 0 || k < 0 || !pool_blocks) return -1;
+    for (int64_t r = 0; r < (int64_t)B * M; ++r)
+        if (n_visible[r] < 0 || n_visible[r] > N_max) return -1;
+    full_ctx c = {q_codes, q_scales, k_codes, k_scales, n_visible, M, N_max, n_pool, k,
+                  scores, block_max, pool_blocks, idx, (N_max + 7) / 8, global_topk};
+    parallel_rows(full_row, &c, (int64_t)B * M, threads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O9: Reindex - score only the pool's positions                      */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const uint8_t *qc, *qs, *kc, *ks;
+    const int32_t *pool_blocks, *n_visible;
+    int n_pool, M; int64_t N_max;
+    float* pool_scores;
+} pool_ctx;
+
+static void pool_row(void* vctx, int64_t r) {
+    pool_ctx* c = (pool_ctx*)vctx;
+    int64_t seq = r / c->M;
+    int64_t nv = c->n_visible[r];
+    for (int i = 0; i < c->n_pool; ++i) {
+        int64_t b = c->pool_blocks[r * c->n_pool + i];
+        for (int t = 0; t < 8; ++t) {
+            int64_t j = 8 * b + t;
+            float v = -INFINITY;
+            if (b >= 0 && j < nv)
+                v = orc_score(c->qc + r * 64, c->qs + r * 4, c->kc + (seq * c->N_max + j) * 64,
+                              c->ks + (seq * c->N_max + j) * 4);
+            c->pool_scores[(r * c->n_pool + i) * 8 + t] = v;
+        }
+    }
+}
+
+int orc_index_pool(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                   const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool,
+                   const int32_t* n_visible, int B, int M, int64_t N_max, float* pool_scores, int threads) {
+    if (B < 0 || M < 0 || n_pool < 0) return -1;
+    pool_ctx c = {q_codes, q_scales, k_codes, k_scales, pool_blocks, n_visible, n_pool, M, N_max, pool_scores};
+    parallel_rows(pool_row, &c, (int64_t)B * M, threads);
+    return 0;
+}
+
+/* O8 over a pool-score array: slot 8i+t is position 8*pool[i]+t when pool[i]
+   >= 0 and the position is visible. */
+typedef struct {
+    const float* pool_scores; const int32_t* pool_blocks; const int32_t* n_visible;
+    int n_pool, k; int32_t* idx;
+} topk_ctx;
+
+static void topk_row(void* vctx, int64_t r) {
+    topk_ctx* c = (topk_ctx*)vctx;
+    ranked_t* cand = (ranked_t*)malloc(sizeof(ranked_t) * (size_t)(8 * c->n_pool + 1));
+    int64_t nc = 0, nv = c->n_visible[r];
+    for (int i = 0; i < c->n_pool; ++i) {
+        int64_t b = c->pool_blocks[r * c->n_pool + i];
+        if (b < 0) continue;
+        for (int t = 0; t < 8; ++t) {
+            int64_t j = 8 * b + t;
+            if (j >= nv) continue;
+            cand[nc].key = orc_order_key(c->pool_scores[(r * c->n_pool + i) * 8 + t]);
+            cand[nc].id = j;
+            ++nc;
+        }
+    }
+    emit_first_k_ascending(cand, nc, c->k, c->idx + r * c->k, c->k);
+    free(cand);
+}
+
+int orc_topk_pool(const float* pool_scores, const int32_t* pool_blocks, int n_pool,
+                  const int32_t* n_visible, int64_t R, int k, int32_t* idx, int threads) {
+    if (R < 0 || n_pool < 0 || k < 0) return -1;
+    topk_ctx c = {pool_scores, pool_blocks, n_visible, n_pool, k, idx};
+    parallel_rows(topk_row, &c, R, threads);
+    return 0;
+}
+
+/* O8 over a full score array [R][N_max], positions < n_visible. */
+typedef struct { const float* scores; const int32_t* n_visible; int64_t N_max; int k; int32_t* idx; } topkf_ctx;
+
+static void topkf_row(void* vctx, int64_t r) {
+    topkf_ctx* c = (topkf_ctx*)vctx;
+    int64_t nv = c->n_visible[r];
+    ranked_t* cand = (ranked_t*)malloc(sizeof(ranked_t) * (size_t)(nv > 0 ? nv : 1));
+    for (int64_t j = 0; j < nv; ++j) { cand[j].key = orc_order_key(c->scores[r * c->N_max + j]); cand[j].id = j; }
+    emit_first_k_ascending(cand, nv, c->k, c->idx + r * c->k, c->k);
+    free(cand);
+}
+
+int orc_topk_full(const float* scores, const int32_t* n_visible, int64_t R, int64_t N_max, int k,
+                  int32_t* idx, int threads) {
+    if (R < 0 || k < 0) return -1;
+    topkf_ctx c = {scores, n_visible, N_max, k, idx};
+    parallel_rows(topkf_row, &c, R, threads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O11: sparse + window attention in double                           */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const float* q; const uint8_t *cc, *cs; const int32_t* idx; int k;
+    const uint8_t* win; const int32_t *win_start, *win_len;
+    int M, H, Tw; int64_t N_max; float sm_scale; float* out;
+} attn_ctx;
+
+static void decode_latent_row(const uint8_t* codes, const uint8_t* scales, double* v) {
+    for (int i = 0; i < 512; ++i) {
+        unsigned code = (i % 2 == 0) ? (codes[i / 2] & 15u) : (codes[i / 2] >> 4);
+        v[i] = orc_e2m1_value(code) * orc_e8m0_scale(scales[i / 32]);
+    }
+}
+
+static void attn_row(void* vctx, int64_t r) {
+    attn_ctx* c = (attn_ctx*)vctx;
+    int64_t seq = r / c->M;
+    int nw = c->win_len[r];
+    int ne_max = c->k + (nw > 0 ? nw : 0);
+    double* vals = (double*)malloc(sizeof(double) * 512 * (size_t)(ne_max > 0 ? ne_max : 1));
+    int ne = 0;
+    /* the selected latent rows (value = key) */
+    for (int j = 0; j < c->k; ++j) {
+        int64_t p = c->idx[r * c->k + j];
+        if (p < 0) continue;
+        const uint8_t* codes = c->cc + (seq * c->N_max + p) * 256;
+        const uint8_t* scales = c->cs + (seq * c->N_max + p) * 16;
+        decode_latent_row(codes, scales, vals + 512 * (size_t)ne);
+        ++ne;
+    }
+    /* the sliding-window rows (FP8, value = key) */
+    for (int t = 0; t < nw; ++t) {
+        const uint8_t* row = c->win + (seq * (int64_t)c->Tw + c->win_start[r] + t) * 512;
+        for (int i = 0; i < 512; ++i) vals[512 * (size_t)ne + i] = orc_e4m3_value(row[i]);
+        ++ne;
+    }
+    double* z = (double*)malloc(sizeof(double) * (size_t)(ne > 0 ? ne : 1));
+    for (int h = 0; h < c->H; ++h) {
+        const float* qh = c->q + (r * c->H + h) * 512;
+        float* oh = c->out + (r * c->H + h) * 512;
+        if (ne == 0) {
+            for (int d = 0; d < 512; ++d) oh[d] = 0.f;
+            continue;
+        }
+        double m = -INFINITY;
+        for (int i = 0; i < ne; ++i) {
+            double dot = 0.0;
+            for (int d = 0; d < 512; ++d) dot += (double)qh[d] * vals[512 * (size_t)i + d];
+            z[i] = dot * (double)c->sm_scale;
+            if (z[i] > m) m = z[i];
+        }
+        double l = 0.0;
+        for (int i = 0; i < ne; ++i) { z[i] = exp(z[i] - m); l += z[i]; }
+        for (int d = 0; d < 512; ++d) {
+            double o = 0.0;
+            for (int i = 0; i < ne; ++i) o += z[i] * vals[512 * (size_t)i + d];
+            oh[d] = (float)(o / l);
+        }
+    }
+    free(z);
+    free(vals);
+}
+
+int orc_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_scales, const int32_t* idx,
+                    int k, const uint8_t* win, const int32_t* win_start, const int32_t* win_len, int B, int M,
+                    int64_t N_max, int H, int Tw, float sm_scale, float* out, int threads) {
+    if (B < 0 || M < 0 || H <= 0 || k < 0 || Tw < 0) return -1;
+    attn_ctx c = {q, c_codes, c_scales, idx, k, win, win_start, win_len, M, H, Tw, N_max, sm_scale, out};
+    parallel_rows(attn_row, &c, (int64_t)B * M, threads);
+    return 0;
+}

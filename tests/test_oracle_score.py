@@ -1,0 +1,97 @@
+"""Pins of the oracle's indexer score.
+
+The pages say the indexer query and key are FP4 and that the indexer scores
+every visible position (fupanwang.com DeepSeek-V4.1-Flash article, section
+三个方向一起压小缓存).  The score is read as one 128-d dot product whose four
+32-element blocks are summed exactly and then added in fp32 in block order.
+The pins: exact rational arithmetic whenever the block exponents are close
+(then every fp32 partial sum is exact), an adversarial case whose value depends
+on the block order, closed forms, and fp32 subnormal rounding.
+"""
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+import synth
+
+
+def _pack(nibbles):
+    nibbles = np.asarray(nibbles, np.uint8)
+    return (nibbles[0::2] | (nibbles[1::2] << 4)).astype(np.uint8)
+
+
+def _exact_dot(qc, qs, kc, ks):
+    def vals(c, s):
+        out = []
+        for i in range(128):
+            code = (c[i // 2] & 15) if i % 2 == 0 else (c[i // 2] >> 4)
+            out.append(Fraction(oracle.e2m1_value(int(code))) * Fraction(2) ** (int(s[i // 32]) - 127))
+        return out
+    return sum(a * b for a, b in zip(vals(qc, qs), vals(kc, ks)))
+
+
+def test_score_equals_exact_dot_when_exponents_are_close():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        qc = rng.integers(0, 256, 64, dtype=np.uint8)
+        kc = rng.integers(0, 256, 64, dtype=np.uint8)
+        base = int(rng.integers(60, 190))
+        qs = (base + rng.integers(0, 5, 4)).astype(np.uint8)      # spread <= 4
+        ks = (127 + rng.integers(-2, 3, 4)).astype(np.uint8)     # spread <= 4
+        s = oracle.score(qc, qs, kc, ks)
+        exact = _exact_dot(qc, qs, kc, ks)
+        assert Fraction(s) == exact, (trial, s, float(exact))
+
+
+def test_score_on_generated_normal_data_is_exact():
+    qc, qs = synth.mxfp4(5, 4, 0, 8, 128)
+    kc, ks = synth.mxfp4(5, 1, 0, 64, 128)
+    for i in range(8):
+        for j in range(64):
+            assert Fraction(oracle.score(qc[i], qs[i], kc[j], ks[j])) == _exact_dot(qc[i], qs[i], kc[j], ks[j])
+
+
+def test_score_block_order_is_fixed():
+    # block values v = (2^30, 1, -2^30, 1): ((v0+v1)+v2)+v3 = 1 in fp32, exact sum is 2
+    qn = np.zeros(128, np.uint8)
+    kn = np.zeros(128, np.uint8)
+    for b, neg in ((0, False), (1, False), (2, True), (3, False)):
+        qn[32 * b] = 1                      # 0.5 -> half-units 1
+        kn[32 * b] = 9 if neg else 1        # -0.5 / 0.5
+    qc, kc = _pack(qn), _pack(kn)
+    qs = np.array([143, 128, 143, 128], np.uint8)
+    ks = np.array([143, 128, 143, 128], np.uint8)
+    # isum_b = +-1, exponent qs+ks-256 = 30 or 0
+    assert oracle.score(qc, qs, kc, ks) == 1.0
+    assert _exact_dot(qc, qs, kc, ks) == 2
+
+
+def test_score_closed_forms():
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        c = rng.integers(0, 256, 64, dtype=np.uint8)
+        s = np.full(4, 127, np.uint8)
+        self_dot = oracle.score(c, s, c, s)
+        vals = oracle.mxfp4_decode(c, s)
+        assert self_dot == float(np.sum(vals * vals))          # exact: small integers / 4
+        assert self_dot >= 0
+        # symmetry and a power-of-two scale shift
+        c2 = rng.integers(0, 256, 64, dtype=np.uint8)
+        assert oracle.score(c, s, c2, s) == oracle.score(c2, s, c, s)
+        assert oracle.score(c, s + 1, c2, s) == 2 * oracle.score(c, s, c2, s)
+        assert oracle.score(c, s, c2, s - 3) == oracle.score(c, s, c2, s) / 8
+
+
+def test_score_subnormal_rounding():
+    # isum = 3 at exponent -150: 3 * 2^-150 rounds (to even) to 2 * 2^-149 in fp32
+    qn = np.zeros(128, np.uint8)
+    kn = np.zeros(128, np.uint8)
+    qn[0] = 3            # 1.5 -> 3 half-units
+    kn[0] = 1            # 0.5 -> 1 half-unit
+    qc, kc = _pack(qn), _pack(kn)
+    qs = np.array([53, 127, 127, 127], np.uint8)
+    ks = np.array([53, 127, 127, 127], np.uint8)   # 53+53-256 = -150
+    got = oracle.score(qc, qs, kc, ks)
+    assert got == float(np.float32(3 * 2.0 ** -150))
+    assert got == 2.0 ** -148

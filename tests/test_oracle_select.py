@@ -1,0 +1,163 @@
+"""Pins of the oracle's selection steps: block max, candidate pool, top-k.
+
+The hierarchical sparse indexer (fupanwang.com DeepSeek-V4.1-Flash article,
+section 三个方向一起压小缓存 and its figure caption): the first Full layer
+scores the visible context, represents each 8-position block by its highest
+score, keeps at most 2048 blocks as the candidate pool and selects its top-512;
+later layers select their top-512 inside the pool.  Ranks are (score desc,
+position asc).  Check (a): every selection equals a full sort done by brute
+force in Python; plus the Full-pool lemma (pool top-k equals the global top-k
+when the pool keeps at least k blocks), all-ties data, partial blocks and empty
+inputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+
+def _brute_blocks(scores, nv):
+    nb = (nv + 7) // 8
+    bm = []
+    for b in range(nb):
+        seg = [scores[j] for j in range(8 * b, min(8 * b + 8, nv))]
+        bm.append(max(seg, key=lambda v: oracle.order_key(v)))
+    return bm
+
+
+def _brute_first_k(keys_ids, k):
+    ranked = sorted(keys_ids, key=lambda t: (-t[0], t[1]))
+    return sorted(i for _, i in ranked[:k])
+
+
+def _pad(ids, n):
+    return np.array(list(ids) + [-1] * (n - len(ids)), np.int32)
+
+
+def _random_case(rng, B, N, M=1, few_values=False):
+    R = B * M
+    if few_values:
+        # tiny alphabet so that many scores tie
+        kc = rng.choice(np.array([0x00, 0x11, 0x22, 0x21], np.uint8), size=(B, N, 64))
+        qc = rng.choice(np.array([0x11, 0x22], np.uint8), size=(R, 64))
+    else:
+        kc = rng.integers(0, 256, (B, N, 64), dtype=np.uint8)
+        qc = rng.integers(0, 256, (R, 64), dtype=np.uint8)
+    ks = (127 + rng.integers(-2, 3, (B, N, 4))).astype(np.uint8)
+    qs = (127 + rng.integers(-2, 3, (R, 4))).astype(np.uint8)
+    return qc, qs, kc, ks
+
+
+@pytest.mark.parametrize("few", [False, True])
+@pytest.mark.parametrize("N,n_pool,k", [(64, 3, 5), (61, 8, 64), (200, 4, 16), (203, 30, 7), (37, 100, 300)])
+def test_index_full_against_brute_force(few, N, n_pool, k):
+    rng = np.random.default_rng(N * 7 + n_pool + k + few)
+    B = 3
+    qc, qs, kc, ks = _random_case(rng, B, N, few_values=few)
+    nv = np.array([N, N - 5, 1], np.int32)
+    out = oracle.index_full(qc, qs, kc, ks, nv, B, 1, N, n_pool=n_pool, k=k, want_scores=True,
+                            want_block_max=True)
+    for r in range(B):
+        s = [oracle.score(qc[r], qs[r], kc[r, j], ks[r, j]) for j in range(nv[r])]
+        assert np.array_equal(np.array(s, np.float32), out["scores"][r, : nv[r]])
+        bm = _brute_blocks(s, nv[r])
+        assert np.array_equal(np.array(bm, np.float32), out["block_max"][r, : len(bm)])
+        pool = _brute_first_k([(oracle.order_key(v), b) for b, v in enumerate(bm)], n_pool)
+        assert np.array_equal(out["pool_blocks"][r], _pad(pool, n_pool))
+        cand = [(oracle.order_key(s[j]), j) for b in pool for j in range(8 * b, min(8 * b + 8, nv[r]))]
+        idx = _brute_first_k(cand, k)
+        assert np.array_equal(out["idx"][r], _pad(idx, k))
+
+
+def test_all_ties_select_first_positions():
+    B, N = 2, 100
+    kc = np.full((B, N, 64), 0x22, np.uint8)
+    ks = np.full((B, N, 4), 127, np.uint8)
+    qc = np.full((B, 64), 0x11, np.uint8)
+    qs = np.full((B, 4), 127, np.uint8)
+    nv = np.array([100, 43], np.int32)
+    out = oracle.index_full(qc, qs, kc, ks, nv, B, 1, N, n_pool=4, k=10)
+    assert np.array_equal(out["pool_blocks"][0], [0, 1, 2, 3])
+    assert np.array_equal(out["idx"][0], np.arange(10))
+    assert np.array_equal(out["idx"][1], np.arange(10))
+
+
+def test_lemma_pool_topk_equals_global_topk():
+    rng = np.random.default_rng(21)
+    for N, n_pool, k in ((4096, 2048, 512), (4096, 600, 512), (3000, 512, 512), (1000, 100, 100),
+                         (999, 125, 100), (60, 8, 100)):
+        assert n_pool >= min(k, (N + 7) // 8)
+        B = 2
+        qc, qs = synth.mxfp4(N, 4, 0, B, 128)
+        kc, ks = synth.mxfp4(N, 1, 0, B * N, 128)
+        kc, ks = kc.reshape(B, N, 64), ks.reshape(B, N, 4)
+        nv = np.array([N, N - 3], np.int32)
+        a = oracle.index_full(qc, qs, kc, ks, nv, B, 1, N, n_pool=n_pool, k=k)
+        g = oracle.index_full(qc, qs, kc, ks, nv, B, 1, N, n_pool=n_pool, k=k, global_topk=True)
+        assert np.array_equal(a["idx"], g["idx"])
+        # and the top-k equals the top-k restricted to the first k blocks
+        b = oracle.index_full(qc, qs, kc, ks, nv, B, 1, N, n_pool=min(k, n_pool), k=k)
+        assert np.array_equal(a["idx"], b["idx"])
+
+
+def test_lemma_needs_enough_blocks():
+    """With fewer kept blocks than k the pool restricts the choice (the
+    approximation the pages acknowledge): the result stays inside the pool."""
+    rng = np.random.default_rng(22)
+    B, N = 1, 512
+    qc, qs, kc, ks = _random_case(rng, B, N)
+    nv = np.array([N], np.int32)
+    a = oracle.index_full(qc, qs, kc, ks, nv, B, 1, N, n_pool=2, k=64)
+    pool = a["pool_blocks"][0]
+    sel = a["idx"][0]
+    assert (sel[:16] // 8 >= 0).all() and set((sel[sel >= 0] // 8).tolist()) <= set(pool.tolist())
+    assert (sel[16:] == -1).all()
+
+
+def test_empty_and_tiny():
+    B, N = 2, 16
+    qc = np.zeros((B, 64), np.uint8)
+    qs = np.full((B, 4), 127, np.uint8)
+    kc = np.zeros((B, N, 64), np.uint8)
+    ks = np.full((B, N, 4), 127, np.uint8)
+    out = oracle.index_full(qc, qs, kc, ks, np.array([0, 3], np.int32), B, 1, N, n_pool=4, k=8)
+    assert (out["pool_blocks"][0] == -1).all() and (out["idx"][0] == -1).all()
+    assert np.array_equal(out["pool_blocks"][1], [0, -1, -1, -1])
+    assert np.array_equal(out["idx"][1], [0, 1, 2, -1, -1, -1, -1, -1])
+
+
+def test_index_pool_and_topk_pool_against_brute_force():
+    rng = np.random.default_rng(23)
+    B, N = 3, 300
+    qc, qs, kc, ks = _random_case(rng, B, N, few_values=True)
+    nv = np.array([300, 297, 150], np.int32)
+    pool = np.array([[0, 5, 7, 37, -1], [2, 3, 4, 36, 37], [1, 2, 18, -1, -1]], np.int32)
+    ps = oracle.index_pool(qc, qs, kc, ks, pool, nv, B, 1, N)
+    for r in range(B):
+        for i, b in enumerate(pool[r]):
+            for t in range(8):
+                j = 8 * b + t
+                v = ps[r, 8 * i + t]
+                if b < 0 or j >= nv[r]:
+                    assert v == -np.inf
+                else:
+                    assert v == oracle.score(qc[r], qs[r], kc[r, j], ks[r, j])
+    for k in (1, 7, 20, 40):
+        idx = oracle.topk_pool(ps, pool, nv, k)
+        for r in range(B):
+            cand = [(oracle.order_key(ps[r, 8 * i + t]), 8 * b + t)
+                    for i, b in enumerate(pool[r]) if b >= 0 for t in range(8) if 8 * b + t < nv[r]]
+            assert np.array_equal(idx[r], _pad(_brute_first_k(cand, k), k))
+
+
+def test_topk_full_against_brute_force():
+    rng = np.random.default_rng(24)
+    R, N = 4, 500
+    scores = np.round(rng.normal(size=(R, N)) * 3).astype(np.float32)   # many ties
+    nv = np.array([500, 499, 10, 0], np.int32)
+    for k in (1, 16, 200):
+        idx = oracle.topk_full(scores, nv, k)
+        for r in range(R):
+            cand = [(oracle.order_key(scores[r, j]), j) for j in range(nv[r])]
+            assert np.array_equal(idx[r], _pad(_brute_first_k(cand, k), k))
