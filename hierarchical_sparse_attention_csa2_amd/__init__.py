@@ -1,0 +1,222 @@
+"""MI355X (gfx950) CSA2 hierarchical sparse attention: Python binding of the C ABI.
+
+Every function here marshals torch tensors (device memory) and the current HIP
+stream into the C entry points of libcsa2.so with the same names; all of the
+step's arithmetic runs in the HIP kernels.  Shapes and dtypes are checked on the
+host before any call so that a mis-shaped tensor never reaches a kernel.  There
+is no fallback: if the library is missing, importing the functions raises.
+
+The step (DeepSeek-V4.1-Flash, fupanwang.com article, section 三个方向一起压小缓存
+and its hierarchical-sparse-indexer figure caption; section 后 20 层干脆共用一份 KV
+for the 128-token window; dreamax.pages.dev notes, CSA2 paragraph, for the
+Full / Reindex / Reuse modes):
+    Full    : csa2_index_full (scan -> 8-position block max -> 2048-block pool ->
+              top-512) then csa2_sparse_attn
+    Reindex : csa2_index_pool over the Full layer's pool -> csa2_topk -> attention
+    Reuse   : csa2_sparse_attn with the previous layer's indices
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+
+CSA2_OK = 0
+CSA2_ERR_INVALID = -1
+CSA2_ERR_UNSUPPORTED = -2
+CSA2_ERR_WORKSPACE = -3
+CSA2_ERR_HIP = -4
+CSA2_OP_INDEX_FULL = 1
+CSA2_OP_SPARSE_ATTN = 2
+
+EXPORTED = (
+    "csa2_index_scan", "csa2_select_blocks", "csa2_index_pool", "csa2_topk", "csa2_index_full",
+    "csa2_sparse_attn", "csa2_workspace_bytes", "csa2_status_string",
+)
+
+_lib = None
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libcsa2.so (built by build.py); raises if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with hierarchical_sparse_attention_csa2_amd/build.py "
+                           "(there is no CPU fallback)")
+    L = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.csa2_index_scan.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, vp]
+    L.csa2_select_blocks.argtypes = [vp, i64, vp, i32, i32, vp, i32, vp, vp]
+    L.csa2_index_pool.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i64, vp, vp]
+    L.csa2_topk.argtypes = [vp, vp, i64, vp, i32, i32, vp, vp]
+    L.csa2_index_full.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.csa2_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i64, i32, i32, f32, vp, vp, sz,
+                                   vp]
+    L.csa2_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32]
+    L.csa2_workspace_bytes.restype = sz
+    L.csa2_status_string.argtypes = [i32]
+    L.csa2_status_string.restype = ctypes.c_char_p
+    for f in ("csa2_index_scan", "csa2_select_blocks", "csa2_index_pool", "csa2_topk", "csa2_index_full",
+              "csa2_sparse_attn"):
+        getattr(L, f).restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load_library().csa2_status_string(int(status)).decode()
+
+
+def csa2_status_string(status: int) -> str:
+    return status_string(status)
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype, shape=None, numel=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn, status):
+    if status != CSA2_OK:
+        raise Csa2Error(fn, status)
+
+
+U8, I32, F32 = torch.uint8, torch.int32, torch.float32
+
+
+# ---------------------------------------------------------------------------
+# the C entry points
+# ---------------------------------------------------------------------------
+def csa2_workspace_bytes(op: int, B: int, M: int, N_max: int, H: int, k: int) -> int:
+    return int(load_library().csa2_workspace_bytes(op, B, M, N_max, H, k))
+
+
+def csa2_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, block_max, scores=None,
+                    stream=None):
+    R = B * M
+    nblk = (N_max + 7) // 8
+    st = load_library().csa2_index_scan(
+        _dev(q_codes, "q_codes", U8, (R, 64)), _dev(q_scales, "q_scales", U8, (R, 4)),
+        _dev(k_codes, "k_codes", U8, numel=B * N_max * 64), _dev(k_scales, "k_scales", U8, numel=B * N_max * 4),
+        _dev(n_visible, "n_visible", I32, (R,)), B, M, N_max,
+        _dev(scores, "scores", F32, (R, N_max), optional=True), _dev(block_max, "block_max", F32, (R, nblk)),
+        _stream(stream))
+    _check("csa2_index_scan", st)
+
+
+def csa2_select_blocks(block_max, n_visible, n_pool, pool_blocks, k_blocks=0, topk_blocks=None, stream=None):
+    R, stride = block_max.shape
+    st = load_library().csa2_select_blocks(
+        _dev(block_max, "block_max", F32), stride, _dev(n_visible, "n_visible", I32, (R,)), R, n_pool,
+        _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), k_blocks,
+        _dev(topk_blocks, "topk_blocks", I32, (R, k_blocks), optional=k_blocks == 0), _stream(stream))
+    _check("csa2_select_blocks", st)
+
+
+def csa2_index_pool(q_codes, q_scales, k_codes, k_scales, pool_blocks, n_visible, B, M, N_max, pool_scores,
+                    stream=None):
+    R = B * M
+    n_pool = pool_blocks.shape[1]
+    st = load_library().csa2_index_pool(
+        _dev(q_codes, "q_codes", U8, (R, 64)), _dev(q_scales, "q_scales", U8, (R, 4)),
+        _dev(k_codes, "k_codes", U8, numel=B * N_max * 64), _dev(k_scales, "k_scales", U8, numel=B * N_max * 4),
+        _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), n_pool, _dev(n_visible, "n_visible", I32, (R,)),
+        B, M, N_max, _dev(pool_scores, "pool_scores", F32, (R, 8 * n_pool)), _stream(stream))
+    _check("csa2_index_pool", st)
+
+
+def csa2_topk(scores, n_visible, k, idx, pool_blocks=None, stream=None):
+    R = scores.shape[0]
+    if pool_blocks is not None:
+        n_pool = pool_blocks.shape[1]
+        sc = _dev(scores, "scores", F32, (R, 8 * n_pool))
+        pb = _dev(pool_blocks, "pool_blocks", I32, (R, n_pool))
+    else:
+        n_pool = scores.shape[1]
+        sc = _dev(scores, "scores", F32, (R, n_pool))
+        pb = None
+    st = load_library().csa2_topk(sc, pb, n_pool, _dev(n_visible, "n_visible", I32, (R,)), R, k,
+                                  _dev(idx, "idx", I32, (R, k)), _stream(stream))
+    _check("csa2_topk", st)
+
+
+def csa2_index_full(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool, k, pool_blocks,
+                    idx=None, workspace=None, scores=None, block_max=None, stream=None):
+    R = B * M
+    nblk = (N_max + 7) // 8
+    need = csa2_workspace_bytes(CSA2_OP_INDEX_FULL, B, M, N_max, 0, k)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=U8, device=q_codes.device)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
+    st = load_library().csa2_index_full(
+        _dev(q_codes, "q_codes", U8, (R, 64)), _dev(q_scales, "q_scales", U8, (R, 4)),
+        _dev(k_codes, "k_codes", U8, numel=B * N_max * 64), _dev(k_scales, "k_scales", U8, numel=B * N_max * 4),
+        _dev(n_visible, "n_visible", I32, (R,)), B, M, N_max, n_pool, k,
+        _dev(scores, "scores", F32, (R, N_max), optional=True),
+        _dev(block_max, "block_max", F32, (R, nblk), optional=True),
+        _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), _dev(idx, "idx", I32, (R, k), optional=k == 0),
+        _dev(workspace, "workspace", U8), workspace.numel(), _stream(stream))
+    _check("csa2_index_full", st)
+
+
+def csa2_sparse_attn(q, c_codes, c_scales, idx, win, win_start, win_len, win_max, B, M, N_max, sm_scale, out,
+                     workspace=None, stream=None):
+    R, H, D = q.shape
+    if D != 512 or R != B * M:
+        raise ValueError("q must be [B*M, H, 512]")
+    k = idx.shape[1] if idx is not None else 0
+    Tw = win.shape[1] if win is not None else 0
+    if win is not None and tuple(win.shape) != (B, Tw, 512):
+        raise ValueError("win must be [B, Tw, 512]")
+    need = csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, M, 0, H, k + win_max)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=U8, device=q.device)
+    if need > 0 and workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
+    st = load_library().csa2_sparse_attn(
+        _dev(q, "q", F32, (R, H, 512)),
+        _dev(c_codes, "c_codes", U8, numel=B * N_max * 256, optional=k == 0),
+        _dev(c_scales, "c_scales", U8, numel=B * N_max * 16, optional=k == 0),
+        _dev(idx, "idx", I32, (R, k), optional=k == 0), k,
+        _dev(win, "win", U8, optional=win_max == 0), _dev(win_start, "win_start", I32, (R,), optional=win_max == 0),
+        _dev(win_len, "win_len", I32, (R,), optional=win_max == 0), win_max, B, M, N_max, H, Tw, float(sm_scale),
+        _dev(out, "out", F32, (R, H, 512)),
+        _dev(workspace, "workspace", U8, optional=True) if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check("csa2_sparse_attn", st)

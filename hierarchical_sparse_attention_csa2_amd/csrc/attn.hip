@@ -1,0 +1,368 @@
+// Sparse + sliding-window attention over the selected latent entries.
+//
+// DeepSeek-V4.1-Flash: every layer reads the 512 selected entries of the shared
+// MXFP4 latent KV plus its own 128-token FP8 sliding window (fupanwang.com
+// article, sections 后 20 层干脆共用一份 KV and 三个方向一起压小缓存).  One softmax
+// runs over both sets with value = key: o_h = sum_i softmax_i(q_h . c_i * scale) c_i.
+//
+// All heads share each entry, so per row this is a dense contraction
+// Q[H x 512] . C^T[512 x E] followed by P[H x E] . C[E x 512]: it runs on the bf16
+// MFMA units.  Decoded entry values (E2M1 x 2^e, E4M3) are exact in bf16; the
+// query and the probabilities are split into hi + lo bf16 parts, so every
+// product carries ~16 mantissa bits and accumulates in fp32.
+//
+// Workgroup = (split, row): H/8 waves.  A pair of waves owns 16 heads; each of
+// the two keeps the query (hi/lo) and the output accumulator O^T for its half of
+// the 512 dims in registers, and the two partial S^T tiles are summed through
+// LDS.  Entries stream through LDS in chunks of 64: each chunk is decoded
+// once into a row-major copy (operand A of S^T = C Q^T) and a transposed copy
+// (operand A of O^T = C^T P^T).  S^T's accumulator layout gives each lane the
+// probabilities of exactly the entries it must feed as operand B of the second
+// product, so P never leaves registers.  An online softmax (log2 domain) runs
+// across chunks; splits > 1 write partial (o, m, l) that a combine kernel merges.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace csa2 {
+
+constexpr int kChunk = 64;                 // entries per LDS chunk
+constexpr int kKLd = 512 + 8;              // bf16 row stride of the row-major copy
+constexpr int kVLd = kChunk + 8;           // bf16 row stride of the transposed copy
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct AttnParams {
+  const float* q;
+  const uint8_t* c_codes;
+  const uint8_t* c_scales;
+  const int32_t* idx;
+  const uint8_t* win;
+  const int32_t* win_start;
+  const int32_t* win_len;
+  float* out;
+  float* part_o;      // [R][splits][H][512]
+  float* part_ml;     // [R][splits][H][2]
+  int64_t N_max;
+  int k, win_max, M, H, Tw;
+  int splits, chunks_per_split, n_chunks;
+  float qscale;       // sm_scale * log2(e)
+};
+
+__device__ __forceinline__ bf16x8_t zero_bf16x8() {
+  bf16x8_t z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+template <int NP>
+__global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) {
+  __shared__ __attribute__((aligned(16))) __bf16 sK[kChunk * kKLd];
+  __shared__ __attribute__((aligned(16))) __bf16 sVt[512 * kVLd];
+  __shared__ __attribute__((aligned(16))) float sS[NP][64][16];
+  __shared__ int64_t sOff[kChunk];
+  __shared__ int sType[kChunk];
+  __shared__ unsigned long long sMask;
+
+  const int split = blockIdx.x;
+  const int r = blockIdx.y;
+  const int64_t seq = r / a.M;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int pr = w % NP;       // head group of 16
+  const int half = w / NP;     // 0: dims 0..255, 1: dims 256..511
+  const int dbase = 256 * half;
+  const int g = lane >> 4;     // lane group 0..3
+  const int hl = lane & 15;
+  const int h = 16 * pr + hl;
+
+  int wl = a.win_max > 0 ? a.win_len[r] : 0;
+  wl = wl < 0 ? 0 : (wl > a.win_max ? a.win_max : wl);
+  const int E = a.k + wl;
+  const int ws0 = a.win_max > 0 ? a.win_start[r] : 0;
+
+  // query operands (B of S^T = C Q^T): head h, dims dbase + 32s + 8g .. +8, prescaled
+  bf16x8_t qhi[8], qlo[8];
+  {
+    const float* qp = a.q + ((int64_t)r * a.H + h) * 512 + dbase + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp + 32 * s);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(qp + 32 * s + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = (e < 4 ? x0[e] : x1[e - 4]) * a.qscale;
+        const __bf16 hi = (__bf16)v;
+        qhi[s][e] = hi;
+        qlo[s][e] = (__bf16)(v - (float)hi);
+      }
+    }
+  }
+
+  f32x4 oacc[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) oacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+
+  const int c_begin = split * a.chunks_per_split;
+  int c_end = c_begin + a.chunks_per_split;
+  c_end = c_end < a.n_chunks ? c_end : a.n_chunks;
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const int ebase = c * kChunk;
+    if (ebase >= E) break;
+    __syncthreads();   // previous chunk's LDS reads are done
+    // 1. entry table
+    if (tid < kChunk) {
+      const int e = ebase + tid;
+      int64_t off = -1;
+      int type = 0;
+      if (e < a.k) {
+        const int64_t p = a.idx[(int64_t)r * a.k + e];
+        if (p >= 0 && p < a.N_max) off = seq * a.N_max + p;
+      } else if (e < E) {
+        const int64_t t = (int64_t)ws0 + (e - a.k);
+        if (t >= 0 && t < a.Tw) off = seq * a.Tw + t;
+        type = 1;
+      }
+      sOff[tid] = off;
+      sType[tid] = type;
+      const unsigned long long m = __ballot(off >= 0);
+      if (tid == 0) sMask = m;
+    }
+    __syncthreads();
+    const unsigned long long vmask = sMask;
+    if (vmask == 0ull) continue;
+
+    // 2. decode 4 entries x 8 dims per tile into both LDS copies
+    for (int T = tid; T < (kChunk / 4) * 64; T += NP * 128) {
+      const int eg = T & 15;
+      const int dg = T >> 4;
+      bf16x8_t v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * eg + i;
+        const int64_t off = sOff[e];
+        if (off < 0) {
+          v[i] = zero_bf16x8();
+        } else if (sType[e] == 0) {
+          const uint32_t wcode = *reinterpret_cast<const uint32_t*>(a.c_codes + off * 256 + 4 * dg);
+          const float sc = e8m0_to_f32(a.c_scales[off * 16 + (dg >> 2)]);
+          const bf16x2_t p0 = fp4x2_to_bf16<0>(wcode, sc);
+          const bf16x2_t p1 = fp4x2_to_bf16<1>(wcode, sc);
+          const bf16x2_t p2 = fp4x2_to_bf16<2>(wcode, sc);
+          const bf16x2_t p3 = fp4x2_to_bf16<3>(wcode, sc);
+          v[i] = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        } else {
+          const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(a.win + off * 512 + 8 * dg);
+          const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(wb[0], false);
+          const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(wb[0], true);
+          const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8(wb[1], false);
+          const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8(wb[1], true);
+          v[i] = bf16x8_t{(__bf16)f0[0], (__bf16)f0[1], (__bf16)f1[0], (__bf16)f1[1],
+                          (__bf16)f2[0], (__bf16)f2[1], (__bf16)f3[0], (__bf16)f3[1]};
+        }
+        *reinterpret_cast<bf16x8_t*>(&sK[e * kKLd + 8 * dg]) = v[i];
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        *reinterpret_cast<bf16x4_t*>(&sVt[(8 * dg + d) * kVLd + 4 * eg]) =
+            bf16x4_t{v[0][d], v[1][d], v[2][d], v[3][d]};
+    }
+    __syncthreads();
+
+    // 3. partial S^T[64 entries x 16 heads] over this wave's 256 dims
+    f32x4 sacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8_t A =
+            *reinterpret_cast<const bf16x8_t*>(&sK[(16 * t + hl) * kKLd + dbase + 32 * s + 8 * g]);
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qhi[s], sacc[t], 0, 0, 0);
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qlo[s], sacc[t], 0, 0, 0);
+      }
+    }
+    // the two halves of a head group exchange partial sums through LDS
+    f32x4* slot = reinterpret_cast<f32x4*>(&sS[pr][lane][0]);
+    if (half == 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) slot[t] = sacc[t];
+    }
+    __syncthreads();
+    if (half == 1) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sacc[t] += slot[t];
+        slot[t] = sacc[t];
+      }
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sacc[t] = slot[t];
+    }
+
+    // 4. online softmax (lane holds entries 16t + 4g + i of head h)
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 16 * t + 4 * g + i;
+        if (!((vmask >> e) & 1ull)) sacc[t][i] = -__builtin_inff();
+        mloc = fmaxf(mloc, sacc[t][i]);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(sacc[t][i] - m_new);
+        sacc[t][i] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) oacc[m] *= alpha;
+
+    // 5. O^T[256 dims x 16 heads] += C^T P^T, two k-steps of 32 entries
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8_t bhi, blo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = i < 4 ? sacc[2 * j][i] : sacc[2 * j + 1][i - 4];
+        const __bf16 hi = (__bf16)p;
+        bhi[i] = hi;
+        blo[i] = (__bf16)(p - (float)hi);
+      }
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const __bf16* vrow = &sVt[(dbase + 16 * m + hl) * kVLd + 32 * j + 4 * g];
+        const bf16x4_t lo4 = *reinterpret_cast<const bf16x4_t*>(vrow);
+        const bf16x4_t hi4 = *reinterpret_cast<const bf16x4_t*>(vrow + 16);
+        const bf16x8_t A = bf16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bhi, oacc[m], 0, 0, 0);
+        oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, blo, oacc[m], 0, 0, 0);
+      }
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot = l_tot + __shfl_xor(l_tot, 32, 64);
+  if (a.splits == 1) {
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    float* op = a.out + ((int64_t)r * a.H + h) * 512 + dbase + 4 * g;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = oacc[m] * inv;
+  } else {
+    const int64_t slot = ((int64_t)r * a.splits + split) * a.H + h;
+    float* op = a.part_o + slot * 512 + dbase + 4 * g;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = oacc[m];
+    if (g == 0 && half == 0) {
+      a.part_ml[2 * slot] = m_run;
+      a.part_ml[2 * slot + 1] = l_tot;
+    }
+  }
+}
+
+// Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml, int splits, int H,
+                                                           float* __restrict__ out) {
+  const int r = blockIdx.x;
+  for (int hd = threadIdx.x; hd < H * 512; hd += 256) {
+    const int h = hd >> 9;
+    float M = -__builtin_inff();
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(((int64_t)r * splits + s) * H + h) * 2]);
+    float L = 0.f, acc = 0.f;
+    if (M != -__builtin_inff()) {
+      for (int s = 0; s < splits; ++s) {
+        const int64_t slot = ((int64_t)r * splits + s) * H + h;
+        const float wgt = exp2f(part_ml[2 * slot] - M);
+        L += wgt * part_ml[2 * slot + 1];
+        acc += wgt * part_o[slot * 512 + (hd & 511)];
+      }
+    }
+    out[(int64_t)r * H * 512 + hd] = L > 0.f ? acc / L : 0.f;
+  }
+}
+
+int attn_splits(int R, int k, int win_max) {
+  const int n_chunks = (k + win_max + kChunk - 1) / kChunk;
+  if (n_chunks <= 1) return 1;
+  int want = (512 + R - 1) / R;            // aim for ~2 workgroups per CU
+  if (want < 1) want = 1;
+  if (want > n_chunks) want = n_chunks;
+  const int cps = (n_chunks + want - 1) / want;
+  return (n_chunks + cps - 1) / cps;
+}
+
+size_t attn_workspace_bytes(int R, int H, int k_plus_win) {
+  const int n_chunks = (k_plus_win + kChunk - 1) / kChunk;
+  const int splits = attn_splits(R, k_plus_win, 0);
+  (void)n_chunks;
+  if (splits <= 1) return 0;
+  return (size_t)R * splits * H * (512 + 2) * sizeof(float);
+}
+
+hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
+  const int R = L.B * L.M;
+  AttnParams a;
+  a.q = L.q;
+  a.c_codes = L.c_codes;
+  a.c_scales = L.c_scales;
+  a.idx = L.idx;
+  a.win = L.win;
+  a.win_start = L.win_start;
+  a.win_len = L.win_len;
+  a.out = L.out;
+  a.N_max = L.N_max;
+  a.k = L.k;
+  a.win_max = L.win_max;
+  a.M = L.M;
+  a.H = L.H;
+  a.Tw = L.Tw;
+  a.qscale = L.sm_scale * kLog2e;
+  a.n_chunks = (L.k + L.win_max + kChunk - 1) / kChunk;
+  a.splits = attn_splits(R, L.k, L.win_max);
+  a.chunks_per_split = (a.n_chunks + a.splits - 1) / a.splits;
+  if (a.n_chunks == 0) {
+    a.splits = 1;
+    a.chunks_per_split = 0;
+  }
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (a.splits > 1) {
+    a.part_o = static_cast<float*>(L.workspace);
+    a.part_ml = a.part_o + (size_t)R * a.splits * L.H * 512;
+  }
+  dim3 grid((unsigned)a.splits, (unsigned)R);
+  const int NP = L.H / 16;
+  switch (NP) {
+    case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(128), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(sparse_attn_kernel<3>, grid, dim3(384), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, dim3(512), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.splits == 1) return err;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)R), dim3(256), 0, stream, a.part_o, a.part_ml, a.splits,
+                     L.H, L.out);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

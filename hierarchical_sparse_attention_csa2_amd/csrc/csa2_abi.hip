@@ -1,0 +1,178 @@
+// C ABI of the CSA2 hierarchical sparse attention step (see include/csa2.h).
+// Every entry point validates its arguments on the host, then enqueues kernels
+// on the caller's stream; nothing is allocated and no state is kept.
+#include "../../include/csa2.h"
+#include "kernels.h"
+
+namespace {
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// index_full workspace carve-up
+struct FullWs {
+  size_t block_max, topk_blocks, topk_scores, total;
+};
+
+inline FullWs full_ws(int64_t R, int64_t N_max, int k) {
+  FullWs w;
+  const int64_t nblk = (N_max + 7) / 8;
+  w.block_max = 0;
+  w.topk_blocks = align_up(w.block_max + (size_t)R * nblk * sizeof(float));
+  w.topk_scores = align_up(w.topk_blocks + (size_t)R * (k > 0 ? k : 0) * sizeof(int32_t));
+  w.total = align_up(w.topk_scores + (size_t)R * (k > 0 ? k : 0) * 8 * sizeof(float));
+  return w;
+}
+
+constexpr int64_t kMaxRows = 1 << 24;
+constexpr int64_t kMaxN = (int64_t)1 << 30;   // ids are int32; 8*blocks must fit
+constexpr int kMaxPool = 1 << 20;
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(int status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_INVALID: return "invalid argument";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA2_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int csa2_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                    const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
+                    float* scores, float* block_max, void* stream) {
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !n_visible || !block_max) return CSA2_ERR_INVALID;
+  if (B < 1 || M < 1 || N_max < 1 || N_max > kMaxN || (int64_t)B * M > kMaxRows) return CSA2_ERR_INVALID;
+  return hip_status(csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, scores,
+                                            block_max, (N_max + 7) / 8, as_stream(stream)));
+}
+
+int csa2_select_blocks(const float* block_max, int64_t nblk_stride, const int32_t* n_visible, int R, int n_pool,
+                       int32_t* pool_blocks, int k_blocks, int32_t* topk_blocks, void* stream) {
+  if (!block_max || !n_visible || !pool_blocks) return CSA2_ERR_INVALID;
+  if (R < 1 || R > kMaxRows || n_pool < 1 || n_pool > kMaxPool || k_blocks < 0 || k_blocks > kMaxPool ||
+      nblk_stride < 1 || nblk_stride > kMaxN / 8)
+    return CSA2_ERR_INVALID;
+  if (k_blocks > 0 && !topk_blocks) return CSA2_ERR_INVALID;
+  return hip_status(csa2::launch_select(csa2::kSelBlocks, block_max, nblk_stride, nullptr, 0, n_visible, R, n_pool,
+                                        pool_blocks, k_blocks, topk_blocks, as_stream(stream)));
+}
+
+int csa2_index_pool(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                    const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool, const int32_t* n_visible,
+                    int B, int M, int64_t N_max, float* pool_scores, void* stream) {
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !pool_blocks || !n_visible || !pool_scores)
+    return CSA2_ERR_INVALID;
+  if (B < 1 || M < 1 || N_max < 1 || N_max > kMaxN || (int64_t)B * M > kMaxRows || n_pool < 1 ||
+      n_pool > kMaxPool)
+    return CSA2_ERR_INVALID;
+  return hip_status(csa2::launch_pool_scan(q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, B,
+                                           M, N_max, pool_scores, as_stream(stream)));
+}
+
+int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, const int32_t* n_visible, int R,
+              int k, int32_t* idx, void* stream) {
+  if (!scores || !n_visible || !idx) return CSA2_ERR_INVALID;
+  if (R < 1 || R > kMaxRows || n_pool < 1 || k < 0 || k > kMaxPool) return CSA2_ERR_INVALID;
+  if (pool_blocks ? n_pool > kMaxPool : n_pool > kMaxN) return CSA2_ERR_INVALID;
+  if (k == 0) return CSA2_OK;
+  const int layout = pool_blocks ? csa2::kSelPool : csa2::kSelFull;
+  return hip_status(csa2::launch_select(layout, scores, pool_blocks ? 8 * n_pool : n_pool, pool_blocks, n_pool,
+                                        n_visible, R, k, idx, 0, nullptr, as_stream(stream)));
+}
+
+int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                    const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max, int n_pool,
+                    int k, float* scores, float* block_max, int32_t* pool_blocks, int32_t* idx, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !n_visible || !pool_blocks) return CSA2_ERR_INVALID;
+  if (B < 1 || M < 1 || N_max < 1 || N_max > kMaxN || (int64_t)B * M > kMaxRows || n_pool < 1 ||
+      n_pool > kMaxPool || k < 0 || k > kMaxPool)
+    return CSA2_ERR_INVALID;
+  if (k > 0 && !idx) return CSA2_ERR_INVALID;
+  const int64_t R = (int64_t)B * M;
+  const int64_t nblk = (N_max + 7) / 8;
+  const FullWs w = full_ws(R, N_max, k);
+  if (!workspace || workspace_bytes < w.total) return CSA2_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* bmax = block_max ? block_max : reinterpret_cast<float*>(ws + w.block_max);
+  int32_t* topk_blocks = reinterpret_cast<int32_t*>(ws + w.topk_blocks);
+  float* topk_scores = reinterpret_cast<float*>(ws + w.topk_scores);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, scores, bmax,
+                                         nblk, s);
+  if (e != hipSuccess) return CSA2_ERR_HIP;
+  // the pool's top-k lies in the pool's first min(k, n_pool) blocks: rescore only those
+  const int kb = k < n_pool ? k : n_pool;
+  e = csa2::launch_select(csa2::kSelBlocks, bmax, nblk, nullptr, 0, n_visible, (int)R, n_pool, pool_blocks,
+                          kb, k > 0 ? topk_blocks : nullptr, s);
+  if (e != hipSuccess) return CSA2_ERR_HIP;
+  if (k == 0) return CSA2_OK;
+  e = csa2::launch_pool_scan(q_codes, q_scales, k_codes, k_scales, topk_blocks, kb, n_visible, B, M, N_max,
+                             topk_scores, s);
+  if (e != hipSuccess) return CSA2_ERR_HIP;
+  e = csa2::launch_select(csa2::kSelPool, topk_scores, 8 * (int64_t)kb, topk_blocks, kb, n_visible, (int)R, k, idx,
+                          0, nullptr, s);
+  return hip_status(e);
+}
+
+int csa2_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_scales, const int32_t* idx, int k,
+                     const uint8_t* win, const int32_t* win_start, const int32_t* win_len, int win_max, int B,
+                     int M, int64_t N_max, int H, int Tw, float sm_scale, float* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!q || !out) return CSA2_ERR_INVALID;
+  if (B < 1 || M < 1 || (int64_t)B * M > kMaxRows || k < 0 || k > kMaxPool || win_max < 0 || Tw < 0 ||
+      win_max > Tw || N_max < 0 || N_max > kMaxN)
+    return CSA2_ERR_INVALID;
+  if (k > 0 && (!idx || !c_codes || !c_scales || N_max < 1)) return CSA2_ERR_INVALID;
+  if (win_max > 0 && (!win || !win_start || !win_len)) return CSA2_ERR_INVALID;
+  if (!(sm_scale == sm_scale)) return CSA2_ERR_INVALID;
+  if (H < 16 || H > 64 || H % 16 != 0) return CSA2_ERR_UNSUPPORTED;
+  const int R = B * M;
+  const size_t need = csa2::attn_workspace_bytes(R, H, k + win_max);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
+  csa2::AttnLaunch L;
+  L.q = q;
+  L.c_codes = c_codes;
+  L.c_scales = c_scales;
+  L.idx = idx;
+  L.k = k;
+  L.win = win;
+  L.win_start = win_start;
+  L.win_len = win_len;
+  L.win_max = win_max;
+  L.B = B;
+  L.M = M;
+  L.H = H;
+  L.Tw = Tw;
+  L.N_max = N_max;
+  L.sm_scale = sm_scale;
+  L.out = out;
+  L.workspace = workspace;
+  L.workspace_bytes = workspace_bytes;
+  return hip_status(csa2::launch_sparse_attn(L, as_stream(stream)));
+}
+
+size_t csa2_workspace_bytes(int op, int B, int M, int64_t N_max, int H, int k) {
+  if (B < 1 || M < 1 || k < 0) return 0;
+  const int64_t R = (int64_t)B * M;
+  if (op == CSA2_OP_INDEX_FULL) {
+    if (N_max < 1) return 0;
+    return full_ws(R, N_max, k).total;
+  }
+  if (op == CSA2_OP_SPARSE_ATTN) {
+    if (H < 16 || H > 64 || H % 16 != 0) return 0;
+    return csa2::attn_workspace_bytes((int)R, H, k);
+  }
+  return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal launchers of the CSA2 kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+int scan_chunk_positions(int64_t N_max);
+
+hipError_t launch_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                             const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
+                             float* scores, float* block_max, int64_t nblk_stride, hipStream_t stream);
+
+hipError_t launch_pool_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                            const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool,
+                            const int32_t* n_visible, int B, int M, int64_t N_max, float* pool_scores,
+                            hipStream_t stream);
+
+// Ranked selection.  layout 0: block maxima (row length ceil(n_visible/8),
+// stride `stride`); 1: pool slots (8*n_pool per row, positions through
+// pool_blocks); 2: full score rows (length min(n_visible, stride)).
+enum SelectLayout { kSelBlocks = 0, kSelPool = 1, kSelFull = 2 };
+
+hipError_t launch_select(int layout, const float* scores, int64_t stride, const int32_t* pool_blocks,
+                         int64_t n_pool, const int32_t* n_visible, int R, int k1, int32_t* out1, int k2,
+                         int32_t* out2, hipStream_t stream);
+
+struct AttnLaunch {
+  const float* q;
+  const uint8_t* c_codes;
+  const uint8_t* c_scales;
+  const int32_t* idx;
+  int k;
+  const uint8_t* win;
+  const int32_t* win_start;
+  const int32_t* win_len;
+  int win_max;
+  int B, M, H, Tw;
+  int64_t N_max;
+  float sm_scale;
+  float* out;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+int attn_splits(int R, int k, int win_max);
+size_t attn_workspace_bytes(int R, int H, int k_plus_win);
+hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t stream);
+
+}  // namespace csa2

@@ -1,0 +1,189 @@
+/*
+ * csa2.h - C ABI of the CSA2 hierarchical sparse attention step on MI355X (gfx950).
+ *
+ * What the step computes (DeepSeek-V4.1-Flash write-ups):
+ *   - fupanwang.com article, section "三个方向一起压小缓存" and the figure caption on
+ *     the hierarchical sparse indexer: the first Full layer's FP4 indexer scores
+ *     every visible cached position; each 8-position block is represented by its
+ *     highest score; the top 2048 blocks (16,384 positions) form a candidate pool
+ *     shared with later layers; every layer reads 512 selected KV entries.
+ *     Reindex layers score only inside the pool; Reuse layers reuse the latest
+ *     selection.  The main KV is OCP MXFP4, the sliding-window KV stays FP8.
+ *   - same article, section "后 20 层干脆共用一份 KV": a 128-token sliding window
+ *     branch next to the sparse global attention.
+ *   - dreamax.pages.dev notes, CSA2 paragraph: the Full / Reindex / Reuse modes.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor arguments are DEVICE pointers to caller-owned memory; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *     default stream).  Calls return before the work finishes: results are valid
+ *     once the caller synchronises the stream.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     validation error nothing is launched and a negative status is returned.
+ *     A failed launch returns CSA2_ERR_HIP.  Device-side contents (codes, scale
+ *     bytes, indices) are not validated unless stated.
+ *   - Rows: a call covers B sequences with M query rows each, R = B*M rows;
+ *     query row r belongs to sequence r / M (decode: M = 1; prefill: M > 1).
+ *   - Storage formats (OCP Microscaling Formats v1.0 / OCP FP8):
+ *       MXFP4: blocks of 32 elements, one E8M0 scale byte per block
+ *              (value 2^(byte-127); 0xFF must not occur), element codes E2M1,
+ *              element 2i in the low nibble of byte i.
+ *       FP8:   E4M3 (OCP "E4M3FN": bias 7, max 448, no infinities).
+ *   - Layouts (row-major, contiguous):
+ *       index query  q_codes u8[R][64],  q_scales u8[R][4]          (128-d MXFP4)
+ *       index keys   k_codes u8[B][N_max][64], k_scales u8[B][N_max][4]
+ *       latent KV    c_codes u8[B][N_max][256], c_scales u8[B][N_max][16] (512-d)
+ *       window KV    win u8[B][Tw][512] (FP8 E4M3)
+ *       n_visible    i32[R]: query row r sees cached entries 0 .. n_visible[r]-1
+ *                    (0 <= n_visible[r] <= N_max, not checked on the device)
+ *       queries/out  f32[R][H][512]
+ *   - Scores compare by IEEE-754 total order of their fp32 bits; positions and
+ *     blocks rank by (score descending, position ascending): ties go to the
+ *     lowest position.  Selected positions/blocks are written in ascending order
+ *     and the rest of each output row is padded with -1.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_BLOCK 8          /* positions per coarse block */
+#define CSA2_INDEX_DIM 128    /* indexer query/key width (4 MXFP4 blocks) */
+#define CSA2_LATENT_DIM 512   /* latent KV / window / query width */
+
+enum {
+    CSA2_OK = 0,
+    CSA2_ERR_INVALID = -1,      /* bad pointer, size or range */
+    CSA2_ERR_UNSUPPORTED = -2,  /* valid but not supported by this build */
+    CSA2_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+    CSA2_ERR_HIP = -4           /* a HIP launch failed */
+};
+
+enum { CSA2_OP_INDEX_FULL = 1, CSA2_OP_SPARSE_ATTN = 2 };
+
+/*
+ * csa2_index_scan - the Full layer's indexer scan (first step of the indexer).
+ * For every row r and visible position j computes the score
+ *     s = ((v0 + v1) + v2) + v3,   v_b = sum_{i in block b} q_i k_i   (b = 0..3)
+ * where each 32-element block sum is exact and the four adds are fp32
+ * round-to-nearest-even in this order; and, per 8-position block
+ * [8i, 8i+8) intersected with the visible range, the block maximum.
+ *   scores     f32[R][N_max] or NULL; entries j >= n_visible[r] are not written.
+ *   block_max  f32[R][nblk_max], nblk_max = ceil(N_max/8); blocks past the
+ *              visible range are not written.  Required.
+ * Returns CSA2_OK, CSA2_ERR_INVALID (NULL input, B<1, M<1, N_max<1),
+ * CSA2_ERR_HIP.
+ */
+int csa2_index_scan(const uint8_t* q_codes, const uint8_t* q_scales,
+                    const uint8_t* k_codes, const uint8_t* k_scales,
+                    const int32_t* n_visible, int B, int M, int64_t N_max,
+                    float* scores, float* block_max, void* stream);
+
+/*
+ * csa2_select_blocks - the coarse filter: rank the visible blocks of each row by
+ * (block max descending, block id ascending) and keep the first
+ * min(n_pool, nblk) as the candidate pool, nblk = ceil(n_visible[r]/8).
+ *   block_max    f32[R][nblk_stride] (as written by csa2_index_scan)
+ *   pool_blocks  i32[R][n_pool]: kept block ids ascending, -1 padded.
+ *   topk_blocks  i32[R][k_blocks] or NULL: the first min(k_blocks, nblk) blocks
+ *                of the same ranking (a prefix of the pool when k_blocks <= n_pool).
+ * Returns CSA2_OK, CSA2_ERR_INVALID (NULL, R<1, n_pool<1, k_blocks<0,
+ * nblk_stride<1), CSA2_ERR_HIP.
+ */
+int csa2_select_blocks(const float* block_max, int64_t nblk_stride, const int32_t* n_visible, int R,
+                       int n_pool, int32_t* pool_blocks, int k_blocks, int32_t* topk_blocks, void* stream);
+
+/*
+ * csa2_index_pool - score only inside a pool (Reindex layers, and the Full
+ * layer's own top-k): for row r, pool block i and t = 0..7 the score of position
+ * j = 8*pool_blocks[r][i] + t against the row's own index query, written to
+ * pool_scores[r][8i+t]; slots with pool_blocks < 0 or j >= n_visible[r] are
+ * written as -inf.  Same score definition as csa2_index_scan.
+ *   pool_blocks  i32[R][n_pool], ids in [0, ceil(N_max/8)) or -1.
+ *   pool_scores  f32[R][8*n_pool]
+ * Returns CSA2_OK, CSA2_ERR_INVALID, CSA2_ERR_HIP.
+ */
+int csa2_index_pool(const uint8_t* q_codes, const uint8_t* q_scales,
+                    const uint8_t* k_codes, const uint8_t* k_scales,
+                    const int32_t* pool_blocks, int n_pool, const int32_t* n_visible,
+                    int B, int M, int64_t N_max, float* pool_scores, void* stream);
+
+/*
+ * csa2_topk - keep the first min(k, #valid) slots of each row by (score desc,
+ * position asc) and write their positions ascending, -1 padded, to idx i32[R][k].
+ *   pool layout (pool_blocks != NULL): scores f32[R][8*n_pool]; slot s is position
+ *     8*pool_blocks[r][s/8] + s%8, valid when the block id is >= 0 and the
+ *     position < n_visible[r].  pool_blocks rows must be ascending (as produced by
+ *     csa2_select_blocks) so that slot order is position order.
+ *   full layout (pool_blocks == NULL): scores f32[R][n_pool] with slot s =
+ *     position s, valid when s < n_visible[r] (n_pool is the row stride).
+ * Returns CSA2_OK, CSA2_ERR_INVALID (NULL, R<1, n_pool<1, k<0), CSA2_ERR_HIP.
+ */
+int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, const int32_t* n_visible,
+              int R, int k, int32_t* idx, void* stream);
+
+/*
+ * csa2_index_full - the whole Full-layer indexer: csa2_index_scan, then
+ * csa2_select_blocks (the pool and its first kb = min(k, n_pool) blocks), then
+ * csa2_index_pool over those kb blocks and csa2_topk.  The row's top-k over the
+ * pool equals its top-k over the pool's kb best blocks (every block ranked ahead
+ * of a block holding a selected position contributes its own best position to
+ * the selection, so such a block ranks within the first k), which is why only
+ * those are rescored.
+ *   scores, block_max  optional outputs (NULL to skip; block_max then lives in
+ *                      the workspace).
+ *   pool_blocks  i32[R][n_pool] required;  idx i32[R][k] or NULL (k = 0 skips).
+ *   workspace    device memory of csa2_workspace_bytes(CSA2_OP_INDEX_FULL, ...)
+ * Returns CSA2_OK, CSA2_ERR_INVALID, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP.
+ */
+int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales,
+                    const uint8_t* k_codes, const uint8_t* k_scales,
+                    const int32_t* n_visible, int B, int M, int64_t N_max,
+                    int n_pool, int k, float* scores, float* block_max,
+                    int32_t* pool_blocks, int32_t* idx,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * csa2_sparse_attn - one softmax attention per row and head over the row's k
+ * selected latent entries and its window rows (value = key for both):
+ *     z_i = (q_h . c_i) * sm_scale,  o_h = sum_i softmax(z)_i c_i
+ * over entries c_i = MXFP4-decoded latent rows idx[r][0..k) (entries < 0 or >=
+ * N_max are skipped; a repeated entry counts each time) followed by the FP8
+ * window rows win[seq][win_start[r] + t], t < min(win_len[r], win_max).
+ * An empty entry set gives a zero output row.  fp32 output; the products run on
+ * MFMA with bf16 split operands (query and probabilities as hi+lo pairs, the
+ * decoded values exact in bf16), accumulation in fp32.
+ *   H: a multiple of 16, 16..64.   win_max: 0 <= win_max <= Tw (0: no window;
+ *   win, win_start and win_len may then be NULL).
+ *   win_start[r] + min(win_len[r], win_max) <= Tw is required (not checked).
+ *   workspace: csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, M, 0, H, k + win_max)
+ * Returns CSA2_OK, CSA2_ERR_INVALID, CSA2_ERR_UNSUPPORTED (H), CSA2_ERR_WORKSPACE,
+ * CSA2_ERR_HIP.
+ */
+int csa2_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_scales,
+                     const int32_t* idx, int k,
+                     const uint8_t* win, const int32_t* win_start, const int32_t* win_len, int win_max,
+                     int B, int M, int64_t N_max, int H, int Tw, float sm_scale,
+                     float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * csa2_workspace_bytes - device workspace needed by an entry point.
+ *   CSA2_OP_INDEX_FULL:  (B, M, N_max, k) as passed to csa2_index_full (H unused)
+ *   CSA2_OP_SPARSE_ATTN: (B, M, -, H, k + win_max)
+ * Returns 0 for an unknown op or invalid sizes.
+ */
+size_t csa2_workspace_bytes(int op, int B, int M, int64_t N_max, int H, int k);
+
+/* Static text for a status code. */
+const char* csa2_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,99 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+entry point that include/csa2.h declares, and rejects bad arguments before any
+HIP call (every call below fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import hierarchical_sparse_attention_csa2_amd as csa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = csa2.load_library()
+    names = _declared()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", csa2.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (csa2_\w+)", out))
+    assert set(names) <= exported
+    assert set(csa2.EXPORTED) == set(names)
+
+
+def test_status_strings():
+    assert csa2.status_string(0) == "ok"
+    assert "invalid" in csa2.status_string(-1)
+    assert "workspace" in csa2.status_string(-3)
+    assert csa2.status_string(12345) == "unknown status"
+
+
+NULL = None
+P = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def test_validation_rejects_before_launch():
+    L = csa2.load_library()
+    # index_scan: NULL inputs, bad sizes
+    assert L.csa2_index_scan(NULL, P, P, P, P, 1, 1, 16, NULL, P, NULL) == -1
+    assert L.csa2_index_scan(P, P, P, P, P, 0, 1, 16, NULL, P, NULL) == -1
+    assert L.csa2_index_scan(P, P, P, P, P, 1, 0, 16, NULL, P, NULL) == -1
+    assert L.csa2_index_scan(P, P, P, P, P, 1, 1, 0, NULL, P, NULL) == -1
+    assert L.csa2_index_scan(P, P, P, P, P, 1, 1, 16, NULL, NULL, NULL) == -1
+    # select_blocks
+    assert L.csa2_select_blocks(P, 2, P, 1, 0, P, 0, NULL, NULL) == -1
+    assert L.csa2_select_blocks(P, 2, P, 1, 4, P, 2, NULL, NULL) == -1
+    assert L.csa2_select_blocks(P, 0, P, 1, 4, P, 0, NULL, NULL) == -1
+    # index_pool
+    assert L.csa2_index_pool(P, P, P, P, NULL, 4, P, 1, 1, 16, P, NULL) == -1
+    assert L.csa2_index_pool(P, P, P, P, P, 0, P, 1, 1, 16, P, NULL) == -1
+    # topk
+    assert L.csa2_topk(NULL, P, 4, P, 1, 8, P, NULL) == -1
+    assert L.csa2_topk(P, P, 4, P, 1, -1, P, NULL) == -1
+    assert L.csa2_topk(P, P, 4, P, 0, 8, P, NULL) == -1
+    assert L.csa2_topk(P, P, 4, P, 1, 0, P, NULL) == 0          # k = 0: nothing to do
+    # index_full: workspace too small, missing idx
+    assert L.csa2_index_full(P, P, P, P, P, 1, 1, 64, 4, 8, NULL, NULL, P, P, NULL, 0, NULL) == -3
+    assert L.csa2_index_full(P, P, P, P, P, 1, 1, 64, 4, 8, NULL, NULL, P, NULL, P, 1 << 20, NULL) == -1
+    assert L.csa2_index_full(P, P, P, P, P, 1, 1, 64, 0, 8, NULL, NULL, P, P, P, 1 << 20, NULL) == -1
+    # sparse_attn: unsupported head counts, bad window, missing workspace
+    f = ctypes.c_float(0.04)
+    assert L.csa2_sparse_attn(P, P, P, P, 8, P, P, P, 4, 1, 1, 64, 24, 8, f, P, P, 1 << 20, NULL) == -2
+    assert L.csa2_sparse_attn(P, P, P, P, 8, P, P, P, 4, 1, 1, 64, 128, 8, f, P, P, 1 << 20, NULL) == -2
+    assert L.csa2_sparse_attn(P, P, P, P, 8, P, P, P, 9, 1, 1, 64, 64, 8, f, P, P, 1 << 20, NULL) == -1
+    assert L.csa2_sparse_attn(P, P, P, NULL, 8, P, P, P, 4, 1, 1, 64, 64, 8, f, P, P, 1 << 20, NULL) == -1
+    assert L.csa2_sparse_attn(P, P, P, P, 512, P, P, P, 128, 1, 1, 64, 64, 128, f, P, NULL, 0, NULL) == -3
+    assert L.csa2_sparse_attn(P, P, P, P, 8, P, P, P, 4, 1, 1, 64, 64, 8, ctypes.c_float(float("nan")), P, P,
+                              1 << 20, NULL) == -1
+
+
+def test_workspace_bytes():
+    L = csa2.load_library()
+    # index_full: block maxima + the first k blocks + their scores
+    n = csa2.csa2_workspace_bytes(csa2.CSA2_OP_INDEX_FULL, 4, 1, 524288, 0, 512)
+    assert n >= 4 * 65536 * 4 + 4 * 512 * 4 + 4 * 4096 * 4
+    assert csa2.csa2_workspace_bytes(csa2.CSA2_OP_INDEX_FULL, 0, 1, 16, 0, 8) == 0
+    assert csa2.csa2_workspace_bytes(99, 1, 1, 16, 0, 8) == 0
+    # attention: split partials only when a row is split over several workgroups
+    a = csa2.csa2_workspace_bytes(csa2.CSA2_OP_SPARSE_ATTN, 4, 1, 0, 64, 640)
+    assert a > 0 and a % (64 * 514 * 4) == 0
+    assert csa2.csa2_workspace_bytes(csa2.CSA2_OP_SPARSE_ATTN, 4, 1, 0, 24, 640) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 64), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        csa2.csa2_index_scan(x, x, x, x, torch.zeros(1, dtype=torch.int32), 1, 1, 1,
+                             torch.zeros((1, 1), dtype=torch.float32))

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, on the same
+seeded bytes.  Scores, block maxima, pools and selected indices must be
+bit-exact; attention outputs must be within 1e-3 (max abs) of the fp64 oracle.
+
+Small cases span several workgroups and ragged tails (visible counts that are
+not multiples of 8 or of the scan chunk, partial pools, k > pool size), tie-
+heavy data and adversarial scale exponents.  The workload-size cases live in
+test_gpu_workloads.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_csa2_amd as csa2
+import oracle
+from hierarchical_sparse_attention_csa2_amd import pipeline
+from synth import Workload
+
+from gpu_cases import SM_SCALE, dev, f32_bits, host_inputs, oracle_attn, oracle_full, say
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-3
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa2.load_library()
+
+
+def _run_scan(w, c, l):
+    nblk = (w.N + 7) // 8
+    scores = torch.full((w.R, w.N), float("nan"), device="cuda")
+    bmax = torch.full((w.R, nblk), float("nan"), device="cuda")
+    csa2.csa2_index_scan(l["q_codes"], l["q_scales"], c["k_codes"], c["k_scales"], l["n_visible"], w.B, w.M, w.N,
+                         bmax, scores=scores)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy(), bmax.cpu().numpy()
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread"])
+@pytest.mark.parametrize("N,nv", [(3000, [3000, 2995, 1]), (4099, [4099, 2048, 2049]), (40, [0, 40, 17])])
+def test_index_scan_bitexact(kind, N, nv):
+    w = Workload("scan", 1234 + N, B=3, N=N)
+    cache, (lay,) = host_inputs(w, kind=kind)
+    lay["n_visible"] = np.array(nv, np.int32)
+    say(f"scan N={N} nv={nv} kind={kind}")
+    scores, bmax = _run_scan(w, dev(cache), dev(lay))
+    ref = oracle_full(w, cache, lay, want_scores=True, want_block_max=True)
+    for r in range(w.R):
+        n = nv[r]
+        assert np.array_equal(f32_bits(scores[r, :n]), f32_bits(ref["scores"][r, :n])), r
+        nb = (n + 7) // 8
+        assert np.array_equal(f32_bits(bmax[r, :nb]), f32_bits(ref["block_max"][r, :nb])), r
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread"])
+@pytest.mark.parametrize("N,n_pool,k,nv", [
+    (4096, 2048, 512, [4096, 4000, 3333]),      # pool covers all blocks
+    (20000, 2048, 512, [20000, 19999, 8191]),   # pool smaller than the block count
+    (2000, 16, 512, [2000, 1999, 5]),           # pool smaller than k
+    (300, 8, 64, [300, 64, 9]),
+    (150000, 2048, 512, [150000, 131071, 65537]),
+])
+def test_index_full_bitexact(kind, N, n_pool, k, nv):
+    w = Workload("full", 99 + N + n_pool, B=3, N=N, n_pool=n_pool, k=k)
+    cache, (lay,) = host_inputs(w, kind=kind)
+    lay["n_visible"] = np.array(nv, np.int32)
+    c, l = dev(cache), dev(lay)
+    say(f"index_full N={N} pool={n_pool} k={k} kind={kind}")
+    ref = oracle_full(w, cache, lay)
+    # composite call
+    pool = torch.empty((w.R, n_pool), dtype=torch.int32, device="cuda")
+    idx = torch.empty((w.R, k), dtype=torch.int32, device="cuda")
+    csa2.csa2_index_full(l["q_codes"], l["q_scales"], c["k_codes"], c["k_scales"], l["n_visible"], w.B, 1, N,
+                         n_pool, k, pool, idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.cpu().numpy(), ref["pool_blocks"])
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    # staged calls (the bench's path)
+    st = pipeline.Step(("full",), w.B, 1, N, H=64, n_pool=n_pool, k=k)
+    st.full_index(pipeline.cache_from(c), pipeline.layer_from(l), st.idx[0])
+    torch.cuda.synchronize()
+    assert np.array_equal(st.pool.cpu().numpy(), ref["pool_blocks"])
+    assert np.array_equal(st.idx[0].cpu().numpy(), ref["idx"])
+
+
+def test_select_blocks_and_topk_full_layout():
+    """csa2_select_blocks (pool + first k blocks) and csa2_topk over full score
+    rows, against the oracle's sorts."""
+    w = Workload("sel", 4242, B=4, N=70000, n_pool=2048, k=512)
+    cache, (lay,) = host_inputs(w, kind="ties")
+    lay["n_visible"] = np.array([70000, 69999, 16385, 12], np.int32)
+    c, l = dev(cache), dev(lay)
+    scores, bmax = _run_scan(w, c, l)
+    ref = oracle_full(w, cache, lay, want_scores=True)
+    R = w.R
+    pool = torch.empty((R, 2048), dtype=torch.int32, device="cuda")
+    tb = torch.empty((R, 300), dtype=torch.int32, device="cuda")
+    csa2.csa2_select_blocks(torch.from_numpy(bmax).cuda(), l["n_visible"], 2048, pool, 300, tb)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.cpu().numpy(), ref["pool_blocks"])
+    # the first 300 blocks = the pool of an oracle run with n_pool = 300
+    w300 = Workload("sel", 4242, B=4, N=70000, n_pool=300, k=512)
+    assert np.array_equal(tb.cpu().numpy(), oracle_full(w300, cache, lay)["pool_blocks"])
+    # top-k over the full score rows (global top-k) equals the oracle's global top-k
+    for k in (1, 512, 5000):
+        idx = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        csa2.csa2_topk(torch.from_numpy(scores).cuda(), l["n_visible"], k, idx)
+        torch.cuda.synchronize()
+        want = oracle.topk_full(np.nan_to_num(ref["scores"], nan=-np.inf), lay["n_visible"], k)
+        assert np.array_equal(idx.cpu().numpy(), want), k
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread"])
+def test_reindex_pool_scores_and_topk(kind):
+    """A Reindex layer: its own index query scored only inside the Full pool."""
+    w = Workload("reidx", 777, B=3, N=50000, n_pool=2048, k=512)
+    cache, (lay0, lay1) = host_inputs(w, layers=2, kind=kind)
+    nv = np.array([50000, 49999, 10003], np.int32)
+    lay0["n_visible"] = nv
+    lay1["n_visible"] = nv
+    c, l1 = dev(cache), dev(lay1)
+    pool_np = oracle_full(w, cache, lay0)["pool_blocks"]
+    pool = torch.from_numpy(pool_np).cuda()
+    ps = torch.empty((w.R, 8 * 2048), dtype=torch.float32, device="cuda")
+    csa2.csa2_index_pool(l1["q_codes"], l1["q_scales"], c["k_codes"], c["k_scales"], pool, l1["n_visible"], w.B, 1,
+                         w.N, ps)
+    idx = torch.empty((w.R, 512), dtype=torch.int32, device="cuda")
+    csa2.csa2_topk(ps, l1["n_visible"], 512, idx, pool_blocks=pool)
+    torch.cuda.synchronize()
+    ref_ps = oracle.index_pool(lay1["q_codes"], lay1["q_scales"], cache["k_codes"], cache["k_scales"], pool_np, nv,
+                               w.B, 1, w.N)
+    assert np.array_equal(f32_bits(ps.cpu().numpy()), f32_bits(ref_ps))
+    ref_idx = oracle.topk_pool(ref_ps, pool_np, nv, 512)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
+def _attn_case(w, cache, lay, idx_np, win_max, H=None):
+    c, l = dev(cache), dev(lay)
+    out = torch.full((w.R, w.H, 512), float("nan"), device="cuda")
+    idx = torch.from_numpy(idx_np).cuda() if idx_np.shape[1] else None
+    csa2.csa2_sparse_attn(l["q"], c["c_codes"], c["c_scales"], idx, l["win"] if win_max else None,
+                          l["win_start"] if win_max else None, l["win_len"] if win_max else None, win_max, w.B, w.M,
+                          w.N, SM_SCALE, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("H", [16, 32, 64])
+@pytest.mark.parametrize("k,win_lens", [(512, [128, 100, 0, 1]), (0, [128, 7, 128, 64]), (37, [0, 0, 0, 0]),
+                                        (1000, [128, 128, 3, 0])])
+def test_sparse_attn_vs_oracle(H, k, win_lens):
+    w = Workload("attn", 31 + H + k, B=4, N=3000, H=H, k=max(k, 1))
+    cache, (lay,) = host_inputs(w)
+    lay["win_len"] = np.array(win_lens, np.int32)
+    rng = np.random.default_rng(H * 1000 + k)
+    idx = np.sort(rng.choice(w.N, size=(w.R, k), replace=True), axis=1).astype(np.int32)
+    if k:
+        idx[1, k // 2:] = -1          # a padded row
+        idx[2, :] = idx[2, 0]         # one entry repeated k times
+    win_max = 128
+    say(f"attn H={H} k={k} win={win_lens}")
+    got = _attn_case(w, cache, lay, idx, win_max)
+    ref = oracle_attn(w, cache, lay, idx)
+    err = np.max(np.abs(got - ref))
+    say(f"  max abs err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= ATOL
+
+
+def test_sparse_attn_no_window_and_empty():
+    w = Workload("attn0", 5, B=2, N=500, H=64, k=64, win_len=0)
+    cache, (lay,) = host_inputs(w)
+    idx = np.full((2, 64), -1, np.int32)
+    idx[0, :10] = np.arange(10)
+    got = _attn_case(w, cache, lay, idx, 0)
+    ref = oracle_attn(w, cache, lay, idx)
+    assert np.max(np.abs(got - ref)) <= ATOL
+    assert (got[1] == 0).all()        # empty set -> zeros
+
+
+def test_dense_equivalence_on_gpu():
+    """Check (b): k covering every entry gives dense attention over cache + window."""
+    w = Workload("dense", 8, B=2, N=700, H=64, k=700)
+    cache, (lay,) = host_inputs(w)
+    idx = np.tile(np.arange(700, dtype=np.int32), (2, 1))
+    got = _attn_case(w, cache, lay, idx, 128)
+    dec = oracle.mxfp4_decode(cache["c_codes"], cache["c_scales"])
+    win = torch.from_numpy(lay["win"]).view(torch.float8_e4m3fn).double().numpy()
+    for r in range(2):
+        rows = np.concatenate([dec[r], win[r]])
+        z = torch.from_numpy(lay["q"][r].astype(np.float64)) @ torch.from_numpy(rows).T * float(SM_SCALE)
+        ref = (torch.softmax(z, -1) @ torch.from_numpy(rows)).numpy()
+        assert np.max(np.abs(got[r] - ref)) <= ATOL
+
+
+def test_chain_full_reindex_reindex_reuse():
+    """Full -> Reindex -> Reindex -> Reuse: shared pool and latent, own queries and
+    windows; check (d): the Reuse layer equals attention with the previous indices."""
+    w = Workload("chain", 4321, B=4, N=30000, layers=("full", "reindex", "reindex", "reuse"))
+    cache, lays = host_inputs(w, layers=4)
+    for d in lays:
+        d["n_visible"] = np.array([30000, 29993, 17000, 4096], np.int32)
+    c = dev(cache)
+    ls = [dev(d) for d in lays]
+    st = pipeline.Step(w.layers, w.B, 1, w.N)
+    pool, idxs, outs = st.run(pipeline.cache_from(c), [pipeline.layer_from(d) for d in ls])
+    torch.cuda.synchronize()
+    ref_full = oracle_full(w, cache, lays[0])
+    assert np.array_equal(pool.cpu().numpy(), ref_full["pool_blocks"])
+    ref_idx = [ref_full["idx"]]
+    for L in (1, 2):
+        ps = oracle.index_pool(lays[L]["q_codes"], lays[L]["q_scales"], cache["k_codes"], cache["k_scales"],
+                               ref_full["pool_blocks"], lays[L]["n_visible"], w.B, 1, w.N)
+        ref_idx.append(oracle.topk_pool(ps, ref_full["pool_blocks"], lays[L]["n_visible"], 512))
+    ref_idx.append(ref_idx[2])
+    for L in range(3):
+        assert np.array_equal(idxs[L].cpu().numpy(), ref_idx[L]), L
+    for L in range(4):
+        ref = oracle_attn(w, cache, lays[L], ref_idx[L])
+        err = np.max(np.abs(outs[L].cpu().numpy() - ref))
+        say(f"chain layer {L} max abs err {err:.3e}")
+        assert err <= ATOL
+    # check (d): Reuse output equals attention of its inputs with the previous layer's indices
+    again = torch.empty_like(outs[3])
+    csa2.csa2_sparse_attn(ls[3]["q"], c["c_codes"], c["c_scales"], idxs[2], ls[3]["win"], ls[3]["win_start"],
+                          ls[3]["win_len"], 128, w.B, 1, w.N, SM_SCALE, again)
+    torch.cuda.synchronize()
+    assert torch.equal(again, outs[3])
+
+
+def test_deterministic_reruns():
+    w = Workload("det", 55, B=4, N=60000)
+    cache, (lay,) = host_inputs(w, kind="ties")
+    c, l = dev(cache), dev(lay)
+    st = pipeline.Step(("full",), w.B, 1, w.N, keep_scores=True)
+    res = []
+    for _ in range(2):
+        pool, idxs, outs = st.run(pipeline.cache_from(c), [pipeline.layer_from(l)])
+        torch.cuda.synchronize()
+        res.append((pool.clone(), idxs[0].clone(), outs[0].clone(), st.scores.clone(), st.block_max.clone()))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)

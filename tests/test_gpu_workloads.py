@@ -1,0 +1,62 @@
+"""GPU parity at the five workload sizes, in the launch configuration bench.py
+times (pipeline.Step, staged calls).  Pools and indices bit-exact, attention
+within 1e-3 of the fp64 oracle, on all rows where the oracle is quick and on
+sampled rows otherwise."""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_csa2_amd as csa2
+import oracle
+import synth
+from hierarchical_sparse_attention_csa2_amd import pipeline
+
+from gpu_cases import dev, oracle_attn, oracle_full, say
+
+pytestmark = pytest.mark.gpu
+ATOL = 1e-3
+
+SAMPLES = {"c1": None, "c2": None, "c3": None, "c4": [0, 1, 31, 62, 63], "c5": [0, 1, 1000, 2047, 4094, 4095]}
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa2.load_library()
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_workload_parity(name):
+    w = synth.WORKLOADS[name]
+    say(f"workload {name}: {w.notes}")
+    cache = synth.gen_cache(w)
+    lays = [synth.gen_layer(w, layer=L, need_index_query=(m != "reuse")) for L, m in enumerate(w.layers)]
+    c = dev(cache)
+    ls = [dev(d) for d in lays]
+    st = pipeline.Step(w.layers, w.B, w.M, w.N, H=w.H, n_pool=w.n_pool, k=w.k, win_max=w.win_len)
+    pool, idxs, outs = st.run(pipeline.cache_from(c), [pipeline.layer_from(d) for d in ls])
+    torch.cuda.synchronize()
+    rows = SAMPLES[name]
+    rows_np = np.arange(w.R) if rows is None else np.asarray(rows)
+    say(f"  GPU done; oracle on {len(rows_np)} rows")
+    ref_full = oracle_full(w, cache, lays[0], rows=rows_np)
+    assert np.array_equal(pool.cpu().numpy()[rows_np], ref_full["pool_blocks"])
+    ref_idx = [ref_full["idx"]]
+    prev = ref_full["idx"]
+    for L, mode in enumerate(w.layers[1:], start=1):
+        if mode == "reindex":
+            d = lays[L]
+            ps = oracle.index_pool(d["q_codes"][rows_np], d["q_scales"][rows_np], cache["k_codes"][rows_np],
+                                   cache["k_scales"][rows_np], ref_full["pool_blocks"], d["n_visible"][rows_np],
+                                   len(rows_np), 1, w.N)
+            prev = oracle.topk_pool(ps, ref_full["pool_blocks"], d["n_visible"][rows_np], w.k)
+        ref_idx.append(prev)
+    for L, mode in enumerate(w.layers):
+        if mode != "reuse":
+            assert np.array_equal(idxs[L].cpu().numpy()[rows_np], ref_idx[L]), (name, L)
+        ref = oracle_attn(w, cache, lays[L], ref_idx[L], rows=rows_np)
+        got = outs[L].cpu().numpy()[rows_np]
+        err = float(np.max(np.abs(got - ref)))
+        say(f"  layer {L} ({mode}) idx ok, attention max abs err {err:.3e}")
+        assert err <= ATOL
