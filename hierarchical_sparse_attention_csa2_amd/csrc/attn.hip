@@ -56,6 +56,88 @@ __device__ __forceinline__ bf16x8_t zero_bf16x8() {
   return z;
 }
 
+enum { kLatentRows = 0, kWindowRows = 1, kMixedRows = 2 };
+
+__device__ __forceinline__ bf16x8_t decode_latent8(uint32_t wcode, uint32_t scale_byte) {
+  const float sc = e8m0_to_f32(scale_byte);
+  const bf16x2_t p0 = fp4x2_to_bf16<0>(wcode, sc);
+  const bf16x2_t p1 = fp4x2_to_bf16<1>(wcode, sc);
+  const bf16x2_t p2 = fp4x2_to_bf16<2>(wcode, sc);
+  const bf16x2_t p3 = fp4x2_to_bf16<3>(wcode, sc);
+  return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ bf16x8_t decode_fp8x8(uint32_t w0, uint32_t w1) {
+  const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+  const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+  const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+  const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+  return bf16x8_t{(__bf16)f0[0], (__bf16)f0[1], (__bf16)f1[0], (__bf16)f1[1],
+                  (__bf16)f2[0], (__bf16)f2[1], (__bf16)f3[0], (__bf16)f3[1]};
+}
+
+// Decode one chunk (64 entries x 512 dims) into the row-major and the
+// transposed LDS copies.  Thread tiles are 4 entries x 8 dims; for chunks of a
+// single row kind every gather of the thread is issued before any conversion.
+template <int NP, int KIND>
+__device__ __forceinline__ void decode_chunk(const AttnParams& a, const int64_t* sOff, const int* sType,
+                                             unsigned long long vmask, __bf16* sK, __bf16* sVt, int tid) {
+  constexpr int kTPT = (kChunk / 4) * 64 / (NP * 128);   // tiles per thread
+  constexpr int kGroup = kTPT > 2 ? kTPT / 2 : 1;         // tiles whose gathers are in flight together
+#pragma unroll
+  for (int j0 = 0; j0 < kTPT; j0 += kGroup) {
+    uint32_t raw0[kGroup][4], raw1[kGroup][4];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const int T = tid + (j0 + j) * NP * 128;
+      const int eg = T & 15, dg = T >> 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t off = sOff[4 * eg + i];
+        if (KIND == kLatentRows) {
+          raw0[j][i] = *reinterpret_cast<const uint32_t*>(a.c_codes + off * 256 + 4 * dg);
+          raw1[j][i] = a.c_scales[off * 16 + (dg >> 2)];
+        } else if (KIND == kWindowRows) {
+          const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(a.win + off * 512 + 8 * dg);
+          raw0[j][i] = wb[0];
+          raw1[j][i] = wb[1];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const int T = tid + (j0 + j) * NP * 128;
+      const int eg = T & 15, dg = T >> 4;
+      bf16x8_t v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * eg + i;
+        if (!((vmask >> e) & 1ull)) {
+          v[i] = zero_bf16x8();
+        } else if (KIND == kLatentRows) {
+          v[i] = decode_latent8(raw0[j][i], raw1[j][i]);
+        } else if (KIND == kWindowRows) {
+          v[i] = decode_fp8x8(raw0[j][i], raw1[j][i]);
+        } else {
+          const int64_t off = sOff[e];
+          if (sType[e] == 0) {
+            v[i] = decode_latent8(*reinterpret_cast<const uint32_t*>(a.c_codes + off * 256 + 4 * dg),
+                                  a.c_scales[off * 16 + (dg >> 2)]);
+          } else {
+            const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(a.win + off * 512 + 8 * dg);
+            v[i] = decode_fp8x8(wb[0], wb[1]);
+          }
+        }
+        *reinterpret_cast<bf16x8_t*>(&sK[e * kKLd + 8 * dg]) = v[i];
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        *reinterpret_cast<bf16x4_t*>(&sVt[(8 * dg + d) * kVLd + 4 * eg]) =
+            bf16x4_t{v[0][d], v[1][d], v[2][d], v[3][d]};
+    }
+  }
+}
+
 template <int NP>
 __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) {
   __shared__ __attribute__((aligned(16))) __bf16 sK[kChunk * kKLd];
@@ -83,6 +165,17 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
   const int E = a.k + wl;
   const int ws0 = a.win_max > 0 ? a.win_start[r] : 0;
 
+  const int c_begin = split * a.chunks_per_split;
+  int c_end = c_begin + a.chunks_per_split;
+  c_end = c_end < a.n_chunks ? c_end : a.n_chunks;
+
+  // the first chunk's selected indices load while the query loads
+  int64_t idx_next = -1;
+  if (tid < kChunk && c_begin < c_end) {
+    const int e = c_begin * kChunk + tid;
+    if (e < a.k) idx_next = a.idx[(int64_t)r * a.k + e];
+  }
+
   // query operands (B of S^T = C Q^T): head h, dims dbase + 32s + 8g .. +8, prescaled
   bf16x8_t qhi[8], qlo[8];
   {
@@ -107,30 +200,32 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  const int c_begin = split * a.chunks_per_split;
-  int c_end = c_begin + a.chunks_per_split;
-  c_end = c_end < a.n_chunks ? c_end : a.n_chunks;
-
   for (int c = c_begin; c < c_end; ++c) {
     const int ebase = c * kChunk;
     if (ebase >= E) break;
     __syncthreads();   // previous chunk's LDS reads are done
     // 1. entry table
     if (tid < kChunk) {
+      // masked entries keep a readable row (the sequence's first) and are zeroed
       const int e = ebase + tid;
-      int64_t off = -1;
-      int type = 0;
+      const int type = e < a.k ? 0 : 1;
+      int64_t off = type == 0 ? seq * a.N_max : seq * a.Tw;
+      bool valid = false;
+      const int64_t p = idx_next;
+      // prefetch the next chunk's indices
+      idx_next = -1;
+      if (c + 1 < c_end && e + kChunk < a.k) idx_next = a.idx[(int64_t)r * a.k + e + kChunk];
       if (e < a.k) {
-        const int64_t p = a.idx[(int64_t)r * a.k + e];
-        if (p >= 0 && p < a.N_max) off = seq * a.N_max + p;
+        valid = p >= 0 && p < a.N_max;
+        if (valid) off += p;
       } else if (e < E) {
         const int64_t t = (int64_t)ws0 + (e - a.k);
-        if (t >= 0 && t < a.Tw) off = seq * a.Tw + t;
-        type = 1;
+        valid = t >= 0 && t < a.Tw;
+        if (valid) off += t;
       }
       sOff[tid] = off;
       sType[tid] = type;
-      const unsigned long long m = __ballot(off >= 0);
+      const unsigned long long m = __ballot(valid);
       if (tid == 0) sMask = m;
     }
     __syncthreads();
@@ -138,40 +233,12 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
     if (vmask == 0ull) continue;
 
     // 2. decode 4 entries x 8 dims per tile into both LDS copies
-    for (int T = tid; T < (kChunk / 4) * 64; T += NP * 128) {
-      const int eg = T & 15;
-      const int dg = T >> 4;
-      bf16x8_t v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * eg + i;
-        const int64_t off = sOff[e];
-        if (off < 0) {
-          v[i] = zero_bf16x8();
-        } else if (sType[e] == 0) {
-          const uint32_t wcode = *reinterpret_cast<const uint32_t*>(a.c_codes + off * 256 + 4 * dg);
-          const float sc = e8m0_to_f32(a.c_scales[off * 16 + (dg >> 2)]);
-          const bf16x2_t p0 = fp4x2_to_bf16<0>(wcode, sc);
-          const bf16x2_t p1 = fp4x2_to_bf16<1>(wcode, sc);
-          const bf16x2_t p2 = fp4x2_to_bf16<2>(wcode, sc);
-          const bf16x2_t p3 = fp4x2_to_bf16<3>(wcode, sc);
-          v[i] = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        } else {
-          const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(a.win + off * 512 + 8 * dg);
-          const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(wb[0], false);
-          const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(wb[0], true);
-          const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8(wb[1], false);
-          const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8(wb[1], true);
-          v[i] = bf16x8_t{(__bf16)f0[0], (__bf16)f0[1], (__bf16)f1[0], (__bf16)f1[1],
-                          (__bf16)f2[0], (__bf16)f2[1], (__bf16)f3[0], (__bf16)f3[1]};
-        }
-        *reinterpret_cast<bf16x8_t*>(&sK[e * kKLd + 8 * dg]) = v[i];
-      }
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-        *reinterpret_cast<bf16x4_t*>(&sVt[(8 * dg + d) * kVLd + 4 * eg]) =
-            bf16x4_t{v[0][d], v[1][d], v[2][d], v[3][d]};
-    }
+    if (ebase + kChunk <= a.k)
+      decode_chunk<NP, kLatentRows>(a, sOff, sType, vmask, sK, sVt, tid);
+    else if (ebase >= a.k)
+      decode_chunk<NP, kWindowRows>(a, sOff, sType, vmask, sK, sVt, tid);
+    else
+      decode_chunk<NP, kMixedRows>(a, sOff, sType, vmask, sK, sVt, tid);
     __syncthreads();
 
     // 3. partial S^T[64 entries x 16 heads] over this wave's 256 dims
@@ -279,25 +346,26 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+// One workgroup per (row, head), one thread per output dim.
+__global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, int splits, int H,
                                                            float* __restrict__ out) {
-  const int r = blockIdx.x;
-  for (int hd = threadIdx.x; hd < H * 512; hd += 256) {
-    const int h = hd >> 9;
-    float M = -__builtin_inff();
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(((int64_t)r * splits + s) * H + h) * 2]);
-    float L = 0.f, acc = 0.f;
-    if (M != -__builtin_inff()) {
-      for (int s = 0; s < splits; ++s) {
-        const int64_t slot = ((int64_t)r * splits + s) * H + h;
-        const float wgt = exp2f(part_ml[2 * slot] - M);
-        L += wgt * part_ml[2 * slot + 1];
-        acc += wgt * part_o[slot * 512 + (hd & 511)];
-      }
+  const int r = blockIdx.y;
+  const int h = blockIdx.x;
+  const int d = threadIdx.x;
+  const int64_t base = (int64_t)r * splits * H + h;     // slot of split s: base + s*H
+  float M = -__builtin_inff();
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[2 * (base + (int64_t)s * H)]);
+  float L = 0.f, acc = 0.f;
+  if (M != -__builtin_inff()) {
+    for (int s = 0; s < splits; ++s) {
+      const int64_t slot = base + (int64_t)s * H;
+      const float wgt = exp2f(part_ml[2 * slot] - M);
+      L += wgt * part_ml[2 * slot + 1];
+      acc += wgt * part_o[slot * 512 + d];
     }
-    out[(int64_t)r * H * 512 + hd] = L > 0.f ? acc / L : 0.f;
   }
+  out[((int64_t)r * H + h) * 512 + d] = L > 0.f ? acc / L : 0.f;
 }
 
 int attn_splits(int R, int k, int win_max) {
@@ -354,14 +422,13 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
   switch (NP) {
     case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(128), 0, stream, a); break;
     case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, dim3(256), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(sparse_attn_kernel<3>, grid, dim3(384), 0, stream, a); break;
     case 4: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, dim3(512), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.splits == 1) return err;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)R), dim3(256), 0, stream, a.part_o, a.part_ml, a.splits,
-                     L.H, L.out);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)L.H, (unsigned)R), dim3(512), 0, stream, a.part_o,
+                     a.part_ml, a.splits, L.H, L.out);
   return hipGetLastError();
 }
 

@@ -135,7 +135,7 @@ int csa2_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_sc
   if (k > 0 && (!idx || !c_codes || !c_scales || N_max < 1)) return CSA2_ERR_INVALID;
   if (win_max > 0 && (!win || !win_start || !win_len)) return CSA2_ERR_INVALID;
   if (!(sm_scale == sm_scale)) return CSA2_ERR_INVALID;
-  if (H < 16 || H > 64 || H % 16 != 0) return CSA2_ERR_UNSUPPORTED;
+  if (H != 16 && H != 32 && H != 64) return CSA2_ERR_UNSUPPORTED;
   const int R = B * M;
   const size_t need = csa2::attn_workspace_bytes(R, H, k + win_max);
   if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
@@ -169,7 +169,7 @@ size_t csa2_workspace_bytes(int op, int B, int M, int64_t N_max, int H, int k) {
     return full_ws(R, N_max, k).total;
   }
   if (op == CSA2_OP_SPARSE_ATTN) {
-    if (H < 16 || H > 64 || H % 16 != 0) return 0;
+    if (H != 16 && H != 32 && H != 64) return 0;
     return csa2::attn_workspace_bytes((int)R, H, k);
   }
   return 0;

@@ -81,23 +81,24 @@ class Step:
                                    dtype=torch.uint8, device=dev)
 
     # the Full layer's indexer, either as the composite call or stage by stage
-    def full_index(self, cache: Cache, li: LayerInputs, idx: torch.Tensor, scan_events=None):
+    def full_index(self, cache: Cache, li: LayerInputs, idx: torch.Tensor):
         B, M, N = self.B, self.M, self.N
         if not self.staged:
             csa2_index_full(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, B, M, N,
                             self.n_pool, self.k, self.pool, idx, self.ws_full, scores=self.scores,
                             block_max=self.block_max)
             return
-        if scan_events is not None:
-            scan_events[0].record()
         csa2_index_scan(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, B, M, N,
                         self.block_max, scores=self.scores)
-        if scan_events is not None:
-            scan_events[1].record()
         csa2_select_blocks(self.block_max, li.n_visible, self.n_pool, self.pool, self.kb, self.topk_blocks)
         csa2_index_pool(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, self.topk_blocks, li.n_visible,
                         B, M, N, self.topk_scores)
         csa2_topk(self.topk_scores, li.n_visible, self.k, idx, pool_blocks=self.topk_blocks)
+
+    def scan_only(self, cache: Cache, li: LayerInputs):
+        """The Full layer's scan alone (block maxima into this step's buffer)."""
+        csa2_index_scan(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, self.B, self.M,
+                        self.N, self.block_max, scores=self.scores)
 
     def reindex(self, cache: Cache, li: LayerInputs, idx: torch.Tensor):
         csa2_index_pool(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, self.pool, li.n_visible,
@@ -108,13 +109,13 @@ class Step:
         csa2_sparse_attn(li.q, cache.c_codes, cache.c_scales, idx, li.win, li.win_start, li.win_len, self.win_max,
                          self.B, self.M, self.N, self.sm_scale, out, self.ws_attn)
 
-    def run(self, cache: Cache, layers, scan_events=None):
+    def run(self, cache: Cache, layers):
         """layers: one LayerInputs per mode.  Returns (pool, [idx per layer], [out per layer])."""
         prev_idx = None
         for li_no, (mode, li) in enumerate(zip(self.modes, layers)):
             idx = self.idx[li_no]
             if mode == "full":
-                self.full_index(cache, li, idx, scan_events)
+                self.full_index(cache, li, idx)
                 cur = idx
             elif mode == "reindex":
                 self.reindex(cache, li, idx)

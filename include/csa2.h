@@ -159,7 +159,7 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales,
  * An empty entry set gives a zero output row.  fp32 output; the products run on
  * MFMA with bf16 split operands (query and probabilities as hi+lo pairs, the
  * decoded values exact in bf16), accumulation in fp32.
- *   H: a multiple of 16, 16..64.   win_max: 0 <= win_max <= Tw (0: no window;
+ *   H: 16, 32 or 64.   win_max: 0 <= win_max <= Tw (0: no window;
  *   win, win_start and win_len may then be NULL).
  *   win_start[r] + min(win_len[r], win_max) <= Tw is required (not checked).
  *   workspace: csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, M, 0, H, k + win_max)
