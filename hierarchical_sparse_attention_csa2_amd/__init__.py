@@ -57,8 +57,8 @@ def load_library(path: str = LIB_PATH):
                            "(there is no CPU fallback)")
     L = ctypes.CDLL(path)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-    L.csa2_index_scan.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, vp]
-    L.csa2_select_blocks.argtypes = [vp, i64, vp, i32, i32, vp, i32, vp, vp]
+    L.csa2_index_scan.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, vp]
+    L.csa2_select_blocks.argtypes = [vp, vp, i64, vp, i32, i32, vp, i32, vp, vp]
     L.csa2_index_pool.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i64, vp, vp]
     L.csa2_topk.argtypes = [vp, vp, i64, vp, i32, i32, vp, vp]
     L.csa2_index_full.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -127,22 +127,25 @@ def csa2_workspace_bytes(op: int, B: int, M: int, N_max: int, H: int, k: int) ->
 
 
 def csa2_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, block_max, scores=None,
-                    stream=None):
+                    super_max=None, stream=None):
     R = B * M
     nblk = (N_max + 7) // 8
+    nsup = (N_max + 63) // 64
     st = load_library().csa2_index_scan(
         _dev(q_codes, "q_codes", U8, (R, 64)), _dev(q_scales, "q_scales", U8, (R, 4)),
         _dev(k_codes, "k_codes", U8, numel=B * N_max * 64), _dev(k_scales, "k_scales", U8, numel=B * N_max * 4),
         _dev(n_visible, "n_visible", I32, (R,)), B, M, N_max,
         _dev(scores, "scores", F32, (R, N_max), optional=True), _dev(block_max, "block_max", F32, (R, nblk)),
-        _stream(stream))
+        _dev(super_max, "super_max", F32, (R, nsup), optional=True), _stream(stream))
     _check("csa2_index_scan", st)
 
 
-def csa2_select_blocks(block_max, n_visible, n_pool, pool_blocks, k_blocks=0, topk_blocks=None, stream=None):
+def csa2_select_blocks(block_max, n_visible, n_pool, pool_blocks, k_blocks=0, topk_blocks=None, super_max=None,
+                       stream=None):
     R, stride = block_max.shape
     st = load_library().csa2_select_blocks(
-        _dev(block_max, "block_max", F32), stride, _dev(n_visible, "n_visible", I32, (R,)), R, n_pool,
+        _dev(block_max, "block_max", F32), _dev(super_max, "super_max", F32, (R, (stride + 7) // 8), optional=True),
+        stride, _dev(n_visible, "n_visible", I32, (R,)), R, n_pool,
         _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), k_blocks,
         _dev(topk_blocks, "topk_blocks", I32, (R, k_blocks), optional=k_blocks == 0), _stream(stream))
     _check("csa2_select_blocks", st)

@@ -14,14 +14,16 @@ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // index_full workspace carve-up
 struct FullWs {
-  size_t block_max, topk_blocks, topk_scores, total;
+  size_t block_max, super_max, topk_blocks, topk_scores, total;
 };
 
 inline FullWs full_ws(int64_t R, int64_t N_max, int k) {
   FullWs w;
   const int64_t nblk = (N_max + 7) / 8;
+  const int64_t nsup = (N_max + 63) / 64;
   w.block_max = 0;
-  w.topk_blocks = align_up(w.block_max + (size_t)R * nblk * sizeof(float));
+  w.super_max = align_up(w.block_max + (size_t)R * nblk * sizeof(float));
+  w.topk_blocks = align_up(w.super_max + (size_t)R * nsup * sizeof(float));
   w.topk_scores = align_up(w.topk_blocks + (size_t)R * (k > 0 ? k : 0) * sizeof(int32_t));
   w.total = align_up(w.topk_scores + (size_t)R * (k > 0 ? k : 0) * 8 * sizeof(float));
   return w;
@@ -48,22 +50,25 @@ const char* csa2_status_string(int status) {
 
 int csa2_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                     const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
-                    float* scores, float* block_max, void* stream) {
+                    float* scores, float* block_max, float* super_max, void* stream) {
   if (!q_codes || !q_scales || !k_codes || !k_scales || !n_visible || !block_max) return CSA2_ERR_INVALID;
   if (B < 1 || M < 1 || N_max < 1 || N_max > kMaxN || (int64_t)B * M > kMaxRows) return CSA2_ERR_INVALID;
   return hip_status(csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, scores,
-                                            block_max, (N_max + 7) / 8, as_stream(stream)));
+                                            block_max, (N_max + 7) / 8, super_max, (N_max + 63) / 64,
+                                            as_stream(stream)));
 }
 
-int csa2_select_blocks(const float* block_max, int64_t nblk_stride, const int32_t* n_visible, int R, int n_pool,
-                       int32_t* pool_blocks, int k_blocks, int32_t* topk_blocks, void* stream) {
+int csa2_select_blocks(const float* block_max, const float* super_max, int64_t nblk_stride,
+                       const int32_t* n_visible, int R, int n_pool, int32_t* pool_blocks, int k_blocks,
+                       int32_t* topk_blocks, void* stream) {
   if (!block_max || !n_visible || !pool_blocks) return CSA2_ERR_INVALID;
   if (R < 1 || R > kMaxRows || n_pool < 1 || n_pool > kMaxPool || k_blocks < 0 || k_blocks > kMaxPool ||
       nblk_stride < 1 || nblk_stride > kMaxN / 8)
     return CSA2_ERR_INVALID;
   if (k_blocks > 0 && !topk_blocks) return CSA2_ERR_INVALID;
   return hip_status(csa2::launch_select(csa2::kSelBlocks, block_max, nblk_stride, nullptr, 0, n_visible, R, n_pool,
-                                        pool_blocks, k_blocks, topk_blocks, as_stream(stream)));
+                                        pool_blocks, k_blocks, topk_blocks, super_max, (nblk_stride + 7) / 8,
+                                        as_stream(stream)));
 }
 
 int csa2_index_pool(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
@@ -86,7 +91,7 @@ int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, c
   if (k == 0) return CSA2_OK;
   const int layout = pool_blocks ? csa2::kSelPool : csa2::kSelFull;
   return hip_status(csa2::launch_select(layout, scores, pool_blocks ? 8 * n_pool : n_pool, pool_blocks, n_pool,
-                                        n_visible, R, k, idx, 0, nullptr, as_stream(stream)));
+                                        n_visible, R, k, idx, 0, nullptr, nullptr, 0, as_stream(stream)));
 }
 
 int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
@@ -106,21 +111,23 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
   float* bmax = block_max ? block_max : reinterpret_cast<float*>(ws + w.block_max);
   int32_t* topk_blocks = reinterpret_cast<int32_t*>(ws + w.topk_blocks);
   float* topk_scores = reinterpret_cast<float*>(ws + w.topk_scores);
+  float* smax = reinterpret_cast<float*>(ws + w.super_max);
+  const int64_t nsup = (N_max + 63) / 64;
   hipStream_t s = as_stream(stream);
   hipError_t e = csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, scores, bmax,
-                                         nblk, s);
+                                         nblk, smax, nsup, s);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   // the pool's top-k lies in the pool's first min(k, n_pool) blocks: rescore only those
   const int kb = k < n_pool ? k : n_pool;
   e = csa2::launch_select(csa2::kSelBlocks, bmax, nblk, nullptr, 0, n_visible, (int)R, n_pool, pool_blocks,
-                          kb, k > 0 ? topk_blocks : nullptr, s);
+                          kb, k > 0 ? topk_blocks : nullptr, smax, nsup, s);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   if (k == 0) return CSA2_OK;
   e = csa2::launch_pool_scan(q_codes, q_scales, k_codes, k_scales, topk_blocks, kb, n_visible, B, M, N_max,
                              topk_scores, s);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   e = csa2::launch_select(csa2::kSelPool, topk_scores, 8 * (int64_t)kb, topk_blocks, kb, n_visible, (int)R, k, idx,
-                          0, nullptr, s);
+                          0, nullptr, nullptr, 0, s);
   return hip_status(e);
 }
 

@@ -5,11 +5,10 @@
 
 namespace csa2 {
 
-int scan_chunk_positions(int64_t N_max);
-
 hipError_t launch_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                              const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
-                             float* scores, float* block_max, int64_t nblk_stride, hipStream_t stream);
+                             float* scores, float* block_max, int64_t nblk_stride, float* super_max,
+                             int64_t nsup_stride, hipStream_t stream);
 
 hipError_t launch_pool_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                             const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool,
@@ -21,9 +20,11 @@ hipError_t launch_pool_scan(const uint8_t* q_codes, const uint8_t* q_scales, con
 // pool_blocks); 2: full score rows (length min(n_visible, stride)).
 enum SelectLayout { kSelBlocks = 0, kSelPool = 1, kSelFull = 2 };
 
+// super_max (blocks layout only, may be null): maxima of 8 consecutive blocks,
+// row stride nsup_stride, as written by the indexer scan.
 hipError_t launch_select(int layout, const float* scores, int64_t stride, const int32_t* pool_blocks,
                          int64_t n_pool, const int32_t* n_visible, int R, int k1, int32_t* out1, int k2,
-                         int32_t* out2, hipStream_t stream);
+                         int32_t* out2, const float* super_max, int64_t nsup_stride, hipStream_t stream);
 
 struct AttnLaunch {
   const float* q;

@@ -21,18 +21,46 @@
 namespace csa2 {
 
 constexpr int kScanThreads = 256;
-constexpr int kScanUnroll = 8;          // 16-position groups in flight per wave
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kSupersPerWave = 2;                               // 64-position super-blocks per wave
+constexpr int kScanChunk = kScanWaves * kSupersPerWave * 64;    // positions per workgroup
+constexpr int kScanGroups = kSupersPerWave * 4;                  // 16-position groups per wave
 
 __device__ __forceinline__ u32x4_t load_codes16(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
-template <bool kScores>
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
+}
+
+// Score of one 16-position group (lane 4p+b holds block b of position p) and
+// the maxima of its two 8-position blocks: on return lanes 16..31 hold block
+// A's (positions 0-7) maximum key and lanes 48..63 block B's (positions 8-15).
+__device__ __forceinline__ uint32_t group_score_max(const u32x4_t c, uint32_t e, const half2_t* qh, int eq, bool vis,
+                                                    float* s_out) {
+  const float v = __builtin_amdgcn_ldexpf(block_dot(c, qh), eq + (int)e - 254);
+  const float s = quad_ordered_sum(v);
+  *s_out = s;
+  uint32_t k = vis ? order_key(s) : 0u;
+  uint32_t y = dpp_u32<0x124, 0xF>(k);   // row_ror:4 -> max of two quads
+  k = y > k ? y : k;
+  y = dpp_u32<0x128, 0xF>(k);            // row_ror:8 -> max of the row (4 positions)
+  k = y > k ? y : k;
+  y = dpp_u32<0x142, 0xA>(k);            // row_bcast:15 -> rows 1, 3 take the row before
+  return y > k ? y : k;
+}
+
+// Each wave scores kSupersPerWave consecutive 64-position super-blocks; all of
+// its loads are issued before any arithmetic.  Outputs: block maxima, optional
+// super-block maxima (8 blocks) and optional per-position scores.
+template <bool kScores, bool kSuper>
 __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
-    const int32_t* __restrict__ n_visible, int M, int64_t N_max, int64_t nblk_stride, int chunk,
-    float* __restrict__ scores, float* __restrict__ block_max) {
+    const int32_t* __restrict__ n_visible, int M, int64_t N_max, int64_t nblk_stride, int64_t nsup_stride,
+    float* __restrict__ scores, float* __restrict__ block_max, float* __restrict__ super_max) {
   const int r = blockIdx.y;
   const int64_t seq = r / M;
   const int lane = threadIdx.x & 63;
@@ -41,45 +69,43 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(
   const int pl = lane >> 2;
   int64_t nv = n_visible[r];
   nv = nv < 0 ? 0 : (nv > N_max ? N_max : nv);
-  const int64_t p0 = (int64_t)blockIdx.x * chunk;
-  if (p0 >= nv) return;
-  const int64_t pend = (p0 + chunk < nv) ? p0 + chunk : nv;
+  const int64_t p0 = (int64_t)blockIdx.x * kScanChunk + (int64_t)wave * (kSupersPerWave * 64);
+  if (p0 >= nv) return;   // no barriers below: waves leave independently
 
   half2_t qh[16];
   load_query_block(q_codes + (int64_t)r * 64 + 16 * b, qh);
   const int eq = q_scales[(int64_t)r * 4 + b];
-
   const uint8_t* kc = k_codes + seq * N_max * 64 + 16 * b;
   const uint8_t* ks = k_scales + seq * N_max * 4 + b;
-  const int ngroups = (int)((pend - p0 + 15) >> 4);
 
-  for (int g0 = wave; g0 < ngroups; g0 += 4 * kScanUnroll) {
-    u32x4_t c[kScanUnroll];
-    uint32_t e[kScanUnroll];
+  u32x4_t c[kScanGroups];
+  uint32_t e[kScanGroups];
 #pragma unroll
-    for (int u = 0; u < kScanUnroll; ++u) {
-      const int g = g0 + 4 * u;
-      int64_t p = p0 + 16 * g + pl;
-      p = p < pend ? p : pend - 1;           // tail lanes re-read a visible row
-      if (g < ngroups) {
-        c[u] = load_codes16(kc + p * 64);
-        e[u] = ks[p * 4];
-      }
+  for (int u = 0; u < kScanGroups; ++u) {
+    int64_t p = p0 + 16 * u + pl;
+    p = p < nv ? p : nv - 1;             // tail lanes re-read a visible row
+    c[u] = load_codes16(kc + p * 64);
+    e[u] = ks[p * 4];
+  }
+#pragma unroll
+  for (int h = 0; h < kSupersPerWave; ++h) {
+    uint32_t smax = 0u;
+#pragma unroll
+    for (int u = 4 * h; u < 4 * h + 4; ++u) {
+      const int64_t gp = p0 + 16 * u;
+      const int64_t p = gp + pl;
+      float s;
+      const uint32_t k = group_score_max(c[u], e[u], qh, eq, p < nv, &s);
+      if (kScores && b == 0 && p < nv) scores[(int64_t)r * N_max + p] = s;
+      smax = k > smax ? k : smax;
+      if (lane == 16 && gp < nv) block_max[(int64_t)r * nblk_stride + (gp >> 3)] = key_to_float(k);
+      if (lane == 48 && gp + 8 < nv) block_max[(int64_t)r * nblk_stride + (gp >> 3) + 1] = key_to_float(k);
     }
-#pragma unroll
-    for (int u = 0; u < kScanUnroll; ++u) {
-      const int g = g0 + 4 * u;
-      if (g >= ngroups) break;
-      const int64_t p = p0 + 16 * g + pl;
-      const float v = __builtin_amdgcn_ldexpf(block_dot(c[u], qh), eq + (int)e[u] - 254);
-      const float s = quad_ordered_sum(v);
-      const bool vis = p < pend;
-      if (kScores && vis && b == 0) scores[(int64_t)r * N_max + p] = s;
-      const uint32_t key = halfwave_quad_max(vis ? order_key(s) : 0u);
-      if ((lane & 31) == 0) {
-        const int64_t blk = ((p0 + 16 * g) >> 3) + (lane >> 5);
-        if (8 * blk < pend) block_max[(int64_t)r * nblk_stride + blk] = key_to_float(key);
-      }
+    if (kSuper) {
+      const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)smax, 16);
+      const uint32_t bb = (uint32_t)__builtin_amdgcn_readlane((int)smax, 48);
+      const int64_t sp = p0 + 64 * h;
+      if (lane == 0 && sp < nv) super_max[(int64_t)r * nsup_stride + (sp >> 6)] = key_to_float(a > bb ? a : bb);
     }
   }
 }
@@ -137,20 +163,20 @@ __global__ __launch_bounds__(kScanThreads) void pool_scan_kernel(
 
 hipError_t launch_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                              const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
-                             float* scores, float* block_max, int64_t nblk_stride, hipStream_t stream) {
+                             float* scores, float* block_max, int64_t nblk_stride, float* super_max,
+                             int64_t nsup_stride, hipStream_t stream) {
   const int R = B * M;
-  const int chunk = scan_chunk_positions(N_max);
-  dim3 grid((unsigned)((N_max + chunk - 1) / chunk), (unsigned)R);
-  if (scores)
-    hipLaunchKernelGGL(index_scan_kernel<true>, grid, dim3(kScanThreads), 0, stream, q_codes, q_scales, k_codes,
-                       k_scales, n_visible, M, N_max, nblk_stride, chunk, scores, block_max);
-  else
-    hipLaunchKernelGGL(index_scan_kernel<false>, grid, dim3(kScanThreads), 0, stream, q_codes, q_scales, k_codes,
-                       k_scales, n_visible, M, N_max, nblk_stride, chunk, scores, block_max);
+  dim3 grid((unsigned)((N_max + kScanChunk - 1) / kScanChunk), (unsigned)R);
+#define CSA2_SCAN(S, P)                                                                                         \
+  hipLaunchKernelGGL((index_scan_kernel<S, P>), grid, dim3(kScanThreads), 0, stream, q_codes, q_scales, k_codes, \
+                     k_scales, n_visible, M, N_max, nblk_stride, nsup_stride, scores, block_max, super_max)
+  if (scores && super_max) CSA2_SCAN(true, true);
+  else if (scores) CSA2_SCAN(true, false);
+  else if (super_max) CSA2_SCAN(false, true);
+  else CSA2_SCAN(false, false);
+#undef CSA2_SCAN
   return hipGetLastError();
 }
-
-int scan_chunk_positions(int64_t /*N_max*/) { return 2048; }
 
 hipError_t launch_pool_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                             const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool,

@@ -507,7 +507,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int layout, const f
                                                              int64_t stride, const int32_t* __restrict__ pool_blocks,
                                                              int64_t n_pool, const int32_t* __restrict__ n_visible,
                                                              int k1, int32_t* __restrict__ out1, int k2,
-                                                             int32_t* __restrict__ out2) {
+                                                             int32_t* __restrict__ out2,
+                                                             const float* __restrict__ super_max,
+                                                             int64_t nsup_stride) {
   __shared__ SelShared sh;
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -550,7 +552,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int layout, const f
     // block maxima (the host guarantees nsuper <= kSuperCap and k <= 2048)
     const int64_t nsuper = (row.n + 7) >> 3;
     const int kmax = k1 > k2 ? k1 : k2;
-    {
+    if (super_max) {
+      // level 1 from the scan's super-block maxima
+      KeyStats st;
+      const float* srow = super_max + (int64_t)r * nsup_stride;
+#pragma unroll 10
+      for (int j = 0; j < kSegIters; ++j) {
+        const int i = w * kSegItems + 64 * j + lane;
+        if (i < nsuper) {
+          const uint32_t k = order_key(srow[i]);
+          sh.u.skeys[i] = k;
+          st.add(k);
+        }
+      }
+      reduce_stats(sh, st);
+    } else {
       // level 1: super-block maxima of 8 consecutive blocks; lanes read
       // consecutive blocks (coalesced) and reduce over groups of 8 lanes
       KeyStats st;
@@ -611,7 +627,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int layout, const f
 
 hipError_t launch_select(int layout, const float* scores, int64_t stride, const int32_t* pool_blocks,
                          int64_t n_pool, const int32_t* n_visible, int R, int k1, int32_t* out1, int k2,
-                         int32_t* out2, hipStream_t stream) {
+                         int32_t* out2, const float* super_max, int64_t nsup_stride, hipStream_t stream) {
   // the longest possible row decides the path
   const int64_t max_n = layout == kSelPool ? 8 * n_pool : stride;
   const int ka = out1 ? k1 : 0, kb = out2 ? k2 : 0;
@@ -619,13 +635,13 @@ hipError_t launch_select(int layout, const float* scores, int64_t stride, const 
   const dim3 grid((unsigned)R), block(kSelThreads);
   if (max_n <= kRowCap)
     hipLaunchKernelGGL(select_kernel<kPathLds>, grid, block, 0, stream, layout, scores, stride, pool_blocks, n_pool,
-                       n_visible, k1, out1, k2, out2);
+                       n_visible, k1, out1, k2, out2, super_max, nsup_stride);
   else if (layout == kSelBlocks && (max_n + 7) / 8 <= kSuperCap && kmax <= 2048)
     hipLaunchKernelGGL(select_kernel<kPathSuper>, grid, block, 0, stream, layout, scores, stride, pool_blocks, n_pool,
-                       n_visible, k1, out1, k2, out2);
+                       n_visible, k1, out1, k2, out2, super_max, nsup_stride);
   else
     hipLaunchKernelGGL(select_kernel<kPathMem>, grid, block, 0, stream, layout, scores, stride, pool_blocks, n_pool,
-                       n_visible, k1, out1, k2, out2);
+                       n_visible, k1, out1, k2, out2, super_max, nsup_stride);
   return hipGetLastError();
 }
 

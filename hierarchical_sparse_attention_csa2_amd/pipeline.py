@@ -67,6 +67,7 @@ class Step:
         dev = torch.device(device)
         R, nblk = self.R, (N + 7) // 8
         self.block_max = torch.empty((R, nblk), dtype=torch.float32, device=dev)
+        self.super_max = torch.empty((R, (N + 63) // 64), dtype=torch.float32, device=dev)
         self.scores = torch.empty((R, N), dtype=torch.float32, device=dev) if keep_scores else None
         self.pool = torch.empty((R, n_pool), dtype=torch.int32, device=dev)
         self.kb = min(k, n_pool)     # the pool's top-k lies in its first min(k, n_pool) blocks
@@ -89,8 +90,9 @@ class Step:
                             block_max=self.block_max)
             return
         csa2_index_scan(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, B, M, N,
-                        self.block_max, scores=self.scores)
-        csa2_select_blocks(self.block_max, li.n_visible, self.n_pool, self.pool, self.kb, self.topk_blocks)
+                        self.block_max, scores=self.scores, super_max=self.super_max)
+        csa2_select_blocks(self.block_max, li.n_visible, self.n_pool, self.pool, self.kb, self.topk_blocks,
+                           super_max=self.super_max)
         csa2_index_pool(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, self.topk_blocks, li.n_visible,
                         B, M, N, self.topk_scores)
         csa2_topk(self.topk_scores, li.n_visible, self.k, idx, pool_blocks=self.topk_blocks)
@@ -98,7 +100,7 @@ class Step:
     def scan_only(self, cache: Cache, li: LayerInputs):
         """The Full layer's scan alone (block maxima into this step's buffer)."""
         csa2_index_scan(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, self.B, self.M,
-                        self.N, self.block_max, scores=self.scores)
+                        self.N, self.block_max, scores=self.scores, super_max=self.super_max)
 
     def reindex(self, cache: Cache, li: LayerInputs, idx: torch.Tensor):
         csa2_index_pool(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, self.pool, li.n_visible,

@@ -77,27 +77,37 @@ enum { CSA2_OP_INDEX_FULL = 1, CSA2_OP_SPARSE_ATTN = 2 };
  *   scores     f32[R][N_max] or NULL; entries j >= n_visible[r] are not written.
  *   block_max  f32[R][nblk_max], nblk_max = ceil(N_max/8); blocks past the
  *              visible range are not written.  Required.
+ *   super_max  f32[R][nsup_max] or NULL, nsup_max = ceil(N_max/64): the maximum
+ *              of the 8 block maxima [8s, 8s+8) (positions [64s, 64s+64) within
+ *              the visible range); entries past the visible range are not
+ *              written.  csa2_select_blocks can take it to rank long rows from
+ *              one level up without re-reading the block maxima.
  * Returns CSA2_OK, CSA2_ERR_INVALID (NULL input, B<1, M<1, N_max<1),
  * CSA2_ERR_HIP.
  */
 int csa2_index_scan(const uint8_t* q_codes, const uint8_t* q_scales,
                     const uint8_t* k_codes, const uint8_t* k_scales,
                     const int32_t* n_visible, int B, int M, int64_t N_max,
-                    float* scores, float* block_max, void* stream);
+                    float* scores, float* block_max, float* super_max, void* stream);
 
 /*
  * csa2_select_blocks - the coarse filter: rank the visible blocks of each row by
  * (block max descending, block id ascending) and keep the first
  * min(n_pool, nblk) as the candidate pool, nblk = ceil(n_visible[r]/8).
  *   block_max    f32[R][nblk_stride] (as written by csa2_index_scan)
+ *   super_max    f32[R][ceil(nblk_stride/8)] or NULL: the maxima of 8
+ *                consecutive blocks, as written by csa2_index_scan with the same
+ *                N_max.  Used only to speed up rows longer than 16,384 blocks;
+ *                the result is the same with or without it.
  *   pool_blocks  i32[R][n_pool]: kept block ids ascending, -1 padded.
  *   topk_blocks  i32[R][k_blocks] or NULL: the first min(k_blocks, nblk) blocks
  *                of the same ranking (a prefix of the pool when k_blocks <= n_pool).
  * Returns CSA2_OK, CSA2_ERR_INVALID (NULL, R<1, n_pool<1, k_blocks<0,
  * nblk_stride<1), CSA2_ERR_HIP.
  */
-int csa2_select_blocks(const float* block_max, int64_t nblk_stride, const int32_t* n_visible, int R,
-                       int n_pool, int32_t* pool_blocks, int k_blocks, int32_t* topk_blocks, void* stream);
+int csa2_select_blocks(const float* block_max, const float* super_max, int64_t nblk_stride,
+                       const int32_t* n_visible, int R, int n_pool, int32_t* pool_blocks, int k_blocks,
+                       int32_t* topk_blocks, void* stream);
 
 /*
  * csa2_index_pool - score only inside a pool (Reindex layers, and the Full

@@ -46,15 +46,15 @@ P = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails valid
 def test_validation_rejects_before_launch():
     L = csa2.load_library()
     # index_scan: NULL inputs, bad sizes
-    assert L.csa2_index_scan(NULL, P, P, P, P, 1, 1, 16, NULL, P, NULL) == -1
-    assert L.csa2_index_scan(P, P, P, P, P, 0, 1, 16, NULL, P, NULL) == -1
-    assert L.csa2_index_scan(P, P, P, P, P, 1, 0, 16, NULL, P, NULL) == -1
-    assert L.csa2_index_scan(P, P, P, P, P, 1, 1, 0, NULL, P, NULL) == -1
-    assert L.csa2_index_scan(P, P, P, P, P, 1, 1, 16, NULL, NULL, NULL) == -1
+    assert L.csa2_index_scan(NULL, P, P, P, P, 1, 1, 16, NULL, P, NULL, NULL) == -1
+    assert L.csa2_index_scan(P, P, P, P, P, 0, 1, 16, NULL, P, NULL, NULL) == -1
+    assert L.csa2_index_scan(P, P, P, P, P, 1, 0, 16, NULL, P, NULL, NULL) == -1
+    assert L.csa2_index_scan(P, P, P, P, P, 1, 1, 0, NULL, P, NULL, NULL) == -1
+    assert L.csa2_index_scan(P, P, P, P, P, 1, 1, 16, NULL, NULL, NULL, NULL) == -1
     # select_blocks
-    assert L.csa2_select_blocks(P, 2, P, 1, 0, P, 0, NULL, NULL) == -1
-    assert L.csa2_select_blocks(P, 2, P, 1, 4, P, 2, NULL, NULL) == -1
-    assert L.csa2_select_blocks(P, 0, P, 1, 4, P, 0, NULL, NULL) == -1
+    assert L.csa2_select_blocks(P, NULL, 2, P, 1, 0, P, 0, NULL, NULL) == -1
+    assert L.csa2_select_blocks(P, NULL, 2, P, 1, 4, P, 2, NULL, NULL) == -1
+    assert L.csa2_select_blocks(P, NULL, 0, P, 1, 4, P, 0, NULL, NULL) == -1
     # index_pool
     assert L.csa2_index_pool(P, P, P, P, NULL, 4, P, 1, 1, 16, P, NULL) == -1
     assert L.csa2_index_pool(P, P, P, P, P, 0, P, 1, 1, 16, P, NULL) == -1

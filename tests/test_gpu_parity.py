@@ -32,13 +32,16 @@ def _need_gpu():
     csa2.load_library()
 
 
-def _run_scan(w, c, l):
+def _run_scan(w, c, l, want_super=False):
     nblk = (w.N + 7) // 8
     scores = torch.full((w.R, w.N), float("nan"), device="cuda")
     bmax = torch.full((w.R, nblk), float("nan"), device="cuda")
+    smax = torch.full((w.R, (w.N + 63) // 64), float("nan"), device="cuda") if want_super else None
     csa2.csa2_index_scan(l["q_codes"], l["q_scales"], c["k_codes"], c["k_scales"], l["n_visible"], w.B, w.M, w.N,
-                         bmax, scores=scores)
+                         bmax, scores=scores, super_max=smax)
     torch.cuda.synchronize()
+    if want_super:
+        return scores.cpu().numpy(), bmax.cpu().numpy(), smax.cpu().numpy()
     return scores.cpu().numpy(), bmax.cpu().numpy()
 
 
@@ -49,13 +52,17 @@ def test_index_scan_bitexact(kind, N, nv):
     cache, (lay,) = host_inputs(w, kind=kind)
     lay["n_visible"] = np.array(nv, np.int32)
     say(f"scan N={N} nv={nv} kind={kind}")
-    scores, bmax = _run_scan(w, dev(cache), dev(lay))
+    scores, bmax, smax = _run_scan(w, dev(cache), dev(lay), want_super=True)
     ref = oracle_full(w, cache, lay, want_scores=True, want_block_max=True)
     for r in range(w.R):
         n = nv[r]
         assert np.array_equal(f32_bits(scores[r, :n]), f32_bits(ref["scores"][r, :n])), r
         nb = (n + 7) // 8
         assert np.array_equal(f32_bits(bmax[r, :nb]), f32_bits(ref["block_max"][r, :nb])), r
+        # super-block maxima: the max of each run of 8 oracle block maxima
+        ns = (n + 63) // 64
+        want = [np.max(ref["block_max"][r, 8 * s:min(8 * s + 8, nb)]) for s in range(ns)]
+        assert np.array_equal(f32_bits(smax[r, :ns]), f32_bits(np.array(want, np.float32))), r
 
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "spread"])
@@ -87,6 +94,11 @@ def test_index_full_bitexact(kind, N, n_pool, k, nv):
     torch.cuda.synchronize()
     assert np.array_equal(st.pool.cpu().numpy(), ref["pool_blocks"])
     assert np.array_equal(st.idx[0].cpu().numpy(), ref["idx"])
+    # the block filter without the scan's super-block maxima gives the same pool
+    pool2 = torch.empty_like(pool)
+    csa2.csa2_select_blocks(st.block_max, l["n_visible"], n_pool, pool2)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool2.cpu().numpy(), ref["pool_blocks"])
 
 
 def test_select_blocks_and_topk_full_layout():
