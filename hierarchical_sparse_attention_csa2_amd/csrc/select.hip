@@ -8,27 +8,29 @@
 // (score desc, id asc): ties go to the lowest position / block id.
 //
 // One 1024-thread workgroup per row; every decision is exact on the IEEE
-// total-order key of the fp32 score (0 = no element).  The working set (up to
-// 20,480 keys) sits in LDS; wave w holds items [1280w, 1280w + 1280), item
-// 64j + lane, so LDS and memory accesses are conflict-free and coalesced, and
-// ordered prefix sums come from ballots.  Cross-lane reductions use DPP.
-//   1. The load pass also finds the smallest and largest key and the count.
-//   2. A histogram of the first digit ((key - kmin) >> s1, 12 bits) -- spread
-//      over the row's own key range so same-address LDS atomics stay rare --
-//      gives, per target k, the bin holding the k-th key.
-//   3. The members of each threshold bin are copied to a short LDS list; the
-//      remaining bits of the k-th key T and how many keys equal to T are taken
-//      come from histograms over that list only.
-//   4. One ordered emit pass writes every target: keys > T and the first
-//      `take` keys == T, ids ascending.
-// Rows of block maxima longer than 16,384 are filtered one level up first:
-// super-blocks of 8 consecutive blocks are ranked by their own maximum, and any
-// set of super-blocks holding the first K super-blocks holds every block of the
-// first K blocks (a super-block ranked ahead of another contributes its best
-// block ahead of every block of the other).  Level 1 keeps the super-blocks at
-// or above the threshold bin when they fit (else exactly the first K), level 2
-// selects exactly among their blocks.  Anything longer runs the same selection
-// with every pass reading the row from memory.
+// total-order key of the fp32 score (0 = no element), and the work is
+// VALU-bound on the row's one compute unit, so every pass keeps its items in
+// registers and as few passes as possible touch all of them.
+//   1. Load (up to 16 items a lane) with the count, minimum and maximum key.
+//   2. One 4096-bin histogram of the first 12-bit digit of (key - kmin), spread
+//      over the row's own key range; all 16 waves search it for the bin of the
+//      K-th key of each target (up to two targets share the passes).
+//   3. The members of a threshold bin (usually a handful) are copied out and
+//      ranked by counting; a bin with more than 256 members (many equal keys) is
+//      narrowed by further 12-bit digits first.
+//   4. One counting pass and one ordered writing pass emit, per target, the ids
+//      of the keys > T and of the first `take` keys == T, ids ascending.
+// Rows of block maxima longer than 16,384 blocks are filtered one level up
+// first: super-blocks of 8 consecutive blocks are ranked by their own maximum
+// (which the indexer scan can supply), and any set of super-blocks holding the
+// first K super-blocks holds every block of the first K blocks (a super-block
+// ranked ahead of another contributes its best block ahead of every block of the
+// other).  Level 1 keeps the super-blocks at or above the threshold bin when
+// they fit (else exactly the first K), which bounds the K-th block key from
+// below by that bin's lower edge T1; level 2 gathers only the blocks >= T1 of the
+// kept super-blocks (a few thousand), compacts them in id order and selects
+// exactly among them.  Anything longer runs a generic selection that re-reads
+// the row from memory in every pass.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -39,7 +41,6 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSegIters = 20;                      // items per lane per pass
 constexpr int kSegItems = 64 * kSegIters;          // 1280 items per wave
 constexpr int kSelCap = kSelWaves * kSegItems;     // 20,480 keys in LDS
-constexpr int kRowCap = 16384;                     // rows cached whole (ids = index)
 constexpr int kBins = 4096;
 constexpr int kSuperCap = 8192;                    // super-block keys (level 1)
 constexpr int kLevelCap = kSelCap / 8;             // super-blocks kept by level 1 (2560)
@@ -500,16 +501,585 @@ __device__ __forceinline__ void select_targets(SelShared& sh, const RowView row,
   __syncthreads();
 }
 
-enum { kPathLds = 0, kPathSuper = 1, kPathMem = 2 };
+// ---------------------------------------------------------------------------
+// register-resident selection (rows up to 16,384 items, and the two-level
+// block filter)
+// ---------------------------------------------------------------------------
+// Item (w, j, lane) of a J-item-per-lane row is index (w*J + j)*64 + lane, so
+// item order is id order and a wave's items are one contiguous range.
+constexpr int kRankCap = 256;                      // threshold-bin members resolved by counting
+constexpr int kKeepCap = 3072;                     // super-blocks kept by level 1
+constexpr int kCompCap = 16384;                    // blocks surviving into level 2
+constexpr int kGatherIters = kKeepCap / 128;       // 8 lanes per super-block
 
-template <int PATH>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(int layout, const float* __restrict__ scores,
-                                                             int64_t stride, const int32_t* __restrict__ pool_blocks,
-                                                             int64_t n_pool, const int32_t* __restrict__ n_visible,
-                                                             int k1, int32_t* __restrict__ out1, int k2,
-                                                             int32_t* __restrict__ out2,
-                                                             const float* __restrict__ super_max,
-                                                             int64_t nsup_stride) {
+struct Core {
+  uint32_t hist[kBins];
+  uint32_t mem[2][kRankCap];
+};
+
+struct Small {
+  int cnt[2];                     // members collected per target
+  int wcnt[4][kSelWaves];         // emit: per-wave counts
+  int wtot[kSelWaves];            // find: per-wave bin totals
+  int wstat[kSelWaves];
+  uint32_t wmin[kSelWaves], wmax[kSelWaves];
+  int res[16];
+};
+
+struct RegShared {
+  Core c;
+  Small s;
+};
+
+__device__ __forceinline__ int mbcnt(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// inclusive prefix sum over each row of 16 lanes
+__device__ __forceinline__ int row_incl_scan(int x) {
+  x += dpp<0x111>(x);
+  x += dpp<0x112>(x);
+  x += dpp<0x114>(x);
+  x += dpp<0x118>(x);
+  return x;
+}
+
+// Count, min and max of the non-zero keys over the workgroup (every thread
+// gets them).  One barrier.
+template <int J>
+__device__ __forceinline__ void key_range(Small& s, const uint32_t (&k)[J], int& valid, uint32_t& kmin,
+                                          uint32_t& kmax) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int c = 0;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t x = k[j];
+    c += x != 0u;
+    mn = (x != 0u && x < mn) ? x : mn;
+    mx = x > mx ? x : mx;
+  }
+  c = wave_sum(c);
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    s.wstat[w] = c;
+    s.wmin[w] = mn;
+    s.wmax[w] = mx;
+  }
+  __syncthreads();
+  const bool in = lane < kSelWaves;
+  const int c2 = row_incl_scan(in ? s.wstat[lane] : 0);
+  valid = __builtin_amdgcn_readlane(c2, kSelWaves - 1);
+  kmin = (uint32_t)__builtin_amdgcn_readlane((int)row16_min(in ? s.wmin[lane] : 0xFFFFFFFFu), 0);
+  kmax = (uint32_t)__builtin_amdgcn_readlane((int)row16_max(in ? s.wmax[lane] : 0u), 0);
+}
+
+__device__ __forceinline__ void hist_zero(Core& c) {
+  reinterpret_cast<u32x4_t*>(c.hist)[threadIdx.x] = u32x4_t{0u, 0u, 0u, 0u};   // 1024 x 4 bins
+}
+
+// hist[((key - kmin) >> shift) & (2^bits - 1)] += 1 over the non-zero keys with
+// ((key - kmin) >> pshift) == prefix (pshift >= 32: every key).
+template <int J>
+__device__ __forceinline__ void hist_add(Core& c, const uint32_t (&k)[J], uint32_t kmin, int shift, int bits,
+                                         int pshift, uint32_t prefix) {
+  const uint32_t dmask = (1u << bits) - 1u;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t d = k[j] - kmin;
+    const bool in = k[j] != 0u && (pshift >= 32 || (d >> pshift) == prefix);
+    if (in) atomicAdd(&c.hist[(d >> shift) & dmask], 1u);
+  }
+}
+
+struct BinHit {
+  int bin, above, inbin;
+};
+
+// With the histogram complete: for each target with need >= 1, the bin b
+// (highest first) with (#keys in bins above b) < need <= (#keys in bins >= b).
+// Wave w reads bins [4096 - 256(w+1), 4096 - 256w), lane l four of them, so
+// the search is a wave scan, a scan over the 16 wave totals and one lane's
+// walk over its four bins.  Two barriers.
+__device__ __forceinline__ void find_bins(Core& c, Small& s, int need0, int need1, BinHit& h0, BinHit& h1) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int base = kBins - 256 * w - 4 * (lane + 1);
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&c.hist[base]);
+  const int sum = (int)(v[0] + v[1] + v[2] + v[3]);
+  const int incl = wave_incl_scan(sum);
+  const int tot = __builtin_amdgcn_readlane(incl, 63);
+  if (lane == 0) s.wtot[w] = tot;
+  __syncthreads();
+  const int x = lane < kSelWaves ? s.wtot[lane] : 0;
+  const int xi = row_incl_scan(x);
+  const int excl_w = __builtin_amdgcn_readlane(xi, w) - tot;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int need = t ? need1 : need0;
+    if (need >= 1 && excl_w < need && need <= excl_w + tot) {
+      const int hi = excl_w + incl;
+      const unsigned long long hit = __ballot(hi - sum < need && need <= hi);
+      if (lane == (int)__builtin_ctzll(hit)) {
+        int acc = hi - sum, bin = base, c_in = (int)v[0];
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          const int ce = (int)v[e];
+          if (acc + ce >= need) {
+            bin = base + e;
+            c_in = ce;
+            break;
+          }
+          acc += ce;
+        }
+        s.res[4 * t + 0] = bin;
+        s.res[4 * t + 1] = acc;
+        s.res[4 * t + 2] = c_in;
+      }
+    }
+  }
+  __syncthreads();
+  h0 = BinHit{s.res[0], s.res[1], s.res[2]};
+  h1 = BinHit{s.res[4], s.res[5], s.res[6]};
+}
+
+// Copy the non-zero keys with ((key - kmin) >> cur_t) == prefix_t into mem[t]
+// (any order) for the targets with want_t.  Ends synchronised.
+template <int J>
+__device__ __forceinline__ void collect_bins(Core& c, Small& s, const uint32_t (&k)[J], uint32_t kmin, bool want0,
+                                             int cur0, uint32_t prefix0, bool want1, int cur1, uint32_t prefix1) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t d = k[j] - kmin;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bool want = t ? want1 : want0;
+      if (!want) continue;
+      const bool in = k[j] != 0u && (d >> (t ? cur1 : cur0)) == (t ? prefix1 : prefix0);
+      const unsigned long long m = __ballot(in);
+      if (m) {
+        int b = 0;
+        if (lane == 0) b = atomicAdd(&s.cnt[t], __popcll(m));
+        b = __builtin_amdgcn_readfirstlane(b);
+        if (in) c.mem[t][b + mbcnt(m)] = k[j];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// For each wanted target, the need-th largest of its m members (T) and how
+// many members equal to T are taken.  Threads [0, 512) serve target 0, [512,
+// 1024) target 1: each counts the members above and equal to its own.
+__device__ __forceinline__ void rank_members(Core& c, Small& s, bool want0, int m0, int need0, bool want1, int m1,
+                                             int need1, uint32_t& T0, int& take0, uint32_t& T1, int& take1) {
+  const int t = threadIdx.x >> 9, u = threadIdx.x & 511;
+  const bool want = t ? want1 : want0;
+  const int m = t ? m1 : m0, need = t ? need1 : need0;
+  if (threadIdx.x == 0) {
+    s.cnt[0] = 0;
+    s.cnt[1] = 0;
+  }
+  if (want && u < m) {
+    const uint32_t* mem = t ? c.mem[1] : c.mem[0];
+    const uint32_t x = mem[u];
+    int gt = 0, eq = 0;
+    int v = 0;
+    for (; v + 4 <= m; v += 4) {
+      const u32x4_t y = *reinterpret_cast<const u32x4_t*>(&mem[v]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gt += y[e] > x;
+        eq += y[e] == x;
+      }
+    }
+    for (; v < m; ++v) {
+      const uint32_t y = mem[v];
+      gt += y > x;
+      eq += y == x;
+    }
+    if (gt < need && need <= gt + eq) {
+      s.res[8 + 2 * t] = (int)x;
+      s.res[9 + 2 * t] = need - gt;
+    }
+  }
+  __syncthreads();
+  if (want0) {
+    T0 = (uint32_t)s.res[8];
+    take0 = s.res[9];
+  }
+  if (want1) {
+    T1 = (uint32_t)s.res[10];
+    take1 = s.res[11];
+  }
+}
+
+// A target's selection: the keys > T and the first `take` keys == T (item
+// order), keff of them, written to positions [0, keff) of a K-entry output and
+// -1 after.
+struct Thr {
+  uint32_t T;
+  int take, keff, K;
+  bool on;
+};
+
+// Thresholds for up to two targets over the non-zero keys (valid of them, all
+// within [kmin, kmax]).  The histogram must be zero on entry.  approx_cap > 0:
+// target 0 may instead keep every key of its threshold bin and above when that
+// is at most approx_cap keys.
+template <int J>
+__device__ __forceinline__ void select_thresholds(Core& c, Small& s, const uint32_t (&k)[J], int valid, uint32_t kmin,
+                                                  uint32_t kmax, int K0, int K1, int approx_cap, Thr& th0,
+                                                  Thr& th1) {
+  const int keff0 = K0 > 0 ? (K0 < valid ? K0 : valid) : 0;
+  const int keff1 = K1 > 0 ? (K1 < valid ? K1 : valid) : 0;
+  th0 = Thr{1u, 0x7FFFFFFF, keff0, K0, keff0 > 0};
+  th1 = Thr{1u, 0x7FFFFFFF, keff1, K1, keff1 > 0};
+  bool act0 = keff0 > 0 && keff0 < valid, act1 = keff1 > 0 && keff1 < valid;
+  if (!act0 && !act1) return;
+  const uint32_t span = kmax - kmin;
+  const int bits = span ? 32 - __builtin_clz(span) : 0;
+  const int s1 = bits > 12 ? bits - 12 : 0;
+  hist_add(c, k, kmin, s1, 12, 32, 0u);
+  __syncthreads();
+  BinHit h0, h1;
+  find_bins(c, s, act0 ? keff0 : 0, act1 ? keff1 : 0, h0, h1);
+  int cur0 = s1, cur1 = s1;
+  uint32_t pre0 = (uint32_t)h0.bin, pre1 = (uint32_t)h1.bin;
+  int need0 = keff0 - h0.above, need1 = keff1 - h1.above;
+  int m0 = h0.inbin, m1 = h1.inbin;
+  if (approx_cap > 0 && act0 && h0.above + h0.inbin <= approx_cap) {
+    th0.T = kmin + (pre0 << s1);
+    th0.take = 0x7FFFFFFF;
+    th0.keff = h0.above + h0.inbin;
+    act0 = false;
+  }
+  // large threshold bins (many equal or near-equal keys): narrow them with
+  // further 12-bit digits
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    bool& act = t ? act1 : act0;
+    int& cur = t ? cur1 : cur0;
+    uint32_t& pre = t ? pre1 : pre0;
+    int& need = t ? need1 : need0;
+    int& m = t ? m1 : m0;
+    while (act && cur > 0 && m > kRankCap) {
+      const int nxt = cur > 12 ? cur - 12 : 0;
+      hist_zero(c);
+      __syncthreads();
+      hist_add(c, k, kmin, nxt, cur - nxt, cur, pre);
+      __syncthreads();
+      BinHit g, unused;
+      find_bins(c, s, need, 0, g, unused);
+      need -= g.above;
+      pre = (pre << (cur - nxt)) | (uint32_t)g.bin;
+      cur = nxt;
+      m = g.inbin;
+    }
+  }
+  if (act0 && cur0 == 0) {
+    th0.T = kmin + pre0;
+    th0.take = need0;
+    act0 = false;
+  }
+  if (act1 && cur1 == 0) {
+    th1.T = kmin + pre1;
+    th1.take = need1;
+    act1 = false;
+  }
+  if (act0 || act1) {
+    collect_bins(c, s, k, kmin, act0, cur0, pre0, act1, cur1, pre1);
+    rank_members(c, s, act0, m0, need0, act1, m1, need1, th0.T, th0.take, th1.T, th1.take);
+  }
+}
+
+// Ordered emit of both targets: one counting pass, a barrier, one writing pass.
+// store(t, pos, j, i) writes the id of item i (slot j of this lane) at
+// position pos of target t; pad(t, p) writes the -1 padding.
+template <int J, class Store, class Pad>
+__device__ __forceinline__ void emit_sel(Small& s, const uint32_t (&k)[J], const Thr& th0, const Thr& th1,
+                                         Store store, Pad pad) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // per-lane counts, two 16-bit fields per word (a wave counts at most 64*J)
+  uint32_t c0 = 0u, c1 = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    c0 += (th0.on && k[j] > th0.T ? 1u : 0u) + (th0.on && k[j] == th0.T ? 0x10000u : 0u);
+    c1 += (th1.on && k[j] > th1.T ? 1u : 0u) + (th1.on && k[j] == th1.T ? 0x10000u : 0u);
+  }
+  c0 = (uint32_t)wave_sum((int)c0);
+  c1 = (uint32_t)wave_sum((int)c1);
+  if (lane == 0) {
+    s.wcnt[0][w] = (int)(c0 & 0xFFFFu);
+    s.wcnt[1][w] = (int)(c0 >> 16);
+    s.wcnt[2][w] = (int)(c1 & 0xFFFFu);
+    s.wcnt[3][w] = (int)(c1 >> 16);
+  }
+  __syncthreads();
+  int run_sel[2], run_tie[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int g = lane < kSelWaves ? s.wcnt[2 * t][lane] : 0;
+    const int e = lane < kSelWaves ? s.wcnt[2 * t + 1][lane] : 0;
+    const int gi = row_incl_scan(g), ei = row_incl_scan(e);
+    const int gb = __builtin_amdgcn_readlane(gi, w) - __builtin_amdgcn_readlane(g, w);
+    const int eb = __builtin_amdgcn_readlane(ei, w) - __builtin_amdgcn_readlane(e, w);
+    const int take = t ? th1.take : th0.take;
+    run_tie[t] = eb;
+    run_sel[t] = gb + (take < eb ? take : eb);
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = (w * J + j) * 64 + lane;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const Thr& th = t ? th1 : th0;
+      if (!th.on) continue;
+      const bool tie = k[j] == th.T;
+      const unsigned long long mt = __ballot(tie);
+      const bool sel = k[j] > th.T || (tie && run_tie[t] + mbcnt(mt) < th.take);
+      const unsigned long long ms = __ballot(sel);
+      const int pos = run_sel[t] + mbcnt(ms);
+      if (sel && pos < th.keff) store(t, pos, j, i);
+      run_tie[t] += __popcll(mt);
+      run_sel[t] += __popcll(ms);
+    }
+  }
+  for (int p = th0.keff + (int)threadIdx.x; p < th0.K; p += kSelThreads) pad(0, p);
+  for (int p = th1.keff + (int)threadIdx.x; p < th1.K; p += kSelThreads) pad(1, p);
+}
+
+// Rows of at most 1024*J items (any layout), items in registers.
+template <int J, int LAYOUT>
+__global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                 const int32_t* __restrict__ pool_blocks,
+                                                                 int64_t n_pool,
+                                                                 const int32_t* __restrict__ n_visible, int K0,
+                                                                 int32_t* __restrict__ out0, int K1,
+                                                                 int32_t* __restrict__ out1) {
+  __shared__ RegShared sh;
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int64_t nv = n_visible[r];
+  nv = nv < 0 ? 0 : nv;
+  int64_t n;
+  const float* row;
+  const int32_t* pb = nullptr;
+  if (LAYOUT == kSelBlocks) {
+    row = scores + (int64_t)r * stride;
+    n = (nv + 7) >> 3;
+    n = n < stride ? n : stride;
+  } else if (LAYOUT == kSelPool) {
+    row = scores + (int64_t)r * n_pool * 8;
+    pb = pool_blocks + (int64_t)r * n_pool;
+    n = 8 * n_pool;
+  } else {
+    row = scores + (int64_t)r * stride;
+    n = nv < stride ? nv : stride;
+  }
+  int32_t* o0 = out0 ? out0 + (int64_t)r * K0 : nullptr;
+  int32_t* o1 = out1 ? out1 + (int64_t)r * K1 : nullptr;
+  if (!out0) K0 = 0;
+  if (!out1) K1 = 0;
+
+  uint32_t k[J];
+  int32_t pbv[LAYOUT == kSelPool ? J : 1];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = (w * J + j) * 64 + lane;
+    if constexpr (LAYOUT == kSelPool) {
+      const int32_t blk = i < n ? pb[i >> 3] : -1;
+      const float x = i < n ? row[i] : 0.0f;
+      pbv[j] = blk;
+      k[j] = (blk >= 0 && 8 * (int64_t)blk + (i & 7) < nv) ? order_key(x) : 0u;
+    } else {
+      k[j] = i < n ? order_key(row[i]) : 0u;
+    }
+  }
+  hist_zero(sh.c);
+  if (threadIdx.x == 0) {
+    sh.s.cnt[0] = 0;
+    sh.s.cnt[1] = 0;
+  }
+  int valid;
+  uint32_t kmin, kmax;
+  key_range(sh.s, k, valid, kmin, kmax);
+  Thr th0, th1;
+  select_thresholds(sh.c, sh.s, k, valid, kmin, kmax, K0, K1, 0, th0, th1);
+  emit_sel(
+      sh.s, k, th0, th1,
+      [&](int t, int pos, int j, int i) {
+        int32_t id = i;
+        if constexpr (LAYOUT == kSelPool) id = 8 * pbv[j] + (i & 7);
+        (t ? o1 : o0)[pos] = id;
+      },
+      [&](int t, int p) { (t ? o1 : o0)[p] = -1; });
+}
+
+// Block rows of up to 65,536 blocks, targets of at most 2048 blocks.
+// Level 1 ranks super-blocks (8 consecutive blocks) by their maximum and keeps
+// those at or above the threshold bin of the K-th (or exactly the first K);
+// every block of the first K blocks lies in them and scores at least that
+// threshold T1.  Level 2 gathers the blocks >= T1 of the kept super-blocks in
+// id order and selects exactly among them.
+struct Blocks2Shared {
+  int32_t cids[kCompCap];
+  union {
+    uint32_t ckeys[kCompCap];
+    Core c;
+  } u;
+  int32_t sbsel[kKeepCap];
+  int gcnt[kGatherIters][kSelWaves];
+  Small s;
+};
+
+template <bool kHaveSuper>
+__global__ __launch_bounds__(kSelThreads) void select_blocks2_kernel(const float* __restrict__ bmax, int64_t stride,
+                                                                     const float* __restrict__ super_max,
+                                                                     int64_t nsup_stride,
+                                                                     const int32_t* __restrict__ n_visible, int K0,
+                                                                     int32_t* __restrict__ out0, int K1,
+                                                                     int32_t* __restrict__ out1) {
+  __shared__ Blocks2Shared sh;
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int64_t nv = n_visible[r];
+  nv = nv < 0 ? 0 : nv;
+  int nblk = (int)(((nv + 7) >> 3) < stride ? ((nv + 7) >> 3) : stride);
+  const int nsuper = (nblk + 7) >> 3;
+  const float* row = bmax + (int64_t)r * stride;
+  int32_t* o0 = out0 ? out0 + (int64_t)r * K0 : nullptr;
+  int32_t* o1 = out1 ? out1 + (int64_t)r * K1 : nullptr;
+  if (!out0) K0 = 0;
+  if (!out1) K1 = 0;
+  const int kmaxK = K0 > K1 ? K0 : K1;
+
+  // level 1: super-block maxima, super-block i = item i
+  auto load_level1 = [&](uint32_t (&k1)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = (w * 8 + j) * 64 + lane;
+      uint32_t key = 0u;
+      if (i < nsuper) {
+        if constexpr (kHaveSuper) {
+          key = order_key(super_max[(int64_t)r * nsup_stride + i]);
+        } else {
+          const uint32_t b0 = 8u * (uint32_t)i;
+          uint32_t m = 0u;
+#pragma unroll
+          for (uint32_t e = 0; e < 8; ++e) {
+            const uint32_t x = b0 + e < (uint32_t)nblk ? order_key(row[b0 + e]) : 0u;
+            m = x > m ? x : m;
+          }
+          key = m;
+        }
+      }
+      k1[j] = key;
+    }
+  };
+  uint32_t k1[8];
+  load_level1(k1);
+  hist_zero(sh.u.c);
+  if (threadIdx.x == 0) {
+    sh.s.cnt[0] = 0;
+    sh.s.cnt[1] = 0;
+  }
+  int valid1;
+  uint32_t kmin1, kmax1;
+  key_range(sh.s, k1, valid1, kmin1, kmax1);
+
+  int approx = kKeepCap;
+  int m2 = 0;
+  uint32_t T1 = 1u;
+  for (;;) {
+    Thr a0, a1;
+    select_thresholds(sh.u.c, sh.s, k1, valid1, kmin1, kmax1, kmaxK, 0, approx, a0, a1);
+    emit_sel(
+        sh.s, k1, a0, a1, [&](int t, int pos, int j, int i) { sh.sbsel[pos] = i; }, [&](int t, int p) {});
+    __syncthreads();
+    const int nkept = a0.keff;
+    T1 = a0.T;
+    // gather: lane takes block (tid & 7) of kept super-block q*128 + tid/8
+    uint32_t g[kGatherIters];
+#pragma unroll
+    for (int q = 0; q < kGatherIters; ++q) {
+      const int u = q * 128 + ((int)threadIdx.x >> 3);
+      uint32_t key = 0u;
+      if (u < nkept) {
+        const uint32_t blk = 8u * (uint32_t)sh.sbsel[u] + (threadIdx.x & 7u);
+        if (blk < (uint32_t)nblk) key = order_key(row[blk]);
+      }
+      g[q] = key >= T1 ? key : 0u;
+    }
+    // survivors per (q, wave); item order (q, wave, lane) is block id order
+#pragma unroll
+    for (int q = 0; q < kGatherIters; ++q) {
+      const int c = __popcll(__ballot(g[q] != 0u));
+      if (lane == 0) sh.gcnt[q][w] = c;
+    }
+    __syncthreads();
+    int qtot = 0, qpre = 0;
+    if (lane < kGatherIters) {
+#pragma unroll
+      for (int v = 0; v < kSelWaves; ++v) {
+        const int c = sh.gcnt[lane][v];
+        qpre += v < w ? c : 0;
+        qtot += c;
+      }
+    }
+    const int qincl = wave_incl_scan(qtot);
+    m2 = __builtin_amdgcn_readlane(qincl, 63);
+    if (m2 > kCompCap && approx > 0) {
+      // too many survivors for LDS: redo level 1 exactly (at most 8 * 2048)
+      approx = 0;
+      load_level1(k1);
+      hist_zero(sh.u.c);
+      __syncthreads();
+      continue;
+    }
+    const int qbase = qincl - qtot + qpre;   // lane q: first position of (q, this wave)
+#pragma unroll
+    for (int q = 0; q < kGatherIters; ++q) {
+      const unsigned long long m = __ballot(g[q] != 0u);
+      const int pos = __builtin_amdgcn_readlane(qbase, q) + mbcnt(m);
+      if (g[q] != 0u && pos < kCompCap) {
+        const int u = q * 128 + ((int)threadIdx.x >> 3);
+        sh.u.ckeys[pos] = g[q];
+        sh.cids[pos] = 8 * sh.sbsel[u] + ((int)threadIdx.x & 7);
+      }
+    }
+    break;
+  }
+  __syncthreads();
+  m2 = m2 < kCompCap ? m2 : kCompCap;   // (exact level 1 keeps at most 8 * 2048 blocks)
+  // level 2 over the m2 survivors (id order), 16 per lane
+  uint32_t k2[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int i = (w * 16 + j) * 64 + lane;
+    k2[j] = i < m2 ? sh.u.ckeys[i] : 0u;
+  }
+  __syncthreads();
+  hist_zero(sh.u.c);
+  __syncthreads();
+  Thr th0, th1;
+  select_thresholds(sh.u.c, sh.s, k2, m2, T1, kmax1, K0, K1, 0, th0, th1);
+  emit_sel(
+      sh.s, k2, th0, th1, [&](int t, int pos, int j, int i) { (t ? o1 : o0)[pos] = sh.cids[i]; },
+      [&](int t, int p) { (t ? o1 : o0)[p] = -1; });
+}
+
+// ---------------------------------------------------------------------------
+// generic selection: the row stays in memory
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSelThreads) void select_mem_kernel(int layout, const float* __restrict__ scores,
+                                                                 int64_t stride,
+                                                                 const int32_t* __restrict__ pool_blocks,
+                                                                 int64_t n_pool,
+                                                                 const int32_t* __restrict__ n_visible, int k1,
+                                                                 int32_t* __restrict__ out1, int k2,
+                                                                 int32_t* __restrict__ out2) {
   __shared__ SelShared sh;
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -535,94 +1105,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int layout, const f
   if (!out2) k2 = 0;
   int32_t* o1 = out1 ? out1 + (int64_t)r * k1 : nullptr;
   int32_t* o2 = out2 ? out2 + (int64_t)r * k2 : nullptr;
-
-  if constexpr (PATH == kPathLds) {
-    // the whole row in LDS (the host guarantees row.n <= kRowCap)
-    KeyStats st;
+  KeyStats st;
+  for (int64_t base = 0; base < row.n; base += kSelCap) {
 #pragma unroll 10
     for (int j = 0; j < kSegIters; ++j) {
-      const int i = w * kSegItems + 64 * j + lane;
-      const uint32_t k = i < row.n ? row.key_mem(i) : 0u;
-      sh.u.keys[i] = k;
-      st.add(k);
+      const int64_t i = base + (int64_t)w * kSegItems + 64 * j + lane;
+      st.add(i < row.n ? row.key_mem(i) : 0u);
     }
-    reduce_stats(sh, st);
-    select_targets<kSrcKeys, kIdRow, false, false>(sh, row, row.n, k1, o1, k2, o2);
-  } else if constexpr (PATH == kPathSuper) {
-    // block maxima (the host guarantees nsuper <= kSuperCap and k <= 2048)
-    const int64_t nsuper = (row.n + 7) >> 3;
-    const int kmax = k1 > k2 ? k1 : k2;
-    if (super_max) {
-      // level 1 from the scan's super-block maxima
-      KeyStats st;
-      const float* srow = super_max + (int64_t)r * nsup_stride;
-#pragma unroll 10
-      for (int j = 0; j < kSegIters; ++j) {
-        const int i = w * kSegItems + 64 * j + lane;
-        if (i < nsuper) {
-          const uint32_t k = order_key(srow[i]);
-          sh.u.skeys[i] = k;
-          st.add(k);
-        }
-      }
-      reduce_stats(sh, st);
-    } else {
-      // level 1: super-block maxima of 8 consecutive blocks; lanes read
-      // consecutive blocks (coalesced) and reduce over groups of 8 lanes
-      KeyStats st;
-      for (int64_t b0 = 0; b0 < 8 * nsuper; b0 += (int64_t)kSelThreads * 8) {
-        uint32_t kk[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int64_t i = b0 + (int64_t)w * 512 + 64 * j + lane;
-          kk[j] = i < row.n ? order_key(row.s[i]) : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t m = group8_max(kk[j]);
-          const int64_t i = b0 + (int64_t)w * 512 + 64 * j + lane;
-          if ((lane & 7) == 0 && (i >> 3) < nsuper) {
-            sh.u.skeys[i >> 3] = m;
-            st.add(m);
-          }
-        }
-      }
-      reduce_stats(sh, st);
-    }
-    // keep (at least) the first kmax super-blocks, ascending, in sbsel
-    select_targets<kSrcSuper, kIdIndex, true, true>(sh, row, nsuper, kmax, nullptr, 0, nullptr, kLevelCap);
-    const int nsel = sh.res[6];
-    // level 2: the blocks of the kept super-blocks, gathered into LDS
-    {
-      KeyStats st;
-#pragma unroll 10
-      for (int j = 0; j < kSegIters; ++j) {
-        const int i = w * kSegItems + 64 * j + lane;
-        uint32_t k = 0u;
-        if (i < 8 * nsel) {
-          const int32_t sb = sh.sbsel[i >> 3];
-          const int64_t blk = 8 * (int64_t)sb + (i & 7);
-          k = (sb >= 0 && blk < row.n) ? order_key(row.s[blk]) : 0u;
-        }
-        sh.u.keys[i] = k;
-        st.add(k);
-      }
-      reduce_stats(sh, st);
-    }
-    select_targets<kSrcKeys, kIdSuperList, false, false>(sh, row, 8 * (int64_t)nsel, k1, o1, k2, o2);
-  } else {
-    // the row stays in memory
-    KeyStats st;
-    for (int64_t base = 0; base < row.n; base += kSelCap) {
-#pragma unroll 10
-      for (int j = 0; j < kSegIters; ++j) {
-        const int64_t i = base + (int64_t)w * kSegItems + 64 * j + lane;
-        st.add(i < row.n ? row.key_mem(i) : 0u);
-      }
-    }
-    reduce_stats(sh, st);
-    select_targets<kSrcMem, kIdRow, false, false>(sh, row, row.n, k1, o1, k2, o2);
   }
+  reduce_stats(sh, st);
+  select_targets<kSrcMem, kIdRow, false, false>(sh, row, row.n, k1, o1, k2, o2);
 }
 
 hipError_t launch_select(int layout, const float* scores, int64_t stride, const int32_t* pool_blocks,
@@ -633,15 +1125,35 @@ hipError_t launch_select(int layout, const float* scores, int64_t stride, const 
   const int ka = out1 ? k1 : 0, kb = out2 ? k2 : 0;
   const int kmax = ka > kb ? ka : kb;
   const dim3 grid((unsigned)R), block(kSelThreads);
-  if (max_n <= kRowCap)
-    hipLaunchKernelGGL(select_kernel<kPathLds>, grid, block, 0, stream, layout, scores, stride, pool_blocks, n_pool,
-                       n_visible, k1, out1, k2, out2, super_max, nsup_stride);
-  else if (layout == kSelBlocks && (max_n + 7) / 8 <= kSuperCap && kmax <= 2048)
-    hipLaunchKernelGGL(select_kernel<kPathSuper>, grid, block, 0, stream, layout, scores, stride, pool_blocks, n_pool,
-                       n_visible, k1, out1, k2, out2, super_max, nsup_stride);
-  else
-    hipLaunchKernelGGL(select_kernel<kPathMem>, grid, block, 0, stream, layout, scores, stride, pool_blocks, n_pool,
-                       n_visible, k1, out1, k2, out2, super_max, nsup_stride);
+#define CSA2_REG(J, L)                                                                                      \
+  hipLaunchKernelGGL((select_reg_kernel<J, L>), grid, block, 0, stream, scores, stride, pool_blocks, n_pool, \
+                     n_visible, k1, out1, k2, out2)
+#define CSA2_REG_J(J)                   \
+  if (layout == kSelBlocks)             \
+    CSA2_REG(J, kSelBlocks);            \
+  else if (layout == kSelPool)          \
+    CSA2_REG(J, kSelPool);              \
+  else                                  \
+    CSA2_REG(J, kSelFull)
+  if (max_n <= 4096) {
+    CSA2_REG_J(4);
+  } else if (max_n <= 8192) {
+    CSA2_REG_J(8);
+  } else if (max_n <= 16384) {
+    CSA2_REG_J(16);
+  } else if (layout == kSelBlocks && (max_n + 7) / 8 <= 8192 && kmax <= 2048) {
+    if (super_max)
+      hipLaunchKernelGGL(select_blocks2_kernel<true>, grid, block, 0, stream, scores, stride, super_max, nsup_stride,
+                         n_visible, k1, out1, k2, out2);
+    else
+      hipLaunchKernelGGL(select_blocks2_kernel<false>, grid, block, 0, stream, scores, stride, super_max,
+                         nsup_stride, n_visible, k1, out1, k2, out2);
+  } else {
+    hipLaunchKernelGGL(select_mem_kernel, grid, block, 0, stream, layout, scores, stride, pool_blocks, n_pool,
+                       n_visible, k1, out1, k2, out2);
+  }
+#undef CSA2_REG_J
+#undef CSA2_REG
   return hipGetLastError();
 }
 
