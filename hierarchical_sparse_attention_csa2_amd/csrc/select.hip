@@ -505,9 +505,10 @@ __device__ __forceinline__ void select_targets(SelShared& sh, const RowView row,
 // register-resident selection (rows up to 16,384 items, and the two-level
 // block filter)
 // ---------------------------------------------------------------------------
-// Item (w, j, lane) of a J-item-per-lane row is index (w*J + j)*64 + lane, so
-// item order is id order and a wave's items are one contiguous range.
-constexpr int kRankCap = 256;                      // threshold-bin members resolved by counting
+// A row of up to n items is held as Jp = ceil(n/1024) <= J items a lane; item
+// (w, j, lane) is index (w*Jp + j)*64 + lane, so item order is id order, a
+// wave's items are one contiguous range and every pass stops after Jp slots.
+constexpr int kRankCap = 128;                      // threshold-bin members resolved by counting
 constexpr int kKeepCap = 3072;                     // super-blocks kept by level 1
 constexpr int kCompCap = 16384;                    // blocks surviving into level 2
 constexpr int kGatherIters = kKeepCap / 128;       // 8 lanes per super-block
@@ -544,17 +545,24 @@ __device__ __forceinline__ int row_incl_scan(int x) {
   return x;
 }
 
+// sum over each aligned group of 4 lanes
+__device__ __forceinline__ int quad_sum(int x) {
+  x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  return x;
+}
+
 // Count, min and max of the non-zero keys over the workgroup (every thread
 // gets them).  One barrier.
 template <int J>
-__device__ __forceinline__ void key_range(Small& s, const uint32_t (&k)[J], int& valid, uint32_t& kmin,
+__device__ __forceinline__ void key_range(Small& s, const uint32_t (&k)[J], int Jp, int& valid, uint32_t& kmin,
                                           uint32_t& kmax) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int c = 0;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const uint32_t x = k[j];
+    const uint32_t x = j < Jp ? k[j] : 0u;
     c += x != 0u;
     mn = (x != 0u && x < mn) ? x : mn;
     mx = x > mx ? x : mx;
@@ -582,13 +590,13 @@ __device__ __forceinline__ void hist_zero(Core& c) {
 // hist[((key - kmin) >> shift) & (2^bits - 1)] += 1 over the non-zero keys with
 // ((key - kmin) >> pshift) == prefix (pshift >= 32: every key).
 template <int J>
-__device__ __forceinline__ void hist_add(Core& c, const uint32_t (&k)[J], uint32_t kmin, int shift, int bits,
+__device__ __forceinline__ void hist_add(Core& c, const uint32_t (&k)[J], int Jp, uint32_t kmin, int shift, int bits,
                                          int pshift, uint32_t prefix) {
   const uint32_t dmask = (1u << bits) - 1u;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const uint32_t d = k[j] - kmin;
-    const bool in = k[j] != 0u && (pshift >= 32 || (d >> pshift) == prefix);
+    const bool in = j < Jp && k[j] != 0u && (pshift >= 32 || (d >> pshift) == prefix);
     if (in) atomicAdd(&c.hist[(d >> shift) & dmask], 1u);
   }
 }
@@ -646,23 +654,26 @@ __device__ __forceinline__ void find_bins(Core& c, Small& s, int need0, int need
 // Copy the non-zero keys with ((key - kmin) >> cur_t) == prefix_t into mem[t]
 // (any order) for the targets with want_t.  Ends synchronised.
 template <int J>
-__device__ __forceinline__ void collect_bins(Core& c, Small& s, const uint32_t (&k)[J], uint32_t kmin, bool want0,
-                                             int cur0, uint32_t prefix0, bool want1, int cur1, uint32_t prefix1) {
+__device__ __forceinline__ void collect_bins(Core& c, Small& s, const uint32_t (&k)[J], int Jp, uint32_t kmin,
+                                             bool want0, int cur0, uint32_t prefix0, bool want1, int cur1,
+                                             uint32_t prefix1) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const uint32_t d = k[j] - kmin;
+    if (j < Jp) {
+      const uint32_t d = k[j] - kmin;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bool want = t ? want1 : want0;
-      if (!want) continue;
-      const bool in = k[j] != 0u && (d >> (t ? cur1 : cur0)) == (t ? prefix1 : prefix0);
-      const unsigned long long m = __ballot(in);
-      if (m) {
-        int b = 0;
-        if (lane == 0) b = atomicAdd(&s.cnt[t], __popcll(m));
-        b = __builtin_amdgcn_readfirstlane(b);
-        if (in) c.mem[t][b + mbcnt(m)] = k[j];
+      for (int t = 0; t < 2; ++t) {
+        const bool want = t ? want1 : want0;
+        if (!want) continue;
+        const bool in = k[j] != 0u && (d >> (t ? cur1 : cur0)) == (t ? prefix1 : prefix0);
+        const unsigned long long m = __ballot(in);
+        if (m) {
+          int b = 0;
+          if (lane == 0) b = atomicAdd(&s.cnt[t], __popcll(m));
+          b = __builtin_amdgcn_readfirstlane(b);
+          if (in) c.mem[t][b + mbcnt(m)] = k[j];
+        }
       }
     }
   }
@@ -670,39 +681,35 @@ __device__ __forceinline__ void collect_bins(Core& c, Small& s, const uint32_t (
 }
 
 // For each wanted target, the need-th largest of its m members (T) and how
-// many members equal to T are taken.  Threads [0, 512) serve target 0, [512,
-// 1024) target 1: each counts the members above and equal to its own.
+// many members equal to T are taken.  Threads [512t, 512t + 512) serve target
+// t, four per member: each compares its member with every fourth member and
+// the quad adds up the counts above and equal.
 __device__ __forceinline__ void rank_members(Core& c, Small& s, bool want0, int m0, int need0, bool want1, int m1,
                                              int need1, uint32_t& T0, int& take0, uint32_t& T1, int& take1) {
-  const int t = threadIdx.x >> 9, u = threadIdx.x & 511;
+  const int t = threadIdx.x >> 9, u = (threadIdx.x & 511) >> 2, part = threadIdx.x & 3;
   const bool want = t ? want1 : want0;
   const int m = t ? m1 : m0, need = t ? need1 : need0;
+  const bool mine = want && u < m;
   if (threadIdx.x == 0) {
     s.cnt[0] = 0;
     s.cnt[1] = 0;
   }
-  if (want && u < m) {
+  int gt = 0, eq = 0;
+  uint32_t x = 0u;
+  if (mine) {
     const uint32_t* mem = t ? c.mem[1] : c.mem[0];
-    const uint32_t x = mem[u];
-    int gt = 0, eq = 0;
-    int v = 0;
-    for (; v + 4 <= m; v += 4) {
-      const u32x4_t y = *reinterpret_cast<const u32x4_t*>(&mem[v]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gt += y[e] > x;
-        eq += y[e] == x;
-      }
-    }
-    for (; v < m; ++v) {
+    x = mem[u];
+    for (int v = part; v < m; v += 4) {
       const uint32_t y = mem[v];
       gt += y > x;
       eq += y == x;
     }
-    if (gt < need && need <= gt + eq) {
-      s.res[8 + 2 * t] = (int)x;
-      s.res[9 + 2 * t] = need - gt;
-    }
+  }
+  gt = quad_sum(gt);
+  eq = quad_sum(eq);
+  if (mine && part == 0 && gt < need && need <= gt + eq) {
+    s.res[8 + 2 * t] = (int)x;
+    s.res[9 + 2 * t] = need - gt;
   }
   __syncthreads();
   if (want0) {
@@ -729,9 +736,9 @@ struct Thr {
 // target 0 may instead keep every key of its threshold bin and above when that
 // is at most approx_cap keys.
 template <int J>
-__device__ __forceinline__ void select_thresholds(Core& c, Small& s, const uint32_t (&k)[J], int valid, uint32_t kmin,
-                                                  uint32_t kmax, int K0, int K1, int approx_cap, Thr& th0,
-                                                  Thr& th1) {
+__device__ __forceinline__ void select_thresholds(Core& c, Small& s, const uint32_t (&k)[J], int Jp, int valid,
+                                                  uint32_t kmin, uint32_t kmax, int K0, int K1, int approx_cap,
+                                                  Thr& th0, Thr& th1) {
   const int keff0 = K0 > 0 ? (K0 < valid ? K0 : valid) : 0;
   const int keff1 = K1 > 0 ? (K1 < valid ? K1 : valid) : 0;
   th0 = Thr{1u, 0x7FFFFFFF, keff0, K0, keff0 > 0};
@@ -741,7 +748,7 @@ __device__ __forceinline__ void select_thresholds(Core& c, Small& s, const uint3
   const uint32_t span = kmax - kmin;
   const int bits = span ? 32 - __builtin_clz(span) : 0;
   const int s1 = bits > 12 ? bits - 12 : 0;
-  hist_add(c, k, kmin, s1, 12, 32, 0u);
+  hist_add(c, k, Jp, kmin, s1, 12, 32, 0u);
   __syncthreads();
   BinHit h0, h1;
   find_bins(c, s, act0 ? keff0 : 0, act1 ? keff1 : 0, h0, h1);
@@ -768,7 +775,7 @@ __device__ __forceinline__ void select_thresholds(Core& c, Small& s, const uint3
       const int nxt = cur > 12 ? cur - 12 : 0;
       hist_zero(c);
       __syncthreads();
-      hist_add(c, k, kmin, nxt, cur - nxt, cur, pre);
+      hist_add(c, k, Jp, kmin, nxt, cur - nxt, cur, pre);
       __syncthreads();
       BinHit g, unused;
       find_bins(c, s, need, 0, g, unused);
@@ -789,7 +796,7 @@ __device__ __forceinline__ void select_thresholds(Core& c, Small& s, const uint3
     act1 = false;
   }
   if (act0 || act1) {
-    collect_bins(c, s, k, kmin, act0, cur0, pre0, act1, cur1, pre1);
+    collect_bins(c, s, k, Jp, kmin, act0, cur0, pre0, act1, cur1, pre1);
     rank_members(c, s, act0, m0, need0, act1, m1, need1, th0.T, th0.take, th1.T, th1.take);
   }
 }
@@ -798,15 +805,16 @@ __device__ __forceinline__ void select_thresholds(Core& c, Small& s, const uint3
 // store(t, pos, j, i) writes the id of item i (slot j of this lane) at
 // position pos of target t; pad(t, p) writes the -1 padding.
 template <int J, class Store, class Pad>
-__device__ __forceinline__ void emit_sel(Small& s, const uint32_t (&k)[J], const Thr& th0, const Thr& th1,
+__device__ __forceinline__ void emit_sel(Small& s, const uint32_t (&k)[J], int Jp, const Thr& th0, const Thr& th1,
                                          Store store, Pad pad) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   // per-lane counts, two 16-bit fields per word (a wave counts at most 64*J)
   uint32_t c0 = 0u, c1 = 0u;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    c0 += (th0.on && k[j] > th0.T ? 1u : 0u) + (th0.on && k[j] == th0.T ? 0x10000u : 0u);
-    c1 += (th1.on && k[j] > th1.T ? 1u : 0u) + (th1.on && k[j] == th1.T ? 0x10000u : 0u);
+    const uint32_t x = j < Jp ? k[j] : 0u;
+    c0 += (th0.on && x > th0.T ? 1u : 0u) + (th0.on && x == th0.T ? 0x10000u : 0u);
+    c1 += (th1.on && x > th1.T ? 1u : 0u) + (th1.on && x == th1.T ? 0x10000u : 0u);
   }
   c0 = (uint32_t)wave_sum((int)c0);
   c1 = (uint32_t)wave_sum((int)c1);
@@ -831,26 +839,30 @@ __device__ __forceinline__ void emit_sel(Small& s, const uint32_t (&k)[J], const
   }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int i = (w * J + j) * 64 + lane;
+    if (j < Jp) {
+      const int i = (w * Jp + j) * 64 + lane;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const Thr& th = t ? th1 : th0;
-      if (!th.on) continue;
-      const bool tie = k[j] == th.T;
-      const unsigned long long mt = __ballot(tie);
-      const bool sel = k[j] > th.T || (tie && run_tie[t] + mbcnt(mt) < th.take);
-      const unsigned long long ms = __ballot(sel);
-      const int pos = run_sel[t] + mbcnt(ms);
-      if (sel && pos < th.keff) store(t, pos, j, i);
-      run_tie[t] += __popcll(mt);
-      run_sel[t] += __popcll(ms);
+      for (int t = 0; t < 2; ++t) {
+        const Thr& th = t ? th1 : th0;
+        if (!th.on) continue;
+        const bool tie = k[j] == th.T;
+        const unsigned long long mt = __ballot(tie);
+        const bool sel = k[j] > th.T || (tie && run_tie[t] + mbcnt(mt) < th.take);
+        const unsigned long long ms = __ballot(sel);
+        const int pos = run_sel[t] + mbcnt(ms);
+        if (sel && pos < th.keff) store(t, pos, j, i);
+        run_tie[t] += __popcll(mt);
+        run_sel[t] += __popcll(ms);
+      }
     }
   }
   for (int p = th0.keff + (int)threadIdx.x; p < th0.K; p += kSelThreads) pad(0, p);
   for (int p = th1.keff + (int)threadIdx.x; p < th1.K; p += kSelThreads) pad(1, p);
 }
 
-// Rows of at most 1024*J items (any layout), items in registers.
+// Rows of at most 1024*J items (any layout), items in registers.  The lane
+// layout follows the row's capacity (stride, or 8*n_pool slots), so the loads
+// are issued before n_visible arrives and masked after.
 template <int J, int LAYOUT>
 __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __restrict__ scores, int64_t stride,
                                                                  const int32_t* __restrict__ pool_blocks,
@@ -861,42 +873,40 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
   __shared__ RegShared sh;
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int cap = (int)(LAYOUT == kSelPool ? 8 * n_pool : stride);
+  const int Jp = (cap + 1023) >> 10;
+  const float* row = scores + (int64_t)r * cap;
+  const int32_t* pb = LAYOUT == kSelPool ? pool_blocks + (int64_t)r * n_pool : nullptr;
+  float x[J];
+  int32_t pbv[LAYOUT == kSelPool ? J : 1];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    x[j] = 0.0f;
+    if constexpr (LAYOUT == kSelPool) pbv[j] = -1;
+    const int i = (w * Jp + j) * 64 + lane;
+    if (j < Jp && i < cap) {
+      x[j] = row[i];
+      if constexpr (LAYOUT == kSelPool) pbv[j] = pb[i >> 3];
+    }
+  }
   int64_t nv = n_visible[r];
   nv = nv < 0 ? 0 : nv;
-  int64_t n;
-  const float* row;
-  const int32_t* pb = nullptr;
-  if (LAYOUT == kSelBlocks) {
-    row = scores + (int64_t)r * stride;
-    n = (nv + 7) >> 3;
-    n = n < stride ? n : stride;
-  } else if (LAYOUT == kSelPool) {
-    row = scores + (int64_t)r * n_pool * 8;
-    pb = pool_blocks + (int64_t)r * n_pool;
-    n = 8 * n_pool;
-  } else {
-    row = scores + (int64_t)r * stride;
-    n = nv < stride ? nv : stride;
+  int64_t n = cap;
+  if (LAYOUT == kSelBlocks) n = (nv + 7) >> 3;
+  if (LAYOUT == kSelFull) n = nv;
+  n = n < cap ? n : cap;
+  uint32_t k[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = (w * Jp + j) * 64 + lane;
+    bool ok = j < Jp && i < n;
+    if constexpr (LAYOUT == kSelPool) ok = ok && pbv[j] >= 0 && 8 * (int64_t)pbv[j] + (i & 7) < nv;
+    k[j] = ok ? order_key(x[j]) : 0u;
   }
   int32_t* o0 = out0 ? out0 + (int64_t)r * K0 : nullptr;
   int32_t* o1 = out1 ? out1 + (int64_t)r * K1 : nullptr;
   if (!out0) K0 = 0;
   if (!out1) K1 = 0;
-
-  uint32_t k[J];
-  int32_t pbv[LAYOUT == kSelPool ? J : 1];
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int i = (w * J + j) * 64 + lane;
-    if constexpr (LAYOUT == kSelPool) {
-      const int32_t blk = i < n ? pb[i >> 3] : -1;
-      const float x = i < n ? row[i] : 0.0f;
-      pbv[j] = blk;
-      k[j] = (blk >= 0 && 8 * (int64_t)blk + (i & 7) < nv) ? order_key(x) : 0u;
-    } else {
-      k[j] = i < n ? order_key(row[i]) : 0u;
-    }
-  }
   hist_zero(sh.c);
   if (threadIdx.x == 0) {
     sh.s.cnt[0] = 0;
@@ -904,11 +914,11 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
   }
   int valid;
   uint32_t kmin, kmax;
-  key_range(sh.s, k, valid, kmin, kmax);
+  key_range(sh.s, k, Jp, valid, kmin, kmax);
   Thr th0, th1;
-  select_thresholds(sh.c, sh.s, k, valid, kmin, kmax, K0, K1, 0, th0, th1);
+  select_thresholds(sh.c, sh.s, k, Jp, valid, kmin, kmax, K0, K1, 0, th0, th1);
   emit_sel(
-      sh.s, k, th0, th1,
+      sh.s, k, Jp, th0, th1,
       [&](int t, int pos, int j, int i) {
         int32_t id = i;
         if constexpr (LAYOUT == kSelPool) id = 8 * pbv[j] + (i & 7);
@@ -924,7 +934,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
 // threshold T1.  Level 2 gathers the blocks >= T1 of the kept super-blocks in
 // id order and selects exactly among them.
 struct Blocks2Shared {
-  int32_t cids[kCompCap];
+  int32_t cids[kCompCap];       // survivor -> slot q*1024 + tid of the gather
   union {
     uint32_t ckeys[kCompCap];
     Core c;
@@ -944,42 +954,48 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks2_kernel(const float
   __shared__ Blocks2Shared sh;
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int64_t nv = n_visible[r];
-  nv = nv < 0 ? 0 : nv;
-  int nblk = (int)(((nv + 7) >> 3) < stride ? ((nv + 7) >> 3) : stride);
-  const int nsuper = (nblk + 7) >> 3;
   const float* row = bmax + (int64_t)r * stride;
+  const int nsup_cap = (int)((stride + 7) >> 3);   // <= 8192
+  const int Jp1 = (nsup_cap + 1023) >> 10;
+  int64_t nv = n_visible[r];
   int32_t* o0 = out0 ? out0 + (int64_t)r * K0 : nullptr;
   int32_t* o1 = out1 ? out1 + (int64_t)r * K1 : nullptr;
   if (!out0) K0 = 0;
   if (!out1) K1 = 0;
   const int kmaxK = K0 > K1 ? K0 : K1;
 
-  // level 1: super-block maxima, super-block i = item i
-  auto load_level1 = [&](uint32_t (&k1)[8]) {
+  // level 1: super-block maxima, super-block i = item i (the scan's maxima are
+  // read ahead of n_visible)
+  float v1[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = (w * 8 + j) * 64 + lane;
-      uint32_t key = 0u;
-      if (i < nsuper) {
-        if constexpr (kHaveSuper) {
-          key = order_key(super_max[(int64_t)r * nsup_stride + i]);
-        } else {
-          const uint32_t b0 = 8u * (uint32_t)i;
-          uint32_t m = 0u;
+  for (int j = 0; j < 8; ++j) {
+    v1[j] = 0.0f;
+    const int i = (w * Jp1 + j) * 64 + lane;
+    if (kHaveSuper && j < Jp1 && i < nsup_cap) v1[j] = super_max[(int64_t)r * nsup_stride + i];
+  }
+  nv = nv < 0 ? 0 : nv;
+  const int nblk = (int)(((nv + 7) >> 3) < stride ? ((nv + 7) >> 3) : stride);
+  const int nsuper = (nblk + 7) >> 3;
+  uint32_t k1[8];
 #pragma unroll
-          for (uint32_t e = 0; e < 8; ++e) {
-            const uint32_t x = b0 + e < (uint32_t)nblk ? order_key(row[b0 + e]) : 0u;
-            m = x > m ? x : m;
-          }
-          key = m;
+  for (int j = 0; j < 8; ++j) {
+    const int i = (w * Jp1 + j) * 64 + lane;
+    uint32_t key = 0u;
+    if (j < Jp1 && i < nsuper) {
+      if constexpr (kHaveSuper) {
+        key = order_key(v1[j]);
+      } else {
+        // the maximum over the super-block's visible blocks
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int b = 8 * i + e;
+          const uint32_t x = b < nblk ? order_key(row[b]) : 0u;
+          key = x > key ? x : key;
         }
       }
-      k1[j] = key;
     }
-  };
-  uint32_t k1[8];
-  load_level1(k1);
+    k1[j] = key;
+  }
   hist_zero(sh.u.c);
   if (threadIdx.x == 0) {
     sh.s.cnt[0] = 0;
@@ -987,16 +1003,16 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks2_kernel(const float
   }
   int valid1;
   uint32_t kmin1, kmax1;
-  key_range(sh.s, k1, valid1, kmin1, kmax1);
+  key_range(sh.s, k1, Jp1, valid1, kmin1, kmax1);
 
   int approx = kKeepCap;
   int m2 = 0;
   uint32_t T1 = 1u;
   for (;;) {
     Thr a0, a1;
-    select_thresholds(sh.u.c, sh.s, k1, valid1, kmin1, kmax1, kmaxK, 0, approx, a0, a1);
+    select_thresholds(sh.u.c, sh.s, k1, Jp1, valid1, kmin1, kmax1, kmaxK, 0, approx, a0, a1);
     emit_sel(
-        sh.s, k1, a0, a1, [&](int t, int pos, int j, int i) { sh.sbsel[pos] = i; }, [&](int t, int p) {});
+        sh.s, k1, Jp1, a0, a1, [&](int t, int pos, int j, int i) { sh.sbsel[pos] = i; }, [&](int t, int p) {});
     __syncthreads();
     const int nkept = a0.keff;
     T1 = a0.T;
@@ -1004,23 +1020,28 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks2_kernel(const float
     uint32_t g[kGatherIters];
 #pragma unroll
     for (int q = 0; q < kGatherIters; ++q) {
+      g[q] = 0u;
       const int u = q * 128 + ((int)threadIdx.x >> 3);
-      uint32_t key = 0u;
       if (u < nkept) {
         const uint32_t blk = 8u * (uint32_t)sh.sbsel[u] + (threadIdx.x & 7u);
-        if (blk < (uint32_t)nblk) key = order_key(row[blk]);
+        if (blk < (uint32_t)nblk) {
+          const uint32_t key = order_key(row[blk]);
+          g[q] = key >= T1 ? key : 0u;
+        }
       }
-      g[q] = key >= T1 ? key : 0u;
     }
     // survivors per (q, wave); item order (q, wave, lane) is block id order
 #pragma unroll
     for (int q = 0; q < kGatherIters; ++q) {
-      const int c = __popcll(__ballot(g[q] != 0u));
-      if (lane == 0) sh.gcnt[q][w] = c;
+      if (q * 128 < nkept) {
+        const int c = __popcll(__ballot(g[q] != 0u));
+        if (lane == 0) sh.gcnt[q][w] = c;
+      }
     }
     __syncthreads();
+    const int nq = (nkept + 127) >> 7;
     int qtot = 0, qpre = 0;
-    if (lane < kGatherIters) {
+    if (lane < nq) {
 #pragma unroll
       for (int v = 0; v < kSelWaves; ++v) {
         const int c = sh.gcnt[lane][v];
@@ -1033,7 +1054,6 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks2_kernel(const float
     if (m2 > kCompCap && approx > 0) {
       // too many survivors for LDS: redo level 1 exactly (at most 8 * 2048)
       approx = 0;
-      load_level1(k1);
       hist_zero(sh.u.c);
       __syncthreads();
       continue;
@@ -1041,32 +1061,38 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks2_kernel(const float
     const int qbase = qincl - qtot + qpre;   // lane q: first position of (q, this wave)
 #pragma unroll
     for (int q = 0; q < kGatherIters; ++q) {
-      const unsigned long long m = __ballot(g[q] != 0u);
-      const int pos = __builtin_amdgcn_readlane(qbase, q) + mbcnt(m);
-      if (g[q] != 0u && pos < kCompCap) {
-        const int u = q * 128 + ((int)threadIdx.x >> 3);
-        sh.u.ckeys[pos] = g[q];
-        sh.cids[pos] = 8 * sh.sbsel[u] + ((int)threadIdx.x & 7);
+      const unsigned long long m = q * 128 < nkept ? __ballot(g[q] != 0u) : 0ull;
+      if (m) {
+        const int pos = __builtin_amdgcn_readlane(qbase, q) + mbcnt(m);
+        if (g[q] != 0u && pos < kCompCap) {
+          sh.u.ckeys[pos] = g[q];
+          sh.cids[pos] = q * 1024 + (int)threadIdx.x;
+        }
       }
     }
     break;
   }
   __syncthreads();
   m2 = m2 < kCompCap ? m2 : kCompCap;   // (exact level 1 keeps at most 8 * 2048 blocks)
-  // level 2 over the m2 survivors (id order), 16 per lane
+  // level 2 over the m2 survivors (id order)
+  const int Jp2 = (m2 + 1023) >> 10;
   uint32_t k2[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int i = (w * 16 + j) * 64 + lane;
-    k2[j] = i < m2 ? sh.u.ckeys[i] : 0u;
+    const int i = (w * Jp2 + j) * 64 + lane;
+    k2[j] = (j < Jp2 && i < m2) ? sh.u.ckeys[i] : 0u;
   }
   __syncthreads();
   hist_zero(sh.u.c);
   __syncthreads();
   Thr th0, th1;
-  select_thresholds(sh.u.c, sh.s, k2, m2, T1, kmax1, K0, K1, 0, th0, th1);
+  select_thresholds(sh.u.c, sh.s, k2, Jp2, m2, T1, kmax1, K0, K1, 0, th0, th1);
   emit_sel(
-      sh.s, k2, th0, th1, [&](int t, int pos, int j, int i) { (t ? o1 : o0)[pos] = sh.cids[i]; },
+      sh.s, k2, Jp2, th0, th1,
+      [&](int t, int pos, int j, int i) {
+        const int slot = sh.cids[i];
+        (t ? o1 : o0)[pos] = 8 * sh.sbsel[slot >> 3] + (slot & 7);
+      },
       [&](int t, int p) { (t ? o1 : o0)[p] = -1; });
 }
 
