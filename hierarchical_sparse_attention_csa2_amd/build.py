@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcsa2.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["scan.hip", "select.hip", "attn.hip", "csa2_abi.hip"]
+SOURCES = ["scan.hip", "prefill_scan.hip", "select.hip", "attn.hip", "csa2_abi.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -28,6 +28,11 @@ HIPCC_FLAGS = [
 ]
 
 
+# per-source extra flags: the prefill scan keeps its MFMA results in VGPRs (the
+# code reads every result element once, right away)
+EXTRA_FLAGS = {"prefill_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -37,7 +42,8 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:

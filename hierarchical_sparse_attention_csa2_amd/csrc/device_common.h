@@ -88,6 +88,45 @@ __device__ __forceinline__ uint32_t halfwave_quad_max(uint32_t k) {
   return k;
 }
 
+// max / min over each row of 16 lanes (every lane of the row gets it), then over the wave
+__device__ __forceinline__ uint32_t row16_max(uint32_t x) {
+  uint32_t y;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x = y > x ? y : x;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x = y > x ? y : x;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x = y > x ? y : x;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);  // row_mirror
+  return y > x ? y : x;
+}
+__device__ __forceinline__ uint32_t row16_min(uint32_t x) {
+  uint32_t y;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+  x = y < x ? y : x;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+  x = y < x ? y : x;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);
+  x = y < x ? y : x;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);
+  return y < x ? y : x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = row16_max(x);
+  uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  a = a > b ? a : b;
+  c = c > d ? c : d;
+  return a > c ? a : c;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = row16_min(x);
+  uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  a = a < b ? a : b;
+  c = c < d ? c : d;
+  return a < c ? a : c;
+}
 // Convert a query block of 16 code bytes to 16 f16 pairs.
 __device__ __forceinline__ void load_query_block(const uint8_t* codes16, half2_t* q) {
   u32x4_t c = *reinterpret_cast<const u32x4_t*>(codes16);

@@ -10,6 +10,13 @@ hipError_t launch_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, co
                              float* scores, float* block_max, int64_t nblk_stride, float* super_max,
                              int64_t nsup_stride, hipStream_t stream);
 
+// Many queries per sequence (M > 1) on the FP4 matrix cores; same outputs as
+// launch_index_scan.
+hipError_t launch_prefill_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                               const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
+                               float* scores, float* block_max, int64_t nblk_stride, float* super_max,
+                               int64_t nsup_stride, hipStream_t stream);
+
 hipError_t launch_pool_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                             const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool,
                             const int32_t* n_visible, int B, int M, int64_t N_max, float* pool_scores,

@@ -25,6 +25,7 @@ constexpr int kScanWaves = kScanThreads / 64;
 constexpr int kSupersPerWave = 2;                               // 64-position super-blocks per wave
 constexpr int kScanChunk = kScanWaves * kSupersPerWave * 64;    // positions per workgroup
 constexpr int kScanGroups = kSupersPerWave * 4;                  // 16-position groups per wave
+constexpr int kPrefillMinQueries = 16;                           // queries per sequence for the MFMA scan
 
 __device__ __forceinline__ u32x4_t load_codes16(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -165,6 +166,10 @@ hipError_t launch_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, co
                              const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
                              float* scores, float* block_max, int64_t nblk_stride, float* super_max,
                              int64_t nsup_stride, hipStream_t stream) {
+  // many queries per sequence share every key: the matrix-core scan
+  if (M >= kPrefillMinQueries)
+    return launch_prefill_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, scores, block_max,
+                               nblk_stride, super_max, nsup_stride, stream);
   const int R = B * M;
   dim3 grid((unsigned)((N_max + kScanChunk - 1) / kScanChunk), (unsigned)R);
 #define CSA2_SCAN(S, P)                                                                                         \

@@ -65,6 +65,39 @@ def test_index_scan_bitexact(kind, N, nv):
         assert np.array_equal(f32_bits(smax[r, :ns]), f32_bits(np.array(want, np.float32))), r
 
 
+def _same_f32(a, b):
+    """Bitwise equality, except that any NaN matches any NaN."""
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    both_nan = np.isnan(a) & np.isnan(b)
+    return bool(np.all(both_nan | (f32_bits(a) == f32_bits(b))))
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread"])
+@pytest.mark.parametrize("B,M,N", [(1, 40, 3000), (2, 33, 2100), (1, 130, 5000)])
+def test_prefill_scan_bitexact(kind, B, M, N):
+    """Many queries per sequence (the matrix-core scan): scores, block maxima and
+    super-block maxima bit-exact for ragged visibility, partial query groups,
+    several key chunks, and tiles whose scales need the VALU path (spread)."""
+    w = Workload("pf", 777 + N + M, B=B, N=N, M=M)
+    cache, (lay,) = host_inputs(w, kind=kind)
+    rng = np.random.default_rng(N + 3 * M)
+    nv = rng.integers(1, N + 1, size=w.R).astype(np.int32)
+    nv[0], nv[-1], nv[w.R // 2] = N, 1, 0
+    lay["n_visible"] = nv
+    say(f"prefill scan B={B} M={M} N={N} kind={kind}")
+    scores, bmax, smax = _run_scan(w, dev(cache), dev(lay), want_super=True)
+    ref = oracle_full(w, cache, lay, want_scores=True, want_block_max=True)
+    for r in range(w.R):
+        n = nv[r]
+        assert _same_f32(scores[r, :n], ref["scores"][r, :n]), r
+        nb = (n + 7) // 8
+        assert _same_f32(bmax[r, :nb], ref["block_max"][r, :nb]), r
+        ns = (n + 63) // 64
+        want = [np.max(ref["block_max"][r, 8 * s:min(8 * s + 8, nb)]) for s in range(ns)]
+        assert _same_f32(smax[r, :ns], np.array(want, np.float32)), r
+
+
 @pytest.mark.parametrize("kind", ["normal", "ties", "spread"])
 @pytest.mark.parametrize("N,n_pool,k,nv", [
     (4096, 2048, 512, [4096, 4000, 3333]),      # pool covers all blocks
