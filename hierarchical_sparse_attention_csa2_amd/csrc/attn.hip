@@ -11,10 +11,10 @@
 // query and the probabilities are split into hi + lo bf16 parts, so every
 // product carries ~16 mantissa bits and accumulates in fp32.
 //
-// Workgroup = (split, row): H/8 waves.  A pair of waves owns 16 heads; each of
-// the two keeps the query (hi/lo) and the output accumulator O^T for its half of
-// the 512 dims in registers, and the two partial S^T tiles are summed through
-// LDS.  Entries stream through LDS in chunks of 64: each chunk is decoded
+// Workgroup = (split, row, head group of 32): 4 waves.  A pair of waves owns 16
+// heads; each of the two keeps the query (hi/lo) and the output accumulator O^T
+// for its half of the 512 dims in registers, and the two partial S^T tiles are
+// summed through LDS.  Entries stream through LDS in chunks of 64: each chunk is decoded
 // once into a row-major copy (operand A of S^T = C Q^T) and a transposed copy
 // (operand A of O^T = C^T P^T).  S^T's accumulator layout gives each lane the
 // probabilities of exactly the entries it must feed as operand B of the second
@@ -83,7 +83,7 @@ template <int NP, int KIND>
 __device__ __forceinline__ void decode_chunk(const AttnParams& a, const int64_t* sOff, const int* sType,
                                              unsigned long long vmask, __bf16* sK, __bf16* sVt, int tid) {
   constexpr int kTPT = (kChunk / 4) * 64 / (NP * 128);   // tiles per thread
-  constexpr int kGroup = kTPT > 2 ? kTPT / 2 : 1;         // tiles whose gathers are in flight together
+  constexpr int kGroup = kTPT;                            // every tile's gathers in flight together
 #pragma unroll
   for (int j0 = 0; j0 < kTPT; j0 += kGroup) {
     uint32_t raw0[kGroup][4], raw1[kGroup][4];
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
   const int dbase = 256 * half;
   const int g = lane >> 4;     // lane group 0..3
   const int hl = lane & 15;
-  const int h = 16 * pr + hl;
+  const int h = 16 * NP * blockIdx.z + 16 * pr + hl;   // head groups of 16*NP heads across blockIdx.z
 
   int wl = a.win_max > 0 ? a.win_len[r] : 0;
   wl = wl < 0 ? 0 : (wl > a.win_max ? a.win_max : wl);
@@ -169,30 +169,41 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
   int c_end = c_begin + a.chunks_per_split;
   c_end = c_end < a.n_chunks ? c_end : a.n_chunks;
 
-  // the first chunk's selected indices load while the query loads
+  // The first chunk's selected indices load first (the entry table waits on
+  // them alone: the memory counter retires loads in order), then the query.
+  // The query is converted to bf16 hi/lo after the first chunk's gathers are in
+  // flight, so its load stays off the index -> gather -> decode path.
   int64_t idx_next = -1;
   if (tid < kChunk && c_begin < c_end) {
     const int e = c_begin * kChunk + tid;
     if (e < a.k) idx_next = a.idx[(int64_t)r * a.k + e];
   }
-
-  // query operands (B of S^T = C Q^T): head h, dims dbase + 32s + 8g .. +8, prescaled
-  bf16x8_t qhi[8], qlo[8];
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 qraw[16];
   {
     const float* qp = a.q + ((int64_t)r * a.H + h) * 512 + dbase + 8 * g;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp + 32 * s);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(qp + 32 * s + 4);
+      qraw[2 * s] = *reinterpret_cast<const f32x4*>(qp + 32 * s);
+      qraw[2 * s + 1] = *reinterpret_cast<const f32x4*>(qp + 32 * s + 4);
+    }
+  }
+  // query operands (B of S^T = C Q^T): head h, dims dbase + 32s + 8g .. +8, prescaled
+  bf16x8_t qhi[8], qlo[8];
+  bool q_ready = false;
+  auto convert_query = [&]() {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = (e < 4 ? x0[e] : x1[e - 4]) * a.qscale;
+        const float v = qraw[2 * s + (e >> 2)][e & 3] * a.qscale;
         const __bf16 hi = (__bf16)v;
         qhi[s][e] = hi;
         qlo[s][e] = (__bf16)(v - (float)hi);
       }
     }
-  }
+    q_ready = true;
+  };
 
   f32x4 oacc[16];
 #pragma unroll
@@ -240,6 +251,8 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
     else
       decode_chunk<NP, kMixedRows>(a, sOff, sType, vmask, sK, sVt, tid);
     __syncthreads();
+
+    if (!q_ready) convert_query();
 
     // 3. partial S^T[64 entries x 16 heads] over this wave's 256 dims
     f32x4 sacc[4];
@@ -346,7 +359,10 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One workgroup per (row, head), one thread per output dim.
+// One workgroup per (row, head), one thread per output dim; the loads of up to
+// kCombineUnroll splits are issued together.
+constexpr int kCombineUnroll = 16;
+
 __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, int splits, int H,
                                                            float* __restrict__ out) {
@@ -354,16 +370,35 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restri
   const int h = blockIdx.x;
   const int d = threadIdx.x;
   const int64_t base = (int64_t)r * splits * H + h;     // slot of split s: base + s*H
-  float M = -__builtin_inff();
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[2 * (base + (int64_t)s * H)]);
-  float L = 0.f, acc = 0.f;
-  if (M != -__builtin_inff()) {
-    for (int s = 0; s < splits; ++s) {
-      const int64_t slot = base + (int64_t)s * H;
-      const float wgt = exp2f(part_ml[2 * slot] - M);
-      L += wgt * part_ml[2 * slot + 1];
-      acc += wgt * part_o[slot * 512 + d];
+  float M = -__builtin_inff(), L = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += kCombineUnroll) {
+    // one round of loads: every split's (m, l) and o[d]
+    float mv[kCombineUnroll], lv[kCombineUnroll], ov[kCombineUnroll];
+#pragma unroll
+    for (int j = 0; j < kCombineUnroll; ++j) {
+      const bool on = s0 + j < splits;
+      const int64_t slot = base + (int64_t)(on ? s0 + j : s0) * H;
+      mv[j] = on ? part_ml[2 * slot] : -__builtin_inff();
+      lv[j] = part_ml[2 * slot + 1];
+      ov[j] = part_o[slot * 512 + d];
     }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < kCombineUnroll; ++j) Mn = fmaxf(Mn, mv[j]);
+    if (Mn == -__builtin_inff()) continue;   // nothing seen yet
+    // rescale what came before, then add this group in split order
+    const float c = exp2f(M - Mn);
+    L *= c;
+    acc *= c;
+#pragma unroll
+    for (int j = 0; j < kCombineUnroll; ++j) {
+      if (s0 + j < splits) {
+        const float wgt = exp2f(mv[j] - Mn);
+        L += wgt * lv[j];
+        acc += wgt * ov[j];
+      }
+    }
+    M = Mn;
   }
   out[((int64_t)r * H + h) * 512 + d] = L > 0.f ? acc / L : 0.f;
 }
@@ -417,14 +452,17 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
     a.part_o = static_cast<float*>(L.workspace);
     a.part_ml = a.part_o + (size_t)R * a.splits * L.H * 512;
   }
-  dim3 grid((unsigned)a.splits, (unsigned)R);
-  const int NP = L.H / 16;
-  switch (NP) {
-    case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(128), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, dim3(512), 0, stream, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  // Workgroups of 32 heads (4 waves): each wave keeps the query and the output
+  // accumulator of 16 heads x 256 dims in registers, which fits the 512
+  // registers a wave has at one wave per SIMD; more heads split over blockIdx.z.
+  if (L.H % 16 != 0 || L.H < 16) return hipErrorInvalidValue;
+  const int NP = L.H >= 32 ? 2 : 1;
+  if (L.H % (16 * NP) != 0) return hipErrorInvalidValue;
+  dim3 grid((unsigned)a.splits, (unsigned)R, (unsigned)(L.H / (16 * NP)));
+  if (NP == 2)
+    hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(128), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.splits == 1) return err;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)L.H, (unsigned)R), dim3(512), 0, stream, a.part_o,
