@@ -28,9 +28,9 @@ HIPCC_FLAGS = [
 ]
 
 
-# per-source extra flags: the prefill scan keeps its MFMA results in VGPRs (the
-# code reads every result element once, right away)
-EXTRA_FLAGS = {"prefill_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source extra flags: the scans keep their MFMA results in VGPRs (the code
+# reads every result element once, right away)
+EXTRA_FLAGS = {"prefill_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

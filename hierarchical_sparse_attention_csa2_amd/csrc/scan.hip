@@ -8,13 +8,20 @@
 // summed exactly; block b contributes v_b = sum_b * 2^(eq_b + ek_b - 254); the
 // score is ((v0+v1)+v2)+v3 in fp32.
 //
-// Thread mapping: four lanes per cached position, lane 4p+b owns 32-element
-// block b, so one 16-byte load per lane reads one whole block and a wave's load
-// instruction covers 16 consecutive positions = 1 KiB of contiguous codes.  The
-// E2M1 codes are decoded in registers (v_cvt_scalef32_pk_f16_fp4, exact) and
-// multiplied with v_dot2 into an fp32 accumulator (exact, see block_dot); the
-// quad's four block values are combined in order with DPP broadcasts and the
-// block max of 8 positions (half a wave) is a DPP/permute reduction.
+// Full-layer scan (few queries per sequence): the block values come from the FP4
+// matrix cores.  One v_mfma_scale_f32_16x16x128_f8f6f4 scores 16 keys: the keys
+// are the B operand (lane 16g + c holds block g of key c with its E8M0 scale, so
+// one load instruction still reads 1 KiB of contiguous codes), and the A operand
+// is block-diagonal in the query: row i holds query block i % 4 in K group
+// i % 4 and zeros elsewhere.  Output row i of column c is then the single block
+// value v_{i%4} of key c, a sum of 32 exact products at one scale: exact while
+// the block exponent eq_b + ek_b - 254 lies in [-124, 114] (the integer sum
+// needs 13 bits and every value stays a normal float).  Each lane receives
+// v_0..v_3 of one key and adds them in order itself, so after four products
+// lane l holds the score of the wave's key l.  A wave whose keys have a block
+// exponent outside that range is scored on the vector ALUs instead (E2M1 codes
+// decoded with v_cvt_scalef32_pk_f16_fp4, v_dot2 into fp32, ldexp), giving the
+// same fixed-order result.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -22,10 +29,11 @@ namespace csa2 {
 
 constexpr int kScanThreads = 256;
 constexpr int kScanWaves = kScanThreads / 64;
-constexpr int kSupersPerWave = 2;                               // 64-position super-blocks per wave
-constexpr int kScanChunk = kScanWaves * kSupersPerWave * 64;    // positions per workgroup
-constexpr int kScanGroups = kSupersPerWave * 4;                  // 16-position groups per wave
-constexpr int kPrefillMinQueries = 16;                           // queries per sequence for the MFMA scan
+constexpr int kScanChunk = kScanWaves * 64;     // positions per workgroup (64 per wave)
+constexpr int kPrefillMinQueries = 16;          // queries per sequence for the many-query scan
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4_t load_codes16(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -36,78 +44,142 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
 }
 
-// Score of one 16-position group (lane 4p+b holds block b of position p) and
-// the maxima of its two 8-position blocks: on return lanes 16..31 hold block
-// A's (positions 0-7) maximum key and lanes 48..63 block B's (positions 8-15).
-__device__ __forceinline__ uint32_t group_score_max(const u32x4_t c, uint32_t e, const half2_t* qh, int eq, bool vis,
-                                                    float* s_out) {
-  const float v = __builtin_amdgcn_ldexpf(block_dot(c, qh), eq + (int)e - 254);
-  const float s = quad_ordered_sum(v);
-  *s_out = s;
-  uint32_t k = vis ? order_key(s) : 0u;
-  uint32_t y = dpp_u32<0x124, 0xF>(k);   // row_ror:4 -> max of two quads
-  k = y > k ? y : k;
-  y = dpp_u32<0x128, 0xF>(k);            // row_ror:8 -> max of the row (4 positions)
-  k = y > k ? y : k;
-  y = dpp_u32<0x142, 0xA>(k);            // row_bcast:15 -> rows 1, 3 take the row before
-  return y > k ? y : k;
+// max over the 8-lane group (lanes 8j..8j+7) of x, in every lane of the group
+__device__ __forceinline__ uint32_t group8_max_u32(uint32_t x) {
+  uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x = y > x ? y : x;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);            // quad_perm [2,3,0,1]
+  x = y > x ? y : x;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);           // row_half_mirror
+  return y > x ? y : x;
 }
 
-// Each wave scores kSupersPerWave consecutive 64-position super-blocks; all of
-// its loads are issued before any arithmetic.  Outputs: block maxima, optional
-// super-block maxima (8 blocks) and optional per-position scores.
+// Vector-ALU scoring of the wave's 64 positions p0..p0+63 (lane 4p+b holds
+// block b of position p of a 16-position group), writing the same outputs as
+// the matrix-core path.  Used for waves with a block exponent out of range.
 template <bool kScores, bool kSuper>
-__global__ __launch_bounds__(kScanThreads) void index_scan_kernel(
+__device__ __forceinline__ void scan_wave_valu(const uint8_t* qr, const uint8_t* qs, const uint8_t* kc,
+                                            const uint8_t* ks, int64_t p0, int64_t nv, int64_t N_max, int r,
+                                            int64_t nblk_stride, int64_t nsup_stride, float* scores,
+                                            float* block_max, float* super_max) {
+  const int lane = threadIdx.x & 63;
+  const int b = lane & 3;
+  const int pl = lane >> 2;
+  half2_t qh[16];
+  load_query_block(qr + 16 * b, qh);
+  const int eq = qs[b];
+  uint32_t smax = 0u;
+  for (int u = 0; u < 4; ++u) {
+    const int64_t gp = p0 + 16 * u;
+    int64_t p = gp + pl;
+    const bool vis = p < nv;
+    p = vis ? p : nv - 1;
+    const u32x4_t c = load_codes16(kc + p * 64 + 16 * b);
+    const uint32_t e = ks[p * 4 + b];
+    const float v = __builtin_amdgcn_ldexpf(block_dot(c, qh), eq + (int)e - 254);
+    const float s = quad_ordered_sum(v);
+    if (kScores && b == 0 && vis) scores[(int64_t)r * N_max + p] = s;
+    // max over the 8 positions of each half of the group: lanes 0..31 and 32..63
+    uint32_t kk = vis ? order_key(s) : 0u;
+    uint32_t y = dpp_u32<0x124, 0xF>(kk);   // row_ror:4 -> max of two quads
+    kk = y > kk ? y : kk;
+    y = dpp_u32<0x128, 0xF>(kk);            // row_ror:8 -> max of the row (4 positions)
+    kk = y > kk ? y : kk;
+    y = dpp_u32<0x142, 0xA>(kk);            // row_bcast:15 -> rows 1, 3 take the row before
+    kk = y > kk ? y : kk;
+    smax = kk > smax ? kk : smax;
+    if (lane == 16 && gp < nv) block_max[(int64_t)r * nblk_stride + (gp >> 3)] = key_to_float(kk);
+    if (lane == 48 && gp + 8 < nv) block_max[(int64_t)r * nblk_stride + (gp >> 3) + 1] = key_to_float(kk);
+  }
+  if (kSuper) {
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)smax, 16);
+    const uint32_t bb = (uint32_t)__builtin_amdgcn_readlane((int)smax, 48);
+    if (lane == 0) super_max[(int64_t)r * nsup_stride + (p0 >> 6)] = key_to_float(a > bb ? a : bb);
+  }
+}
+
+// Grid (ceil(N_max / 256), M, B): query row r = seq * M + blockIdx.y.  Each wave
+// scores 64 consecutive positions; all of its loads are issued before any
+// arithmetic.  Outputs: block maxima, optional super-block maxima (8 blocks) and
+// optional per-position scores.
+template <bool kScores, bool kSuper>
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void index_scan_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     const int32_t* __restrict__ n_visible, int M, int64_t N_max, int64_t nblk_stride, int64_t nsup_stride,
     float* __restrict__ scores, float* __restrict__ block_max, float* __restrict__ super_max) {
-  const int r = blockIdx.y;
-  const int64_t seq = r / M;
+  const int64_t seq = blockIdx.z;
+  const int r = (int)seq * M + (int)blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int b = lane & 3;
-  const int pl = lane >> 2;
+  const int c = lane & 15;   // key within a 16-position group (B column)
+  const int g = lane >> 4;   // block held by this lane (B K group)
   int64_t nv = n_visible[r];
   nv = nv < 0 ? 0 : (nv > N_max ? N_max : nv);
-  const int64_t p0 = (int64_t)blockIdx.x * kScanChunk + (int64_t)wave * (kSupersPerWave * 64);
+  const int64_t p0 = (int64_t)blockIdx.x * kScanChunk + (int64_t)wave * 64;
   if (p0 >= nv) return;   // no barriers below: waves leave independently
 
-  half2_t qh[16];
-  load_query_block(q_codes + (int64_t)r * 64 + 16 * b, qh);
-  const int eq = q_scales[(int64_t)r * 4 + b];
-  const uint8_t* kc = k_codes + seq * N_max * 64 + 16 * b;
-  const uint8_t* ks = k_scales + seq * N_max * 4 + b;
-
-  u32x4_t c[kScanGroups];
-  uint32_t e[kScanGroups];
+  const uint8_t* kc = k_codes + seq * N_max * 64;
+  const uint8_t* ks = k_scales + seq * N_max * 4;
+  u32x4_t kb[4];
+  uint32_t ek[4];
 #pragma unroll
-  for (int u = 0; u < kScanGroups; ++u) {
-    int64_t p = p0 + 16 * u + pl;
-    p = p < nv ? p : nv - 1;             // tail lanes re-read a visible row
-    c[u] = load_codes16(kc + p * 64);
-    e[u] = ks[p * 4];
+  for (int u = 0; u < 4; ++u) {
+    int64_t p = p0 + 16 * u + c;
+    p = p < nv ? p : nv - 1;   // tail lanes re-read a visible row
+    kb[u] = load_codes16(kc + p * 64 + 16 * g);
+    ek[u] = ks[p * 4 + g];
   }
+  // A operand: lane 16g + i (row i, K group g) holds query block g when i % 4 == g
+  const uint8_t* qr = q_codes + (int64_t)r * 64;
+  const int eq = q_scales[(int64_t)r * 4 + g];
+  u32x4_t qa = {0u, 0u, 0u, 0u};
+  if ((lane & 3) == g) qa = *reinterpret_cast<const u32x4_t*>(qr + 16 * g);
+
+  // every visible block exponent in [-124, 114]
+  bool bad = false;
 #pragma unroll
-  for (int h = 0; h < kSupersPerWave; ++h) {
-    uint32_t smax = 0u;
+  for (int u = 0; u < 4; ++u)
+    bad |= p0 + 16 * u + c < nv && (uint32_t)(eq + (int)ek[u] - 130) > 244u;
+  if (__ballot(bad) != 0ull) {
+    scan_wave_valu<kScores, kSuper>(qr, q_scales + (int64_t)r * 4, kc, ks, p0, nv, N_max, r, nblk_stride,
+                                    nsup_stride, scores, block_max, super_max);
+    return;
+  }
+
+  const i32x8_t a8 = {(int)qa[0], (int)qa[1], (int)qa[2], (int)qa[3], 0, 0, 0, 0};
+  f32x4_t acc[4];
 #pragma unroll
-    for (int u = 4 * h; u < 4 * h + 4; ++u) {
-      const int64_t gp = p0 + 16 * u;
-      const int64_t p = gp + pl;
-      float s;
-      const uint32_t k = group_score_max(c[u], e[u], qh, eq, p < nv, &s);
-      if (kScores && b == 0 && p < nv) scores[(int64_t)r * N_max + p] = s;
-      smax = k > smax ? k : smax;
-      if (lane == 16 && gp < nv) block_max[(int64_t)r * nblk_stride + (gp >> 3)] = key_to_float(k);
-      if (lane == 48 && gp + 8 < nv) block_max[(int64_t)r * nblk_stride + (gp >> 3) + 1] = key_to_float(k);
-    }
-    if (kSuper) {
-      const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)smax, 16);
-      const uint32_t bb = (uint32_t)__builtin_amdgcn_readlane((int)smax, 48);
-      const int64_t sp = p0 + 64 * h;
-      if (lane == 0 && sp < nv) super_max[(int64_t)r * nsup_stride + (sp >> 6)] = key_to_float(a > bb ? a : bb);
-    }
+  for (int u = 0; u < 4; ++u) {
+    const i32x8_t b8 = {(int)kb[u][0], (int)kb[u][1], (int)kb[u][2], (int)kb[u][3], 0, 0, 0, 0};
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, zero, 4, 4, 0, eq, 0, (int)ek[u]);
+    // keep the product here, with every lane active: the matrix core reads its
+    // operands from all 64 lanes, so it must not be moved into the branch below
+    // that only the visible lanes take
+    asm volatile("" : "+v"(acc[u]));
+  }
+  // lane 16g + c: column c, rows 4g..4g+3, element i = row 4g + i = v_i of key
+  // 16u + c.  Lane l takes group u = l / 16, i.e. key l of the wave.
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = (g & 1) ? acc[1][i] : acc[0][i];
+    const float hi = (g & 1) ? acc[3][i] : acc[2][i];
+    v[i] = (g & 2) ? hi : lo;
+  }
+  float s = v[0] + v[1];
+  s = s + v[2];
+  s = s + v[3];
+  s = s + 0.0f;   // an exact zero sum is +0
+  const int64_t key = p0 + lane;
+  const bool vis = key < nv;
+  if (kScores && vis) scores[(int64_t)r * N_max + key] = s;
+  const uint32_t m8 = group8_max_u32(vis ? order_key(s) : 0u);
+  if ((lane & 7) == 0 && vis) block_max[(int64_t)r * nblk_stride + (key >> 3)] = key_to_float(m8);
+  if (kSuper) {
+    const uint32_t m = wave_max_u32(m8);
+    if (lane == 0) super_max[(int64_t)r * nsup_stride + (p0 >> 6)] = key_to_float(m);
   }
 }
 
@@ -170,9 +242,9 @@ hipError_t launch_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, co
   if (M >= kPrefillMinQueries)
     return launch_prefill_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, scores, block_max,
                                nblk_stride, super_max, nsup_stride, stream);
-  const int R = B * M;
-  dim3 grid((unsigned)((N_max + kScanChunk - 1) / kScanChunk), (unsigned)R);
-#define CSA2_SCAN(S, P)                                                                                         \
+  if (M > 65535 || B > 65535) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)((N_max + kScanChunk - 1) / kScanChunk), (unsigned)M, (unsigned)B);
+#define CSA2_SCAN(S, P)                                                                                        \
   hipLaunchKernelGGL((index_scan_kernel<S, P>), grid, dim3(kScanThreads), 0, stream, q_codes, q_scales, k_codes, \
                      k_scales, n_visible, M, N_max, nblk_stride, nsup_stride, scores, block_max, super_max)
   if (scores && super_max) CSA2_SCAN(true, true);

@@ -27,6 +27,10 @@ def host_inputs(w: Workload, layers=1, kind="normal", seed_offset=0):
           "ties"    - a 4-code key alphabet and 2-code queries (scores tie a lot)
           "spread"  - N(0,1) codes with scale bytes spread over [60, 200]
                       (block exponents far apart: fp32 rounding in the score)
+          "mixed"   - the workload's own distribution, with 2% of the cached
+                      positions given four scale bytes 126 + U[-7, 7] (key
+                      tiles whose block exponents span 0..14 next to ordinary
+                      ones, so the matrix-core and vector paths meet in a row)
     """
     cache = synth.gen_cache(w)
     lays = [synth.gen_layer(w, layer=L) for L in range(layers)]
@@ -41,6 +45,10 @@ def host_inputs(w: Workload, layers=1, kind="normal", seed_offset=0):
         cache["k_scales"] = rng.integers(60, 201, size=cache["k_scales"].shape).astype(np.uint8)
         for d in lays:
             d["q_scales"] = rng.integers(60, 201, size=d["q_scales"].shape).astype(np.uint8)
+    elif kind == "mixed":
+        ks = cache["k_scales"]
+        hit = rng.random(ks.shape[:-1]) < 0.02
+        ks[hit] = (126 + rng.integers(-7, 8, size=(int(hit.sum()), ks.shape[-1]))).astype(np.uint8)
     elif kind != "normal":
         raise ValueError(kind)
     return cache, lays

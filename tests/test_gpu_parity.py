@@ -45,7 +45,7 @@ def _run_scan(w, c, l, want_super=False):
     return scores.cpu().numpy(), bmax.cpu().numpy()
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "spread"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed"])
 @pytest.mark.parametrize("N,nv", [(3000, [3000, 2995, 1]), (4099, [4099, 2048, 2049]), (40, [0, 40, 17])])
 def test_index_scan_bitexact(kind, N, nv):
     w = Workload("scan", 1234 + N, B=3, N=N)
@@ -73,7 +73,7 @@ def _same_f32(a, b):
     return bool(np.all(both_nan | (f32_bits(a) == f32_bits(b))))
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "spread"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed"])
 @pytest.mark.parametrize("B,M,N", [(1, 40, 3000), (2, 33, 2100), (1, 130, 5000)])
 def test_prefill_scan_bitexact(kind, B, M, N):
     """Many queries per sequence (the matrix-core scan): scores, block maxima and
@@ -98,7 +98,7 @@ def test_prefill_scan_bitexact(kind, B, M, N):
         assert _same_f32(smax[r, :ns], np.array(want, np.float32)), r
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "spread"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed"])
 @pytest.mark.parametrize("N,n_pool,k,nv", [
     (4096, 2048, 512, [4096, 4000, 3333]),      # pool covers all blocks
     (20000, 2048, 512, [20000, 19999, 8191]),   # pool smaller than the block count
@@ -161,7 +161,7 @@ def test_select_blocks_and_topk_full_layout():
         assert np.array_equal(idx.cpu().numpy(), want), k
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "spread"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed"])
 def test_reindex_pool_scores_and_topk(kind):
     """A Reindex layer: its own index query scored only inside the Full pool."""
     w = Workload("reidx", 777, B=3, N=50000, n_pool=2048, k=512)
