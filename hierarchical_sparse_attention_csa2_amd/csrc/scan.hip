@@ -54,48 +54,61 @@ __device__ __forceinline__ uint32_t group8_max_u32(uint32_t x) {
   return y > x ? y : x;
 }
 
-// Vector-ALU scoring of the wave's 64 positions p0..p0+63 (lane 4p+b holds
-// block b of position p of a 16-position group), writing the same outputs as
-// the matrix-core path.  Used for waves with a block exponent out of range.
-template <bool kScores, bool kSuper>
-__device__ __forceinline__ void scan_wave_valu(const uint8_t* qr, const uint8_t* qs, const uint8_t* kc,
-                                            const uint8_t* ks, int64_t p0, int64_t nv, int64_t N_max, int r,
-                                            int64_t nblk_stride, int64_t nsup_stride, float* scores,
-                                            float* block_max, float* super_max) {
-  const int lane = threadIdx.x & 63;
-  const int b = lane & 3;
-  const int pl = lane >> 2;
-  half2_t qh[16];
-  load_query_block(qr + 16 * b, qh);
-  const int eq = qs[b];
-  uint32_t smax = 0u;
+// Score of one key on the vector ALUs, for any scale bytes: each block's exact
+// sum (E2M1 codes decoded to f16 with v_cvt_scalef32_pk_f16_fp4, v_dot2 into
+// fp32) scaled with ldexp, then ((v0+v1)+v2)+v3 in fp32.
+__device__ __forceinline__ float score_key_valu(const uint8_t* qr, const uint8_t* qs, const uint8_t* kr,
+                                                const uint8_t* ksr) {
+  float s = 0.0f;
+#pragma unroll 1
+  for (int b = 0; b < 4; ++b) {
+    half2_t qh[16];
+    load_query_block(qr + 16 * b, qh);
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(kr + 16 * b);
+    const float v = __builtin_amdgcn_ldexpf(block_dot(c, qh), (int)qs[b] + (int)ksr[b] - 254);
+    s = b == 0 ? v : s + v;
+  }
+  return s;
+}
+
+// The four block values of 16 keys on the matrix cores.  kb[u], ek[u]: lane
+// 16g + c holds block g of key c of group u (codes, scale byte); qa, eq: the
+// block-diagonal query operand (lane 16g + i holds query block g when
+// i % 4 == g) and this lane's query scale byte (block g).  Returns the score of
+// key c of group g, the wave's key 16g + c, in lane 16g + c.
+__device__ __forceinline__ float score_groups_mfma(const u32x4_t qa, int eq, const u32x4_t* kb, const uint32_t* ek) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const i32x8_t a8 = {(int)qa[0], (int)qa[1], (int)qa[2], (int)qa[3], 0, 0, 0, 0};
+  f32x4_t acc[4];
+#pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int64_t gp = p0 + 16 * u;
-    int64_t p = gp + pl;
-    const bool vis = p < nv;
-    p = vis ? p : nv - 1;
-    const u32x4_t c = load_codes16(kc + p * 64 + 16 * b);
-    const uint32_t e = ks[p * 4 + b];
-    const float v = __builtin_amdgcn_ldexpf(block_dot(c, qh), eq + (int)e - 254);
-    const float s = quad_ordered_sum(v);
-    if (kScores && b == 0 && vis) scores[(int64_t)r * N_max + p] = s;
-    // max over the 8 positions of each half of the group: lanes 0..31 and 32..63
-    uint32_t kk = vis ? order_key(s) : 0u;
-    uint32_t y = dpp_u32<0x124, 0xF>(kk);   // row_ror:4 -> max of two quads
-    kk = y > kk ? y : kk;
-    y = dpp_u32<0x128, 0xF>(kk);            // row_ror:8 -> max of the row (4 positions)
-    kk = y > kk ? y : kk;
-    y = dpp_u32<0x142, 0xA>(kk);            // row_bcast:15 -> rows 1, 3 take the row before
-    kk = y > kk ? y : kk;
-    smax = kk > smax ? kk : smax;
-    if (lane == 16 && gp < nv) block_max[(int64_t)r * nblk_stride + (gp >> 3)] = key_to_float(kk);
-    if (lane == 48 && gp + 8 < nv) block_max[(int64_t)r * nblk_stride + (gp >> 3) + 1] = key_to_float(kk);
+    const i32x8_t b8 = {(int)kb[u][0], (int)kb[u][1], (int)kb[u][2], (int)kb[u][3], 0, 0, 0, 0};
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, zero, 4, 4, 0, eq, 0, (int)ek[u]);
+    // keep the product here, with every lane active: the matrix core reads its
+    // operands from all 64 lanes, so it must not be moved into a branch that
+    // only some lanes take
+    asm volatile("" : "+v"(acc[u]));
   }
-  if (kSuper) {
-    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)smax, 16);
-    const uint32_t bb = (uint32_t)__builtin_amdgcn_readlane((int)smax, 48);
-    if (lane == 0) super_max[(int64_t)r * nsup_stride + (p0 >> 6)] = key_to_float(a > bb ? a : bb);
+  // lane 16g + c: column c, rows 4g..4g+3; element i = row 4g + i = v_i of
+  // key c of group u.  Take group u = g.
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = (g & 1) ? acc[1][i] : acc[0][i];
+    const float hi = (g & 1) ? acc[3][i] : acc[2][i];
+    v[i] = (g & 2) ? hi : lo;
   }
+  float s = v[0] + v[1];
+  s = s + v[2];
+  s = s + v[3];
+  return s + 0.0f;   // an exact zero sum is +0
+}
+
+// block exponent eq + ek - 254 outside [-124, 114]: the matrix-core value may
+// be inexact
+__device__ __forceinline__ bool exponent_out_of_range(int eq, uint32_t ek) {
+  return (uint32_t)(eq + (int)ek - 130) > 244u;
 }
 
 // Grid (ceil(N_max / 256), M, B): query row r = seq * M + blockIdx.y.  Each wave
@@ -139,39 +152,15 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8,
   // every visible block exponent in [-124, 114]
   bool bad = false;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    bad |= p0 + 16 * u + c < nv && (uint32_t)(eq + (int)ek[u] - 130) > 244u;
-  if (__ballot(bad) != 0ull) {
-    scan_wave_valu<kScores, kSuper>(qr, q_scales + (int64_t)r * 4, kc, ks, p0, nv, N_max, r, nblk_stride,
-                                    nsup_stride, scores, block_max, super_max);
-    return;
+  for (int u = 0; u < 4; ++u) bad |= p0 + 16 * u + c < nv && exponent_out_of_range(eq, ek[u]);
+  float s;
+  if (__ballot(bad) == 0ull) {
+    s = score_groups_mfma(qa, eq, kb, ek);
+  } else {
+    int64_t p = p0 + lane;
+    p = p < nv ? p : nv - 1;
+    s = score_key_valu(qr, q_scales + (int64_t)r * 4, kc + p * 64, ks + p * 4);
   }
-
-  const i32x8_t a8 = {(int)qa[0], (int)qa[1], (int)qa[2], (int)qa[3], 0, 0, 0, 0};
-  f32x4_t acc[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const i32x8_t b8 = {(int)kb[u][0], (int)kb[u][1], (int)kb[u][2], (int)kb[u][3], 0, 0, 0, 0};
-    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-    acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, zero, 4, 4, 0, eq, 0, (int)ek[u]);
-    // keep the product here, with every lane active: the matrix core reads its
-    // operands from all 64 lanes, so it must not be moved into the branch below
-    // that only the visible lanes take
-    asm volatile("" : "+v"(acc[u]));
-  }
-  // lane 16g + c: column c, rows 4g..4g+3, element i = row 4g + i = v_i of key
-  // 16u + c.  Lane l takes group u = l / 16, i.e. key l of the wave.
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = (g & 1) ? acc[1][i] : acc[0][i];
-    const float hi = (g & 1) ? acc[3][i] : acc[2][i];
-    v[i] = (g & 2) ? hi : lo;
-  }
-  float s = v[0] + v[1];
-  s = s + v[2];
-  s = s + v[3];
-  s = s + 0.0f;   // an exact zero sum is +0
   const int64_t key = p0 + lane;
   const bool vis = key < nv;
   if (kScores && vis) scores[(int64_t)r * N_max + key] = s;
@@ -183,55 +172,71 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8,
   }
 }
 
-// Pool scan: each half wave scores one pool block (8 positions x 4 blocks).
-constexpr int kPoolBlocksPerWG = 64;
+// Pool scan: one wave scores 8 pool blocks (64 positions) on the matrix cores,
+// with the operand layout of the Full-layer scan (group u = pool blocks 2u and
+// 2u + 1; lane 16g + c holds block g of position c & 7 of pool block
+// 2u + (c >> 3)); lane l's result is slot l of the wave's 64 output slots.
+// Grid (ceil(n_pool / 8), M, B), one wave per workgroup.
+constexpr int kPoolWaveBlocks = 8;
 
-__global__ __launch_bounds__(kScanThreads) void pool_scan_kernel(
+__global__ __launch_bounds__(64) void pool_scan_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     const int32_t* __restrict__ pool_blocks, int n_pool, const int32_t* __restrict__ n_visible, int M,
     int64_t N_max, float* __restrict__ pool_scores) {
-  const int r = blockIdx.y;
-  const int64_t seq = r / M;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int b = lane & 3;
-  const int t = (lane >> 2) & 7;
-  const int half = lane >> 5;
+  const int64_t seq = blockIdx.z;
+  const int r = (int)seq * M + (int)blockIdx.y;
+  const int lane = threadIdx.x;
+  const int c = lane & 15, g = lane >> 4;
   int64_t nv = n_visible[r];
   nv = nv < 0 ? 0 : (nv > N_max ? N_max : nv);
-
-  half2_t qh[16];
-  load_query_block(q_codes + (int64_t)r * 64 + 16 * b, qh);
-  const int eq = q_scales[(int64_t)r * 4 + b];
-  const uint8_t* kc = k_codes + seq * N_max * 64 + 16 * b;
-  const uint8_t* ks = k_scales + seq * N_max * 4 + b;
+  const int base = (int)blockIdx.x * kPoolWaveBlocks;
   const int32_t* pb = pool_blocks + (int64_t)r * n_pool;
+  // pool block of group u for this lane's column: base + 2u + (c >> 3); loads at
+  // clamped indices, all issued together; ids past the pool are -1
+  int32_t blk[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = base + 2 * u + (c >> 3);
+    const int32_t v = pb[i < n_pool ? i : n_pool - 1];
+    blk[u] = i < n_pool ? v : -1;
+  }
 
-  const int i_begin = blockIdx.x * kPoolBlocksPerWG;
-  const int i_end = min(i_begin + kPoolBlocksPerWG, n_pool);
-  // wave-groups of two pool blocks; wave w takes pairs w, w+4, ...
-  constexpr int kPairs = kPoolBlocksPerWG / 2 / 4;
-  u32x4_t c[kPairs];
-  uint32_t e[kPairs];
-  bool valid[kPairs];
+  const uint8_t* kc = k_codes + seq * N_max * 64;
+  const uint8_t* ks = k_scales + seq * N_max * 4;
+  u32x4_t kb[4];
+  uint32_t ek[4];
+  bool ok[4];
 #pragma unroll
-  for (int u = 0; u < kPairs; ++u) {
-    const int i = i_begin + 2 * (wave + 4 * u) + half;
-    int64_t blk = (i < i_end) ? pb[i] : -1;
-    int64_t p = 8 * blk + t;
-    valid[u] = (blk >= 0) && (p < nv);
-    p = valid[u] ? p : 0;
-    c[u] = load_codes16(kc + p * 64);
-    e[u] = ks[p * 4];
+  for (int u = 0; u < 4; ++u) {
+    const int32_t b = blk[u];
+    int64_t p = 8 * (int64_t)b + (c & 7);
+    ok[u] = b >= 0 && p < nv;
+    p = ok[u] ? p : 0;   // masked lanes read position 0 (in bounds)
+    kb[u] = load_codes16(kc + p * 64 + 16 * g);
+    ek[u] = ks[p * 4 + g];
   }
+  const uint8_t* qr = q_codes + (int64_t)r * 64;
+  const int eq = q_scales[(int64_t)r * 4 + g];
+  u32x4_t qa = {0u, 0u, 0u, 0u};
+  if ((lane & 3) == g) qa = *reinterpret_cast<const u32x4_t*>(qr + 16 * g);
+
+  bool bad = false;
 #pragma unroll
-  for (int u = 0; u < kPairs; ++u) {
-    const int i = i_begin + 2 * (wave + 4 * u) + half;
-    const float v = __builtin_amdgcn_ldexpf(block_dot(c[u], qh), eq + (int)e[u] - 254);
-    const float s = quad_ordered_sum(v);
-    if (b == 0 && i < i_end) pool_scores[((int64_t)r * n_pool + i) * 8 + t] = valid[u] ? s : -__builtin_inff();
+  for (int u = 0; u < 4; ++u) bad |= ok[u] && exponent_out_of_range(eq, ek[u]);
+  // this lane's output slot: group g, column c
+  const bool mine_ok = (g & 2) ? ((g & 1) ? ok[3] : ok[2]) : ((g & 1) ? ok[1] : ok[0]);
+  float s;
+  if (__ballot(bad) == 0ull) {
+    s = score_groups_mfma(qa, eq, kb, ek);
+  } else {
+    const int32_t b = (g & 2) ? ((g & 1) ? blk[3] : blk[2]) : ((g & 1) ? blk[1] : blk[0]);
+    int64_t p = 8 * (int64_t)b + (c & 7);
+    p = mine_ok ? p : 0;
+    s = score_key_valu(qr, q_scales + (int64_t)r * 4, kc + p * 64, ks + p * 4);
   }
+  if (base + 2 * g + (c >> 3) < n_pool)
+    pool_scores[((int64_t)r * n_pool + base) * 8 + lane] = mine_ok ? s : -__builtin_inff();
 }
 
 hipError_t launch_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
@@ -259,9 +264,9 @@ hipError_t launch_pool_scan(const uint8_t* q_codes, const uint8_t* q_scales, con
                             const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool,
                             const int32_t* n_visible, int B, int M, int64_t N_max, float* pool_scores,
                             hipStream_t stream) {
-  const int R = B * M;
-  dim3 grid((unsigned)((n_pool + kPoolBlocksPerWG - 1) / kPoolBlocksPerWG), (unsigned)R);
-  hipLaunchKernelGGL(pool_scan_kernel, grid, dim3(kScanThreads), 0, stream, q_codes, q_scales, k_codes, k_scales,
+  if (M > 65535 || B > 65535) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)((n_pool + kPoolWaveBlocks - 1) / kPoolWaveBlocks), (unsigned)M, (unsigned)B);
+  hipLaunchKernelGGL(pool_scan_kernel, grid, dim3(64), 0, stream, q_codes, q_scales, k_codes, k_scales,
                      pool_blocks, n_pool, n_visible, M, N_max, pool_scores);
   return hipGetLastError();
 }

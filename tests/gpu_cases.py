@@ -28,9 +28,11 @@ def host_inputs(w: Workload, layers=1, kind="normal", seed_offset=0):
           "spread"  - N(0,1) codes with scale bytes spread over [60, 200]
                       (block exponents far apart: fp32 rounding in the score)
           "mixed"   - the workload's own distribution, with 2% of the cached
-                      positions given four scale bytes 126 + U[-7, 7] (key
-                      tiles whose block exponents span 0..14 next to ordinary
-                      ones, so the matrix-core and vector paths meet in a row)
+                      positions given four scale bytes 126 + U[-7, 7] (block
+                      exponents spanning 0..14) and 0.3% given one scale byte
+                      in {1..4, 250..253} (block exponents outside the range
+                      where a matrix-core block sum is exact), so the
+                      matrix-core and vector paths meet in one row
     """
     cache = synth.gen_cache(w)
     lays = [synth.gen_layer(w, layer=L) for L in range(layers)]
@@ -49,6 +51,10 @@ def host_inputs(w: Workload, layers=1, kind="normal", seed_offset=0):
         ks = cache["k_scales"]
         hit = rng.random(ks.shape[:-1]) < 0.02
         ks[hit] = (126 + rng.integers(-7, 8, size=(int(hit.sum()), ks.shape[-1]))).astype(np.uint8)
+        ext = np.argwhere(rng.random(ks.shape[:-1]) < 0.003)
+        extreme = np.array([1, 2, 3, 4, 250, 251, 252, 253], np.uint8)
+        for pos in ext:
+            ks[tuple(pos) + (int(rng.integers(0, ks.shape[-1])),)] = extreme[int(rng.integers(0, len(extreme)))]
     elif kind != "normal":
         raise ValueError(kind)
     return cache, lays
