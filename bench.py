@@ -126,6 +126,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 512 MiB of index keys in rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--staged", action="store_true",
+                    help="run the Full indexer as its separate entry points instead of csa2_index_full")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -162,7 +164,8 @@ def main():
     key_bytes = w.B * w.N * INDEX_KEY_BYTES
     n_rep = args.replicas or max(1, math.ceil((512 << 20) / key_bytes))
     reps = replicate(cache, layers, n_rep, torch)
-    st = pipeline.Step(w.layers, w.B, w.M, w.N, H=w.H, n_pool=w.n_pool, k=w.k, win_max=w.win_len)
+    st = pipeline.Step(w.layers, w.B, w.M, w.N, H=w.H, n_pool=w.n_pool, k=w.k, win_max=w.win_len,
+                       staged=args.staged)
     scan_bytes = INDEX_KEY_BYTES * int(np.sum(lays_np[0]["n_visible"].astype(np.int64)))
     log(f"workload {w.name}: {w.notes}; {n_rep} replica(s); scan bytes/launch {scan_bytes / 1e6:.1f} MB")
 

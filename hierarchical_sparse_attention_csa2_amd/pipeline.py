@@ -55,7 +55,7 @@ class Step:
     """A chain of layers ("full", "reindex", "reuse") over one cache."""
 
     def __init__(self, modes, B, M, N, H=64, n_pool=2048, k=512, win_max=128, device="cuda",
-                 staged=True, keep_scores=False):
+                 staged=False, keep_scores=False):
         if modes[0] != "full":
             raise ValueError("the chain starts with a Full layer")
         self.modes = tuple(modes)

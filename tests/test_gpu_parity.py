@@ -121,8 +121,8 @@ def test_index_full_bitexact(kind, N, n_pool, k, nv):
     torch.cuda.synchronize()
     assert np.array_equal(pool.cpu().numpy(), ref["pool_blocks"])
     assert np.array_equal(idx.cpu().numpy(), ref["idx"])
-    # staged calls (the bench's path)
-    st = pipeline.Step(("full",), w.B, 1, N, H=64, n_pool=n_pool, k=k)
+    # staged calls (scan, block select, pool scan, top-k as separate entry points)
+    st = pipeline.Step(("full",), w.B, 1, N, H=64, n_pool=n_pool, k=k, staged=True)
     st.full_index(pipeline.cache_from(c), pipeline.layer_from(l), st.idx[0])
     torch.cuda.synchronize()
     assert np.array_equal(st.pool.cpu().numpy(), ref["pool_blocks"])

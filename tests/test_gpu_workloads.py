@@ -1,5 +1,5 @@
 """GPU parity at the five workload sizes, in the launch configuration bench.py
-times (pipeline.Step, staged calls).  Pools and indices bit-exact, attention
+times (pipeline.Step: csa2_index_full, then csa2_sparse_attn).  Pools and indices bit-exact, attention
 within 1e-3 of the fp64 oracle, on all rows where the oracle is quick and on
 sampled rows otherwise."""
 import numpy as np
