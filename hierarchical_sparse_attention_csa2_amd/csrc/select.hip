@@ -472,7 +472,6 @@ __device__ __forceinline__ void select_targets(SelShared& sh, const RowView row,
 constexpr int kRankCap = 128;                      // threshold-bin members resolved by counting
 constexpr int kKeepCap = 3072;                     // super-blocks kept by level 1
 constexpr int kCompCap = 16384;                    // blocks surviving into level 2
-constexpr int kGatherIters = kKeepCap / 128;       // 8 lanes per super-block
 
 struct Core {
   uint32_t hist[kBins];
@@ -696,21 +695,31 @@ struct Thr {
 // within [kmin, kmax]).  The histogram must be zero on entry.  approx_cap > 0:
 // target 0 may instead keep every key of its threshold bin and above when that
 // is at most approx_cap keys.
+// First-digit shift of a key range: bins of 2^shift keys cover [kmin, kmax] in
+// at most 4096 bins.
+__device__ __forceinline__ int first_digit_shift(uint32_t kmin, uint32_t kmax) {
+  const uint32_t span = kmax - kmin;
+  const int bits = span ? 32 - __builtin_clz(span) : 0;
+  return bits > 12 ? bits - 12 : 0;
+}
+
+// prebuilt: the caller has already counted every key into hist[(key - kmin) >>
+// first_digit_shift(kmin, kmax)] and synchronised.
 template <int J>
 __device__ __forceinline__ void select_thresholds(Core& c, Small& s, const uint32_t (&k)[J], int Jp, int valid,
                                                   uint32_t kmin, uint32_t kmax, int K0, int K1, int approx_cap,
-                                                  Thr& th0, Thr& th1) {
+                                                  Thr& th0, Thr& th1, bool prebuilt = false) {
   const int keff0 = K0 > 0 ? (K0 < valid ? K0 : valid) : 0;
   const int keff1 = K1 > 0 ? (K1 < valid ? K1 : valid) : 0;
   th0 = Thr{1u, 0x7FFFFFFF, keff0, K0, keff0 > 0};
   th1 = Thr{1u, 0x7FFFFFFF, keff1, K1, keff1 > 0};
   bool act0 = keff0 > 0 && keff0 < valid, act1 = keff1 > 0 && keff1 < valid;
   if (!act0 && !act1) return;
-  const uint32_t span = kmax - kmin;
-  const int bits = span ? 32 - __builtin_clz(span) : 0;
-  const int s1 = bits > 12 ? bits - 12 : 0;
-  hist_add(c, k, Jp, kmin, s1, 12, 32, 0u);
-  __syncthreads();
+  const int s1 = first_digit_shift(kmin, kmax);
+  if (!prebuilt) {
+    hist_add(c, k, Jp, kmin, s1, 12, 32, 0u);
+    __syncthreads();
+  }
   BinHit h0, h1;
   find_bins(c, s, act0 ? keff0 : 0, act1 ? keff1 : 0, h0, h1);
   int cur0 = s1, cur1 = s1;
@@ -892,61 +901,95 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
 // Level 1 ranks super-blocks (8 consecutive blocks) by their maximum and keeps
 // those at or above the threshold bin of the K-th (or exactly the first K);
 // every block of the first K blocks lies in them and scores at least that
-// threshold T1.  Level 2 gathers the blocks >= T1 of the kept super-blocks in
-// id order and selects exactly among them.
-struct Blocks2Shared {
-  int32_t cids[kCompCap];       // survivor -> slot q*1024 + tid of the gather
-  union {
-    uint32_t ckeys[kCompCap];
-    Core c;
-  } u;
-  int32_t sbsel[kKeepCap];
-  int gcnt[kGatherIters][kSelWaves];
+// threshold T1.  Level 2 selects exactly among the blocks >= T1 of the kept
+// super-blocks.
+//
+// Thread t owns super-blocks 8t..8t+7 at level 1; the kept super-blocks are
+// listed in id order with one workgroup prefix sum, and thread t then gathers a
+// contiguous run of at most three of them.  Its blocks >= T1 (the survivors)
+// are written to LDS in id order at positions from a second prefix sum, and
+// counted into level 2's histogram on the way.
+constexpr int kB3Items = 8;                        // super-blocks per thread at level 1
+constexpr int kB3Gather = kKeepCap / kSelThreads;  // kept super-blocks per thread (3)
+
+struct Blocks3Shared {
+  int32_t cids[kCompCap];       // survivors' block ids, id order
+  uint32_t ckeys[kCompCap];     // survivors' keys, id order
+  Core c;
+  int32_t sbsel[kKeepCap];      // kept super-blocks, id order
+  int wsum[4][kSelWaves];       // per-wave totals of the prefix sums
   Small s;
 };
 
-template <bool kHaveSuper>
-__global__ __launch_bounds__(kSelThreads) void select_blocks2_kernel(const float* __restrict__ bmax, int64_t stride,
+// Exclusive prefix sum of x over the workgroup in thread order, and the total.
+// buf: 16 ints that no other thread reads or writes between the barrier before
+// this call and the one inside it.
+__device__ __forceinline__ int block_excl_scan(int* buf, int x, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(x);
+  if (lane == 63) buf[w] = incl;
+  __syncthreads();
+  const int wt = lane < kSelWaves ? buf[lane] : 0;
+  const int wi = row_incl_scan(wt);
+  total = __builtin_amdgcn_readlane(wi, kSelWaves - 1);
+  return __builtin_amdgcn_readlane(wi, w) - __builtin_amdgcn_readlane(wt, w) + incl - x;
+}
+
+// kVec: super_max rows 16-byte aligned and block rows 32-byte aligned, so a
+// thread's 8 super maxima and a super-block's 8 block maxima are two 16-byte
+// loads each.
+template <bool kHaveSuper, bool kVec>
+__global__ __launch_bounds__(kSelThreads) void select_blocks3_kernel(const float* __restrict__ bmax, int64_t stride,
                                                                      const float* __restrict__ super_max,
                                                                      int64_t nsup_stride,
                                                                      const int32_t* __restrict__ n_visible, int K0,
                                                                      int32_t* __restrict__ out0, int K1,
                                                                      int32_t* __restrict__ out1) {
-  __shared__ Blocks2Shared sh;
+  __shared__ Blocks3Shared sh;
   const int r = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = threadIdx.x;
   const float* row = bmax + (int64_t)r * stride;
   const int nsup_cap = (int)((stride + 7) >> 3);   // <= 8192
-  const int Jp1 = (nsup_cap + 1023) >> 10;
-  int64_t nv = n_visible[r];
   int32_t* o0 = out0 ? out0 + (int64_t)r * K0 : nullptr;
   int32_t* o1 = out1 ? out1 + (int64_t)r * K1 : nullptr;
   if (!out0) K0 = 0;
   if (!out1) K1 = 0;
   const int kmaxK = K0 > K1 ? K0 : K1;
+  if (kmaxK == 0) return;
 
-  // level 1: super-block maxima, super-block i = item i (the scan's maxima are
-  // read ahead of n_visible)
-  float v1[8];
+  // level 1: super-blocks 8t..8t+7 (the scan's maxima are read ahead of n_visible)
+  float sv[kB3Items];
+  if constexpr (kHaveSuper && kVec) {
+    // in bounds: nsup_stride is a multiple of 4 and i < nsup_cap <= nsup_stride
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    v1[j] = 0.0f;
-    const int i = (w * Jp1 + j) * 64 + lane;
-    if (kHaveSuper && j < Jp1 && i < nsup_cap) v1[j] = super_max[(int64_t)r * nsup_stride + i];
+    for (int h = 0; h < 2; ++h) {
+      const int i = kB3Items * t + 4 * h;
+      const f32x4_t v = i < nsup_cap ? *reinterpret_cast<const f32x4_t*>(super_max + (int64_t)r * nsup_stride + i)
+                                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[4 * h + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kB3Items; ++j) {
+      const int i = kB3Items * t + j;
+      sv[j] = 0.0f;
+      if (kHaveSuper && i < nsup_cap) sv[j] = super_max[(int64_t)r * nsup_stride + i];
+    }
   }
+  int64_t nv = n_visible[r];
   nv = nv < 0 ? 0 : nv;
   const int nblk = (int)(((nv + 7) >> 3) < stride ? ((nv + 7) >> 3) : stride);
   const int nsuper = (nblk + 7) >> 3;
-  uint32_t k1[8];
+  uint32_t k1[kB3Items];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = (w * Jp1 + j) * 64 + lane;
+  for (int j = 0; j < kB3Items; ++j) {
+    const int i = kB3Items * t + j;
     uint32_t key = 0u;
-    if (j < Jp1 && i < nsuper) {
+    if (i < nsuper) {
       if constexpr (kHaveSuper) {
-        key = order_key(v1[j]);
+        key = order_key(sv[j]);
       } else {
-        // the maximum over the super-block's visible blocks
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int b = 8 * i + e;
@@ -957,104 +1000,133 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks2_kernel(const float
     }
     k1[j] = key;
   }
-  hist_zero(sh.u.c);
-  if (threadIdx.x == 0) {
+  hist_zero(sh.c);
+  if (t == 0) {
     sh.s.cnt[0] = 0;
     sh.s.cnt[1] = 0;
   }
   int valid1;
   uint32_t kmin1, kmax1;
-  key_range(sh.s, k1, Jp1, valid1, kmin1, kmax1);
+  key_range(sh.s, k1, kB3Items, valid1, kmin1, kmax1);
 
   int approx = kKeepCap;
-  int m2 = 0;
   uint32_t T1 = 1u;
+  int nkept = 0, m2 = 0, cpos = 0;
+  int sbq[kB3Gather];
+  uint32_t ck[kB3Gather * 8];   // survivors (>= T1) of this thread's run, 0 elsewhere
   for (;;) {
     Thr a0, a1;
-    select_thresholds(sh.u.c, sh.s, k1, Jp1, valid1, kmin1, kmax1, kmaxK, 0, approx, a0, a1);
-    emit_sel(
-        sh.s, k1, Jp1, a0, a1, [&](int t, int pos, int j, int i) { sh.sbsel[pos] = i; }, [&](int t, int p) {});
-    __syncthreads();
-    const int nkept = a0.keff;
+    select_thresholds(sh.c, sh.s, k1, kB3Items, valid1, kmin1, kmax1, kmaxK, 0, approx, a0, a1);
     T1 = a0.T;
-    // gather: lane takes block (tid & 7) of kept super-block q*128 + tid/8
-    uint32_t g[kGatherIters];
+    // kept super-blocks: > T1, or == T1 within the first `take` ties (id order);
+    // at most kKeepCap of them
+    int tie_base = 0;
+    if (a0.take != 0x7FFFFFFF) {
+      int nt = 0;
 #pragma unroll
-    for (int q = 0; q < kGatherIters; ++q) {
-      g[q] = 0u;
-      const int u = q * 128 + ((int)threadIdx.x >> 3);
-      if (u < nkept) {
-        const uint32_t blk = 8u * (uint32_t)sh.sbsel[u] + (threadIdx.x & 7u);
-        if (blk < (uint32_t)nblk) {
-          const uint32_t key = order_key(row[blk]);
-          g[q] = key >= T1 ? key : 0u;
+      for (int j = 0; j < kB3Items; ++j) nt += (k1[j] != 0u && k1[j] == T1) ? 1 : 0;
+      int unused;
+      tie_base = block_excl_scan(sh.wsum[0], nt, unused);
+    }
+    int nk = 0;
+    unsigned keep = 0u;
+#pragma unroll
+    for (int j = 0; j < kB3Items; ++j) {
+      bool kp = k1[j] != 0u && k1[j] >= T1;
+      if (a0.take != 0x7FFFFFFF && k1[j] == T1) {
+        kp = tie_base < a0.take;
+        ++tie_base;
+      }
+      keep |= kp ? (1u << j) : 0u;
+      nk += kp ? 1 : 0;
+    }
+    const int kbase = block_excl_scan(sh.wsum[1], nk, nkept);
+    {
+      int pos = kbase;
+#pragma unroll
+      for (int j = 0; j < kB3Items; ++j)
+        if ((keep >> j) & 1u) sh.sbsel[pos++] = kB3Items * t + j;
+    }
+    // level 1's histogram is no longer read: clear it for level 2
+    __syncthreads();
+    hist_zero(sh.c);
+    if (t == 0) {
+      sh.s.cnt[0] = 0;
+      sh.s.cnt[1] = 0;
+    }
+    // gather: thread t takes kept super-blocks [G t, G t + G), G = ceil(nkept / 1024)
+    const int G = (nkept + kSelThreads - 1) / kSelThreads;   // <= 3
+    float gv[kB3Gather * 8];
+#pragma unroll
+    for (int q = 0; q < kB3Gather; ++q) {
+      const int u = G * t + q;
+      const bool on = q < G && u < nkept;
+      sbq[q] = on ? sh.sbsel[u] : -1;
+      const int sb = on ? sbq[q] : 0;
+      if constexpr (kVec) {
+        // 8 sb + 7 < stride: stride is a multiple of 8 here
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x4_t v =
+              on ? *reinterpret_cast<const f32x4_t*>(row + 8 * sb + 4 * h) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gv[8 * q + 4 * h + e] = v[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int b = 8 * sb + e;
+          gv[8 * q + e] = (on && b < nblk) ? row[b] : 0.0f;
         }
       }
     }
-    // survivors per (q, wave); item order (q, wave, lane) is block id order
+    int nc = 0;
 #pragma unroll
-    for (int q = 0; q < kGatherIters; ++q) {
-      if (q * 128 < nkept) {
-        const int c = __popcll(__ballot(g[q] != 0u));
-        if (lane == 0) sh.gcnt[q][w] = c;
+    for (int q = 0; q < kB3Gather; ++q) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t key = (sbq[q] >= 0 && 8 * sbq[q] + e < nblk) ? order_key(gv[8 * q + e]) : 0u;
+        ck[8 * q + e] = key >= T1 ? key : 0u;
+        nc += ck[8 * q + e] != 0u ? 1 : 0;
       }
     }
-    __syncthreads();
-    const int nq = (nkept + 127) >> 7;
-    int qtot = 0, qpre = 0;
-    if (lane < nq) {
-#pragma unroll
-      for (int v = 0; v < kSelWaves; ++v) {
-        const int c = sh.gcnt[lane][v];
-        qpre += v < w ? c : 0;
-        qtot += c;
-      }
-    }
-    const int qincl = wave_incl_scan(qtot);
-    m2 = __builtin_amdgcn_readlane(qincl, 63);
+    cpos = block_excl_scan(sh.wsum[2], nc, m2);
     if (m2 > kCompCap && approx > 0) {
       // too many survivors for LDS: redo level 1 exactly (at most 8 * 2048)
       approx = 0;
-      hist_zero(sh.u.c);
-      __syncthreads();
-      continue;
-    }
-    const int qbase = qincl - qtot + qpre;   // lane q: first position of (q, this wave)
-#pragma unroll
-    for (int q = 0; q < kGatherIters; ++q) {
-      const unsigned long long m = q * 128 < nkept ? __ballot(g[q] != 0u) : 0ull;
-      if (m) {
-        const int pos = __builtin_amdgcn_readlane(qbase, q) + mbcnt(m);
-        if (g[q] != 0u && pos < kCompCap) {
-          sh.u.ckeys[pos] = g[q];
-          sh.cids[pos] = q * 1024 + (int)threadIdx.x;
-        }
-      }
+      continue;   // the histogram is clear and every thread is past the barrier above
     }
     break;
   }
+  // survivors to LDS in id order, counted into level 2's first-digit histogram
+  {
+    const int s2 = first_digit_shift(T1, kmax1);
+    int pos = cpos;
+#pragma unroll
+    for (int j = 0; j < kB3Gather * 8; ++j) {
+      if (ck[j] != 0u) {
+        sh.ckeys[pos] = ck[j];
+        sh.cids[pos] = 8 * sbq[j >> 3] + (j & 7);
+        atomicAdd(&sh.c.hist[((ck[j] - T1) >> s2) & (kBins - 1)], 1u);
+        ++pos;
+      }
+    }
+  }
   __syncthreads();
-  m2 = m2 < kCompCap ? m2 : kCompCap;   // (exact level 1 keeps at most 8 * 2048 blocks)
-  // level 2 over the m2 survivors (id order)
+  // level 2 over the m2 survivors (item order = id order), all within [T1, kmax1]
+  const int lane = t & 63, w = t >> 6;
   const int Jp2 = (m2 + 1023) >> 10;
   uint32_t k2[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int i = (w * Jp2 + j) * 64 + lane;
-    k2[j] = (j < Jp2 && i < m2) ? sh.u.ckeys[i] : 0u;
+    k2[j] = (j < Jp2 && i < m2) ? sh.ckeys[i] : 0u;
   }
-  __syncthreads();
-  hist_zero(sh.u.c);
-  __syncthreads();
   Thr th0, th1;
-  select_thresholds(sh.u.c, sh.s, k2, Jp2, m2, T1, kmax1, K0, K1, 0, th0, th1);
+  select_thresholds(sh.c, sh.s, k2, Jp2, m2, T1, kmax1, K0, K1, 0, th0, th1, true);
   emit_sel(
-      sh.s, k2, Jp2, th0, th1,
-      [&](int t, int pos, int j, int i) {
-        const int slot = sh.cids[i];
-        (t ? o1 : o0)[pos] = 8 * sh.sbsel[slot >> 3] + (slot & 7);
-      },
-      [&](int t, int p) { (t ? o1 : o0)[p] = -1; });
+      sh.s, k2, Jp2, th0, th1, [&](int tg, int pos, int j, int i) { (tg ? o1 : o0)[pos] = sh.cids[i]; },
+      [&](int tg, int p) { (tg ? o1 : o0)[p] = -1; });
 }
 
 // ---------------------------------------------------------------------------
@@ -1129,11 +1201,16 @@ hipError_t launch_select(int layout, const float* scores, int64_t stride, const 
   } else if (max_n <= 16384) {
     CSA2_REG_J(16);
   } else if (layout == kSelBlocks && (max_n + 7) / 8 <= 8192 && kmax <= 2048) {
-    if (super_max)
-      hipLaunchKernelGGL(select_blocks2_kernel<true>, grid, block, 0, stream, scores, stride, super_max, nsup_stride,
-                         n_visible, k1, out1, k2, out2);
+    const bool vec = super_max && reinterpret_cast<uintptr_t>(super_max) % 16 == 0 && nsup_stride % 4 == 0 &&
+                     reinterpret_cast<uintptr_t>(scores) % 32 == 0 && stride % 8 == 0;
+    if (vec)
+      hipLaunchKernelGGL((select_blocks3_kernel<true, true>), grid, block, 0, stream, scores, stride, super_max,
+                         nsup_stride, n_visible, k1, out1, k2, out2);
+    else if (super_max)
+      hipLaunchKernelGGL((select_blocks3_kernel<true, false>), grid, block, 0, stream, scores, stride, super_max,
+                         nsup_stride, n_visible, k1, out1, k2, out2);
     else
-      hipLaunchKernelGGL(select_blocks2_kernel<false>, grid, block, 0, stream, scores, stride, super_max,
+      hipLaunchKernelGGL((select_blocks3_kernel<false, false>), grid, block, 0, stream, scores, stride, super_max,
                          nsup_stride, n_visible, k1, out1, k2, out2);
   } else {
     hipLaunchKernelGGL(select_mem_kernel, grid, block, 0, stream, layout, scores, stride, pool_blocks, n_pool,
