@@ -11,10 +11,10 @@
 // query and the probabilities are split into hi + lo bf16 parts, so every
 // product carries ~16 mantissa bits and accumulates in fp32.
 //
-// Workgroup = (split, row, head group of 32): 4 waves.  A pair of waves owns 16
-// heads; each of the two keeps the query (hi/lo) and the output accumulator O^T
-// for its half of the 512 dims in registers, and the two partial S^T tiles are
-// summed through LDS.  Entries stream through LDS in chunks of 64: each chunk is decoded
+// Workgroup = (split, row, head group of 32): 8 waves.  Four waves own 16 heads;
+// each keeps the query (hi/lo) and the output accumulator O^T for its quarter of
+// the 512 dims in registers, and the four partial S^T tiles are summed through
+// LDS in a fixed order.  Entries stream through LDS in chunks of 64: each chunk is decoded
 // once into a row-major copy (operand A of S^T = C Q^T) and a transposed copy
 // (operand A of O^T = C^T P^T).  S^T's accumulator layout gives each lane the
 // probabilities of exactly the entries it must feed as operand B of the second
@@ -79,17 +79,17 @@ __device__ __forceinline__ bf16x8_t decode_fp8x8(uint32_t w0, uint32_t w1) {
 // Decode one chunk (64 entries x 512 dims) into the row-major and the
 // transposed LDS copies.  Thread tiles are 4 entries x 8 dims; for chunks of a
 // single row kind every gather of the thread is issued before any conversion.
-template <int NP, int KIND>
+template <int NT, int KIND>
 __device__ __forceinline__ void decode_chunk(const AttnParams& a, const int64_t* sOff, const int* sType,
                                              unsigned long long vmask, __bf16* sK, __bf16* sVt, int tid) {
-  constexpr int kTPT = (kChunk / 4) * 64 / (NP * 128);   // tiles per thread
+  constexpr int kTPT = (kChunk / 4) * 64 / NT;   // tiles per thread
   constexpr int kGroup = kTPT;                            // every tile's gathers in flight together
 #pragma unroll
   for (int j0 = 0; j0 < kTPT; j0 += kGroup) {
     uint32_t raw0[kGroup][4], raw1[kGroup][4];
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
-      const int T = tid + (j0 + j) * NP * 128;
+      const int T = tid + (j0 + j) * NT;
       const int eg = T & 15, dg = T >> 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -106,7 +106,7 @@ __device__ __forceinline__ void decode_chunk(const AttnParams& a, const int64_t*
     }
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
-      const int T = tid + (j0 + j) * NP * 128;
+      const int T = tid + (j0 + j) * NT;
       const int eg = T & 15, dg = T >> 4;
       bf16x8_t v[4];
 #pragma unroll
@@ -138,11 +138,16 @@ __device__ __forceinline__ void decode_chunk(const AttnParams& a, const int64_t*
   }
 }
 
-template <int NP>
-__global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) {
+// NP head groups of 16 per workgroup, ND waves per head group (each 512/ND dims)
+template <int NP, int ND>
+__global__ __launch_bounds__(NP * ND * 64, 1) void sparse_attn_kernel(AttnParams a) {
+  constexpr int NT = NP * ND * 64;
+  constexpr int kDims = 512 / ND;     // dims per wave
+  constexpr int kS = kDims / 32;      // K steps of S^T
+  constexpr int kM = kDims / 16;      // dim tiles of O^T
+  static_assert(NP * ND * 64 * 16 * 4 <= kChunk * kKLd * 2, "S^T partials fit in the row-major copy");
   __shared__ __attribute__((aligned(16))) __bf16 sK[kChunk * kKLd];
   __shared__ __attribute__((aligned(16))) __bf16 sVt[512 * kVLd];
-  __shared__ __attribute__((aligned(16))) float sS[NP][64][16];
   __shared__ int64_t sOff[kChunk];
   __shared__ int sType[kChunk];
   __shared__ unsigned long long sMask;
@@ -154,8 +159,8 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int pr = w % NP;       // head group of 16
-  const int half = w / NP;     // 0: dims 0..255, 1: dims 256..511
-  const int dbase = 256 * half;
+  const int part = w / NP;     // dims [kDims * part, kDims * (part + 1))
+  const int dbase = kDims * part;
   const int g = lane >> 4;     // lane group 0..3
   const int hl = lane & 15;
   const int h = 16 * NP * blockIdx.z + 16 * pr + hl;   // head groups of 16*NP heads across blockIdx.z
@@ -179,21 +184,21 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
     if (e < a.k) idx_next = a.idx[(int64_t)r * a.k + e];
   }
   __builtin_amdgcn_sched_barrier(0);
-  f32x4 qraw[16];
+  f32x4 qraw[2 * kS];
   {
     const float* qp = a.q + ((int64_t)r * a.H + h) * 512 + dbase + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kS; ++s) {
       qraw[2 * s] = *reinterpret_cast<const f32x4*>(qp + 32 * s);
       qraw[2 * s + 1] = *reinterpret_cast<const f32x4*>(qp + 32 * s + 4);
     }
   }
   // query operands (B of S^T = C Q^T): head h, dims dbase + 32s + 8g .. +8, prescaled
-  bf16x8_t qhi[8], qlo[8];
+  bf16x8_t qhi[kS], qlo[kS];
   bool q_ready = false;
   auto convert_query = [&]() {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kS; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = qraw[2 * s + (e >> 2)][e & 3] * a.qscale;
@@ -205,9 +210,9 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
     q_ready = true;
   };
 
-  f32x4 oacc[16];
+  f32x4 oacc[kM];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) oacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < kM; ++m) oacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
@@ -245,21 +250,21 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
 
     // 2. decode 4 entries x 8 dims per tile into both LDS copies
     if (ebase + kChunk <= a.k)
-      decode_chunk<NP, kLatentRows>(a, sOff, sType, vmask, sK, sVt, tid);
+      decode_chunk<NT, kLatentRows>(a, sOff, sType, vmask, sK, sVt, tid);
     else if (ebase >= a.k)
-      decode_chunk<NP, kWindowRows>(a, sOff, sType, vmask, sK, sVt, tid);
+      decode_chunk<NT, kWindowRows>(a, sOff, sType, vmask, sK, sVt, tid);
     else
-      decode_chunk<NP, kMixedRows>(a, sOff, sType, vmask, sK, sVt, tid);
+      decode_chunk<NT, kMixedRows>(a, sOff, sType, vmask, sK, sVt, tid);
     __syncthreads();
 
     if (!q_ready) convert_query();
 
-    // 3. partial S^T[64 entries x 16 heads] over this wave's 256 dims
+    // 3. partial S^T[64 entries x 16 heads] over this wave's kDims dims
     f32x4 sacc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kS; ++s) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const bf16x8_t A =
@@ -268,24 +273,22 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
         sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qlo[s], sacc[t], 0, 0, 0);
       }
     }
-    // the two halves of a head group exchange partial sums through LDS
-    f32x4* slot = reinterpret_cast<f32x4*>(&sS[pr][lane][0]);
-    if (half == 0) {
+    // the ND waves of a head group add their partial sums in part order,
+    // through the row-major copy's LDS once every wave is done reading it
+    __syncthreads();
+    f32x4* slots = reinterpret_cast<f32x4*>(sK);   // [NP][ND][64 lanes][4]
+    {
+      f32x4* mine = slots + ((pr * ND + part) * 64 + lane) * 4;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) slot[t] = sacc[t];
+      for (int t = 0; t < 4; ++t) mine[t] = sacc[t];
     }
     __syncthreads();
-    if (half == 1) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        sacc[t] += slot[t];
-        slot[t] = sacc[t];
-      }
-    }
-    __syncthreads();
-    if (half == 0) {
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc = slots[((pr * ND + 0) * 64 + lane) * 4 + t];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sacc[t] = slot[t];
+      for (int p = 1; p < ND; ++p) acc += slots[((pr * ND + p) * 64 + lane) * 4 + t];
+      sacc[t] = acc;
     }
 
     // 4. online softmax (lane holds entries 16t + 4g + i of head h)
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
     l_run = l_run * alpha + psum;
     m_run = m_new;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) oacc[m] *= alpha;
+    for (int m = 0; m < kM; ++m) oacc[m] *= alpha;
 
     // 5. O^T[256 dims x 16 heads] += C^T P^T, two k-steps of 32 entries
 #pragma unroll
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
         blo[i] = (__bf16)(p - (float)hi);
       }
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
+      for (int m = 0; m < kM; ++m) {
         const __bf16* vrow = &sVt[(dbase + 16 * m + hl) * kVLd + 32 * j + 4 * g];
         const bf16x4_t lo4 = *reinterpret_cast<const bf16x4_t*>(vrow);
         const bf16x4_t hi4 = *reinterpret_cast<const bf16x4_t*>(vrow + 16);
@@ -345,13 +348,13 @@ __global__ __launch_bounds__(NP * 128, 1) void sparse_attn_kernel(AttnParams a) 
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     float* op = a.out + ((int64_t)r * a.H + h) * 512 + dbase + 4 * g;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = oacc[m] * inv;
+    for (int m = 0; m < kM; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = oacc[m] * inv;
   } else {
     const int64_t slot = ((int64_t)r * a.splits + split) * a.H + h;
     float* op = a.part_o + slot * 512 + dbase + 4 * g;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = oacc[m];
-    if (g == 0 && half == 0) {
+    for (int m = 0; m < kM; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = oacc[m];
+    if (g == 0 && part == 0) {
       a.part_ml[2 * slot] = m_run;
       a.part_ml[2 * slot + 1] = l_tot;
     }
@@ -452,17 +455,17 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
     a.part_o = static_cast<float*>(L.workspace);
     a.part_ml = a.part_o + (size_t)R * a.splits * L.H * 512;
   }
-  // Workgroups of 32 heads (4 waves): each wave keeps the query and the output
-  // accumulator of 16 heads x 256 dims in registers, which fits the 512
-  // registers a wave has at one wave per SIMD; more heads split over blockIdx.z.
+  // Workgroups of 32 heads (8 waves): each wave keeps the query and the output
+  // accumulator of 16 heads x 128 dims in registers; more heads split over
+  // blockIdx.z.
   if (L.H % 16 != 0 || L.H < 16) return hipErrorInvalidValue;
   const int NP = L.H >= 32 ? 2 : 1;
   if (L.H % (16 * NP) != 0) return hipErrorInvalidValue;
   dim3 grid((unsigned)a.splits, (unsigned)R, (unsigned)(L.H / (16 * NP)));
   if (NP == 2)
-    hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((sparse_attn_kernel<2, 4>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((sparse_attn_kernel<1, 4>), grid, dim3(256), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.splits == 1) return err;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)L.H, (unsigned)R), dim3(512), 0, stream, a.part_o,
