@@ -29,6 +29,7 @@ constexpr int kChunk = 64;                 // entries per LDS chunk
 constexpr int kKLd = 512 + 8;              // bf16 row stride of the row-major copy
 constexpr int kVLd = kChunk + 8;           // bf16 row stride of the transposed copy
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kAttnTargetWorkgroups = 256;   // one per compute unit
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -406,20 +407,25 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restri
   out[((int64_t)r * H + h) * 512 + d] = L > 0.f ? acc / L : 0.f;
 }
 
-int attn_splits(int R, int k, int win_max) {
-  const int n_chunks = (k + win_max + kChunk - 1) / kChunk;
+// Head groups of 16 heads per workgroup (32 when H allows).
+static int attn_group_heads(int H) { return H >= 32 ? 32 : 16; }
+
+// Splits of a row's entry chunks: enough workgroups to give every compute unit
+// about one (a workgroup's LDS fills a compute unit), never more splits than
+// chunks, and chunks spread evenly over the splits.
+int attn_splits(int R, int H, int k_plus_win) {
+  const int n_chunks = (k_plus_win + kChunk - 1) / kChunk;
   if (n_chunks <= 1) return 1;
-  int want = (512 + R - 1) / R;            // aim for ~2 workgroups per CU
+  const int64_t groups = (int64_t)R * (H > 0 ? (H + attn_group_heads(H) - 1) / attn_group_heads(H) : 1);
+  int64_t want = (kAttnTargetWorkgroups + groups - 1) / groups;
   if (want < 1) want = 1;
   if (want > n_chunks) want = n_chunks;
-  const int cps = (n_chunks + want - 1) / want;
+  const int cps = (int)((n_chunks + want - 1) / want);
   return (n_chunks + cps - 1) / cps;
 }
 
 size_t attn_workspace_bytes(int R, int H, int k_plus_win) {
-  const int n_chunks = (k_plus_win + kChunk - 1) / kChunk;
-  const int splits = attn_splits(R, k_plus_win, 0);
-  (void)n_chunks;
+  const int splits = attn_splits(R, H, k_plus_win);
   if (splits <= 1) return 0;
   return (size_t)R * splits * H * (512 + 2) * sizeof(float);
 }
@@ -443,7 +449,7 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
   a.Tw = L.Tw;
   a.qscale = L.sm_scale * kLog2e;
   a.n_chunks = (L.k + L.win_max + kChunk - 1) / kChunk;
-  a.splits = attn_splits(R, L.k, L.win_max);
+  a.splits = attn_splits(R, L.H, L.k + L.win_max);
   a.chunks_per_split = (a.n_chunks + a.splits - 1) / a.splits;
   if (a.n_chunks == 0) {
     a.splits = 1;
@@ -455,11 +461,11 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
     a.part_o = static_cast<float*>(L.workspace);
     a.part_ml = a.part_o + (size_t)R * a.splits * L.H * 512;
   }
-  // Workgroups of 32 heads (8 waves): each wave keeps the query and the output
-  // accumulator of 16 heads x 128 dims in registers; more heads split over
-  // blockIdx.z.
+  // Workgroups of 32 heads (8 waves); more heads split over blockIdx.z.  Four
+  // waves of 128 dims per 16-head group keep every wave's chain of products
+  // short and leave two waves per SIMD to overlap LDS and matrix-core work.
   if (L.H % 16 != 0 || L.H < 16) return hipErrorInvalidValue;
-  const int NP = L.H >= 32 ? 2 : 1;
+  const int NP = attn_group_heads(L.H) / 16;
   if (L.H % (16 * NP) != 0) return hipErrorInvalidValue;
   dim3 grid((unsigned)a.splits, (unsigned)R, (unsigned)(L.H / (16 * NP)));
   if (NP == 2)

@@ -51,7 +51,7 @@ struct AttnLaunch {
   size_t workspace_bytes;
 };
 
-int attn_splits(int R, int k, int win_max);
+int attn_splits(int R, int H, int k_plus_win);
 size_t attn_workspace_bytes(int R, int H, int k_plus_win);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t stream);
 
