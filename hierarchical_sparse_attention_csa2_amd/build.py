@@ -30,7 +30,7 @@ HIPCC_FLAGS = [
 
 # per-source extra flags: the scans keep their MFMA results in VGPRs (the code
 # reads every result element once, right away)
-EXTRA_FLAGS = {"prefill_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {name: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for name in ("prefill_scan.hip", "scan.hip")}
 
 
 def hipcc() -> str:

@@ -24,6 +24,7 @@
 // same fixed-order result.
 #include "device_common.h"
 #include "kernels.h"
+#include "score_core.h"
 
 namespace csa2 {
 
@@ -31,13 +32,6 @@ constexpr int kScanThreads = 256;
 constexpr int kScanWaves = kScanThreads / 64;
 constexpr int kScanChunk = kScanWaves * 64;     // positions per workgroup (64 per wave)
 constexpr int kPrefillMinQueries = 16;          // queries per sequence for the many-query scan
-
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ u32x4_t load_codes16(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
 
 template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
@@ -52,63 +46,6 @@ __device__ __forceinline__ uint32_t group8_max_u32(uint32_t x) {
   x = y > x ? y : x;
   y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);           // row_half_mirror
   return y > x ? y : x;
-}
-
-// Score of one key on the vector ALUs, for any scale bytes: each block's exact
-// sum (E2M1 codes decoded to f16 with v_cvt_scalef32_pk_f16_fp4, v_dot2 into
-// fp32) scaled with ldexp, then ((v0+v1)+v2)+v3 in fp32.
-__device__ __forceinline__ float score_key_valu(const uint8_t* qr, const uint8_t* qs, const uint8_t* kr,
-                                                const uint8_t* ksr) {
-  float s = 0.0f;
-#pragma unroll 1
-  for (int b = 0; b < 4; ++b) {
-    half2_t qh[16];
-    load_query_block(qr + 16 * b, qh);
-    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(kr + 16 * b);
-    const float v = __builtin_amdgcn_ldexpf(block_dot(c, qh), (int)qs[b] + (int)ksr[b] - 254);
-    s = b == 0 ? v : s + v;
-  }
-  return s;
-}
-
-// The four block values of 16 keys on the matrix cores.  kb[u], ek[u]: lane
-// 16g + c holds block g of key c of group u (codes, scale byte); qa, eq: the
-// block-diagonal query operand (lane 16g + i holds query block g when
-// i % 4 == g) and this lane's query scale byte (block g).  Returns the score of
-// key c of group g, the wave's key 16g + c, in lane 16g + c.
-__device__ __forceinline__ float score_groups_mfma(const u32x4_t qa, int eq, const u32x4_t* kb, const uint32_t* ek) {
-  const int g = (threadIdx.x & 63) >> 4;
-  const i32x8_t a8 = {(int)qa[0], (int)qa[1], (int)qa[2], (int)qa[3], 0, 0, 0, 0};
-  f32x4_t acc[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const i32x8_t b8 = {(int)kb[u][0], (int)kb[u][1], (int)kb[u][2], (int)kb[u][3], 0, 0, 0, 0};
-    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-    acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, zero, 4, 4, 0, eq, 0, (int)ek[u]);
-    // keep the product here, with every lane active: the matrix core reads its
-    // operands from all 64 lanes, so it must not be moved into a branch that
-    // only some lanes take
-    asm volatile("" : "+v"(acc[u]));
-  }
-  // lane 16g + c: column c, rows 4g..4g+3; element i = row 4g + i = v_i of
-  // key c of group u.  Take group u = g.
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = (g & 1) ? acc[1][i] : acc[0][i];
-    const float hi = (g & 1) ? acc[3][i] : acc[2][i];
-    v[i] = (g & 2) ? hi : lo;
-  }
-  float s = v[0] + v[1];
-  s = s + v[2];
-  s = s + v[3];
-  return s + 0.0f;   // an exact zero sum is +0
-}
-
-// block exponent eq + ek - 254 outside [-124, 114]: the matrix-core value may
-// be inexact
-__device__ __forceinline__ bool exponent_out_of_range(int eq, uint32_t ek) {
-  return (uint32_t)(eq + (int)ek - 130) > 244u;
 }
 
 // Grid (ceil(N_max / 256), M, B): query row r = seq * M + blockIdx.y.  Each wave
