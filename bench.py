@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0
 INDEX_KEY_BYTES = 68          # 64 B of E2M1 codes + 4 E8M0 scale bytes per cached entry
 COUNTERS = os.path.join(ROOT, "profiles", "index_scan_kernel_c3_hbm_counters.txt")
 SCAN_SOURCES = ("hierarchical_sparse_attention_csa2_amd/csrc/scan.hip",
+                "hierarchical_sparse_attention_csa2_amd/csrc/score_core.h",
                 "hierarchical_sparse_attention_csa2_amd/csrc/device_common.h")
 
 
