@@ -528,6 +528,27 @@ __device__ __forceinline__ int block_excl_scan(int* buf, int x, int& total) {
   return __builtin_amdgcn_readlane(wi, w) - __builtin_amdgcn_readlane(wt, w) + incl - x;
 }
 
+// Level 2 of the block filter: exact selection among the m2 <= 1024*J
+// survivors in sh.ckeys / sh.cids (id order), whose first-digit histogram over
+// [T1, kmax1] is already counted.
+template <int J>
+__device__ __forceinline__ void blocks_level2(Blocks3Shared& sh, int m2, uint32_t T1, uint32_t kmax1, int K0,
+                                              int32_t* o0, int K1, int32_t* o1) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int Jp2 = (m2 + 1023) >> 10;
+  uint32_t k2[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = (w * Jp2 + j) * 64 + lane;
+    k2[j] = (j < Jp2 && i < m2) ? sh.ckeys[i] : 0u;
+  }
+  Thr th0, th1;
+  select_thresholds(sh.c, sh.s, k2, Jp2, m2, T1, kmax1, K0, K1, 0, th0, th1, true);
+  emit_sel(
+      sh.s, k2, Jp2, th0, th1, [&](int tg, int pos, int j, int i) { (tg ? o1 : o0)[pos] = sh.cids[i]; },
+      [&](int tg, int p) { (tg ? o1 : o0)[p] = -1; });
+}
+
 // kVec: super_max rows 16-byte aligned and block rows 32-byte aligned, so a
 // thread's 8 super maxima and a super-block's 8 block maxima are two 16-byte
 // loads each.
@@ -706,20 +727,12 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks3_kernel(const float
     }
   }
   __syncthreads();
-  // level 2 over the m2 survivors (item order = id order), all within [T1, kmax1]
-  const int lane = t & 63, w = t >> 6;
-  const int Jp2 = (m2 + 1023) >> 10;
-  uint32_t k2[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int i = (w * Jp2 + j) * 64 + lane;
-    k2[j] = (j < Jp2 && i < m2) ? sh.ckeys[i] : 0u;
-  }
-  Thr th0, th1;
-  select_thresholds(sh.c, sh.s, k2, Jp2, m2, T1, kmax1, K0, K1, 0, th0, th1, true);
-  emit_sel(
-      sh.s, k2, Jp2, th0, th1, [&](int tg, int pos, int j, int i) { (tg ? o1 : o0)[pos] = sh.cids[i]; },
-      [&](int tg, int p) { (tg ? o1 : o0)[p] = -1; });
+  // level 2 over the m2 survivors (item order = id order), all within [T1, kmax1];
+  // registers sized to the count (a typical row keeps 2,000-3,000)
+  if (m2 <= 4 * kSelThreads)
+    blocks_level2<4>(sh, m2, T1, kmax1, K0, o0, K1, o1);
+  else
+    blocks_level2<16>(sh, m2, T1, kmax1, K0, o0, K1, o1);
 }
 
 // ---------------------------------------------------------------------------
