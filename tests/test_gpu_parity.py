@@ -74,11 +74,14 @@ def _same_f32(a, b):
 
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed"])
-@pytest.mark.parametrize("B,M,N", [(1, 40, 3000), (2, 33, 2100), (1, 130, 5000)])
+@pytest.mark.parametrize("B,M,N", [(1, 40, 3000), (2, 33, 2100), (1, 130, 5000), (3, 5, 2500), (2, 15, 700),
+                                   (2, 16, 1900)])
 def test_prefill_scan_bitexact(kind, B, M, N):
-    """Many queries per sequence (the matrix-core scan): scores, block maxima and
-    super-block maxima bit-exact for ragged visibility, partial query groups,
-    several key chunks, and tiles whose scales need the VALU path (spread)."""
+    """Several queries per sequence: scores, block maxima and super-block maxima
+    bit-exact for ragged visibility, partial query groups, several key chunks,
+    and tiles whose scales need the VALU path (spread, mixed).  M < 16 runs the
+    decode scan over a (chunk, query, sequence) grid, M >= 16 the many-query
+    matrix-core scan; M = 15 and 16 sit on either side of that switch."""
     w = Workload("pf", 777 + N + M, B=B, N=N, M=M)
     cache, (lay,) = host_inputs(w, kind=kind)
     rng = np.random.default_rng(N + 3 * M)
