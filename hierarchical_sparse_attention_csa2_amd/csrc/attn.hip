@@ -363,47 +363,63 @@ __global__ __launch_bounds__(NP * ND * 64, 1) void sparse_attn_kernel(AttnParams
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One workgroup per (row, head), one thread per output dim; the loads of up to
-// kCombineUnroll splits are issued together.
-constexpr int kCombineUnroll = 16;
+// One workgroup per (row, head), one thread per output dim.  The splits' (m, l)
+// pairs are read once into LDS and turned into weights there; each thread then
+// reads only its own dim of every split's o, kCombineGroup loads in flight.
+constexpr int kMaxSplits = kAttnTargetWorkgroups;   // attn_splits never exceeds it
+constexpr int kCombineGroup = 8;
 
 __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, int splits, int H,
                                                            float* __restrict__ out) {
+  __shared__ float sw[kMaxSplits];   // 2^(m_s - M), 0 for splits that saw nothing
+  __shared__ float sL;
   const int r = blockIdx.y;
   const int h = blockIdx.x;
   const int d = threadIdx.x;
   const int64_t base = (int64_t)r * splits * H + h;     // slot of split s: base + s*H
-  float M = -__builtin_inff(), L = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < splits; s0 += kCombineUnroll) {
-    // one round of loads: every split's (m, l) and o[d]
-    float mv[kCombineUnroll], lv[kCombineUnroll], ov[kCombineUnroll];
+  if (threadIdx.x < 64) {
+    // wave 0: M = max_s m_s, then the weights and L = sum_s w_s l_s in split order
+    float m[kMaxSplits / 64], l[kMaxSplits / 64];
+    float M = -__builtin_inff();
 #pragma unroll
-    for (int j = 0; j < kCombineUnroll; ++j) {
-      const bool on = s0 + j < splits;
-      const int64_t slot = base + (int64_t)(on ? s0 + j : s0) * H;
-      mv[j] = on ? part_ml[2 * slot] : -__builtin_inff();
-      lv[j] = part_ml[2 * slot + 1];
-      ov[j] = part_o[slot * 512 + d];
-    }
-    float Mn = M;
-#pragma unroll
-    for (int j = 0; j < kCombineUnroll; ++j) Mn = fmaxf(Mn, mv[j]);
-    if (Mn == -__builtin_inff()) continue;   // nothing seen yet
-    // rescale what came before, then add this group in split order
-    const float c = exp2f(M - Mn);
-    L *= c;
-    acc *= c;
-#pragma unroll
-    for (int j = 0; j < kCombineUnroll; ++j) {
-      if (s0 + j < splits) {
-        const float wgt = exp2f(mv[j] - Mn);
-        L += wgt * lv[j];
-        acc += wgt * ov[j];
+    for (int j = 0; j < kMaxSplits / 64; ++j) {
+      const int sidx = 64 * j + threadIdx.x;
+      m[j] = -__builtin_inff();
+      l[j] = 0.f;
+      if (sidx < splits) {
+        m[j] = part_ml[2 * (base + (int64_t)sidx * H)];
+        l[j] = part_ml[2 * (base + (int64_t)sidx * H) + 1];
       }
+      M = fmaxf(M, m[j]);
     }
-    M = Mn;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    // L = sum_s w_s l_s: per lane in j order, then a fixed butterfly
+    float L = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxSplits / 64; ++j) {
+      const int sidx = 64 * j + threadIdx.x;
+      const float w = (M == -__builtin_inff() || m[j] == -__builtin_inff()) ? 0.f : exp2f(m[j] - M);
+      if (sidx < splits) sw[sidx] = w;
+      L += w * l[j];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+    if (threadIdx.x == 0) sL = L;
   }
+  __syncthreads();
+  float acc = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += kCombineGroup) {
+    float ov[kCombineGroup];
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j)
+      ov[j] = s0 + j < splits ? part_o[(base + (int64_t)(s0 + j) * H) * 512 + d] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j)
+      if (s0 + j < splits) acc += sw[s0 + j] * ov[j];
+  }
+  const float L = sL;
   out[((int64_t)r * H + h) * 512 + d] = L > 0.f ? acc / L : 0.f;
 }
 
