@@ -14,7 +14,7 @@ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // index_full workspace carve-up
 struct FullWs {
-  size_t block_max, super_max, topk_blocks, topk_scores, total;
+  size_t block_max, super_max, topk_blocks, topk_scores, key_floor, total;
 };
 
 inline FullWs full_ws(int64_t R, int64_t N_max, int k) {
@@ -25,7 +25,8 @@ inline FullWs full_ws(int64_t R, int64_t N_max, int k) {
   w.super_max = align_up(w.block_max + (size_t)R * nblk * sizeof(float));
   w.topk_blocks = align_up(w.super_max + (size_t)R * nsup * sizeof(float));
   w.topk_scores = align_up(w.topk_blocks + (size_t)R * (k > 0 ? k : 0) * sizeof(int32_t));
-  w.total = align_up(w.topk_scores + (size_t)R * (k > 0 ? k : 0) * 8 * sizeof(float));
+  w.key_floor = align_up(w.topk_scores + (size_t)R * (k > 0 ? k : 0) * 8 * sizeof(float));
+  w.total = align_up(w.key_floor + (size_t)R * sizeof(uint32_t));
   return w;
 }
 
@@ -119,15 +120,20 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
   if (e != hipSuccess) return CSA2_ERR_HIP;
   // the pool's top-k lies in the pool's first min(k, n_pool) blocks: rescore only those
   const int kb = k < n_pool ? k : n_pool;
+  // When the first kb = k blocks are the k best of the row, the k-th best block
+  // maximum (the selection's floor) is at most the k-th best position score:
+  // those k block maxima are k positions reaching it.  The top-k then drops
+  // every slot below that floor unexamined.
+  uint32_t* key_floor = reinterpret_cast<uint32_t*>(ws + w.key_floor);
   e = csa2::launch_select(csa2::kSelBlocks, bmax, nblk, nullptr, 0, n_visible, (int)R, n_pool, pool_blocks,
-                          kb, k > 0 ? topk_blocks : nullptr, smax, nsup, s);
+                          kb, k > 0 ? topk_blocks : nullptr, smax, nsup, s, nullptr, key_floor);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   if (k == 0) return CSA2_OK;
   e = csa2::launch_pool_scan(q_codes, q_scales, k_codes, k_scales, topk_blocks, kb, n_visible, B, M, N_max,
                              topk_scores, s);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   e = csa2::launch_select(csa2::kSelPool, topk_scores, 8 * (int64_t)kb, topk_blocks, kb, n_visible, (int)R, k, idx,
-                          0, nullptr, nullptr, 0, s);
+                          0, nullptr, nullptr, 0, s, kb == k ? key_floor : nullptr, nullptr);
   return hip_status(e);
 }
 

@@ -29,9 +29,14 @@ enum SelectLayout { kSelBlocks = 0, kSelPool = 1, kSelFull = 2 };
 
 // super_max (blocks layout only, may be null): maxima of 8 consecutive blocks,
 // row stride nsup_stride, as written by the indexer scan.
+// floor_in (may be null): per row, an order key that every selected item
+// reaches (items below it are dropped unexamined); floor_out (may be null):
+// per row, the order key of target 2's k2-th item, or 1 when the row has at
+// most k2 items.
 hipError_t launch_select(int layout, const float* scores, int64_t stride, const int32_t* pool_blocks,
                          int64_t n_pool, const int32_t* n_visible, int R, int k1, int32_t* out1, int k2,
-                         int32_t* out2, const float* super_max, int64_t nsup_stride, hipStream_t stream);
+                         int32_t* out2, const float* super_max, int64_t nsup_stride, hipStream_t stream,
+                         const uint32_t* floor_in = nullptr, uint32_t* floor_out = nullptr);
 
 struct AttnLaunch {
   const float* q;

@@ -426,13 +426,18 @@ __device__ __forceinline__ void select_targets(SelShared& sh, const RowView row,
 // Rows of at most 1024*J items (any layout), items in registers.  The lane
 // layout follows the row's capacity (stride, or 8*n_pool slots), so the loads
 // are issued before n_visible arrives and masked after.
+// floor_in (may be null): keys below floor_in[r] cannot be selected and are
+// dropped; floor_out (may be null): the key of target 1's K1-th item, or 1 when
+// the row has at most K1 items.
 template <int J, int LAYOUT>
 __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __restrict__ scores, int64_t stride,
                                                                  const int32_t* __restrict__ pool_blocks,
                                                                  int64_t n_pool,
                                                                  const int32_t* __restrict__ n_visible, int K0,
                                                                  int32_t* __restrict__ out0, int K1,
-                                                                 int32_t* __restrict__ out1) {
+                                                                 int32_t* __restrict__ out1,
+                                                                 const uint32_t* __restrict__ floor_in,
+                                                                 uint32_t* __restrict__ floor_out) {
   __shared__ RegShared sh;
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -458,13 +463,15 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
   if (LAYOUT == kSelBlocks) n = (nv + 7) >> 3;
   if (LAYOUT == kSelFull) n = nv;
   n = n < cap ? n : cap;
+  const uint32_t fl = floor_in ? floor_in[r] : 1u;
   uint32_t k[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int i = (w * Jp + j) * 64 + lane;
     bool ok = j < Jp && i < n;
     if constexpr (LAYOUT == kSelPool) ok = ok && pbv[j] >= 0 && 8 * (int64_t)pbv[j] + (i & 7) < nv;
-    k[j] = ok ? order_key(x[j]) : 0u;
+    const uint32_t key = order_key(x[j]);
+    k[j] = ok && key >= fl ? key : 0u;
   }
   int32_t* o0 = out0 ? out0 + (int64_t)r * K0 : nullptr;
   int32_t* o1 = out1 ? out1 + (int64_t)r * K1 : nullptr;
@@ -480,6 +487,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
   key_range(sh.s, k, Jp, valid, kmin, kmax);
   Thr th0, th1;
   select_thresholds(sh.c, sh.s, k, Jp, valid, kmin, kmax, K0, K1, 0, th0, th1);
+  if (floor_out && threadIdx.x == 0) floor_out[r] = (K1 > 0 && th1.keff == K1 && valid > K1) ? th1.T : 1u;
   emit_sel(
       sh.s, k, Jp, th0, th1,
       [&](int t, int pos, int j, int i) {
@@ -533,7 +541,7 @@ __device__ __forceinline__ int block_excl_scan(int* buf, int x, int& total) {
 // [T1, kmax1] is already counted.
 template <int J>
 __device__ __forceinline__ void blocks_level2(Blocks3Shared& sh, int m2, uint32_t T1, uint32_t kmax1, int K0,
-                                              int32_t* o0, int K1, int32_t* o1) {
+                                              int32_t* o0, int K1, int32_t* o1, uint32_t* floor_out) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int Jp2 = (m2 + 1023) >> 10;
   uint32_t k2[J];
@@ -544,6 +552,9 @@ __device__ __forceinline__ void blocks_level2(Blocks3Shared& sh, int m2, uint32_
   }
   Thr th0, th1;
   select_thresholds(sh.c, sh.s, k2, Jp2, m2, T1, kmax1, K0, K1, 0, th0, th1, true);
+  // the K1-th block of the whole row is the K1-th survivor (every block of the
+  // first K1 survives level 1)
+  if (floor_out && threadIdx.x == 0) *floor_out = (K1 > 0 && th1.keff == K1 && m2 > K1) ? th1.T : 1u;
   emit_sel(
       sh.s, k2, Jp2, th0, th1, [&](int tg, int pos, int j, int i) { (tg ? o1 : o0)[pos] = sh.cids[i]; },
       [&](int tg, int p) { (tg ? o1 : o0)[p] = -1; });
@@ -558,7 +569,8 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks3_kernel(const float
                                                                      int64_t nsup_stride,
                                                                      const int32_t* __restrict__ n_visible, int K0,
                                                                      int32_t* __restrict__ out0, int K1,
-                                                                     int32_t* __restrict__ out1) {
+                                                                     int32_t* __restrict__ out1,
+                                                                     uint32_t* __restrict__ floor_out) {
   __shared__ Blocks3Shared sh;
   const int r = blockIdx.x;
   const int t = threadIdx.x;
@@ -569,7 +581,10 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks3_kernel(const float
   if (!out0) K0 = 0;
   if (!out1) K1 = 0;
   const int kmaxK = K0 > K1 ? K0 : K1;
-  if (kmaxK == 0) return;
+  if (kmaxK == 0) {
+    if (floor_out && t == 0) floor_out[r] = 1u;
+    return;
+  }
 
   // level 1: super-blocks 8t..8t+7 (the scan's maxima are read ahead of n_visible)
   float sv[kB3Items];
@@ -730,9 +745,9 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks3_kernel(const float
   // level 2 over the m2 survivors (item order = id order), all within [T1, kmax1];
   // registers sized to the count (a typical row keeps 2,000-3,000)
   if (m2 <= 4 * kSelThreads)
-    blocks_level2<4>(sh, m2, T1, kmax1, K0, o0, K1, o1);
+    blocks_level2<4>(sh, m2, T1, kmax1, K0, o0, K1, o1, floor_out ? floor_out + r : nullptr);
   else
-    blocks_level2<16>(sh, m2, T1, kmax1, K0, o0, K1, o1);
+    blocks_level2<16>(sh, m2, T1, kmax1, K0, o0, K1, o1, floor_out ? floor_out + r : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -744,9 +759,11 @@ __global__ __launch_bounds__(kSelThreads) void select_mem_kernel(int layout, con
                                                                  int64_t n_pool,
                                                                  const int32_t* __restrict__ n_visible, int k1,
                                                                  int32_t* __restrict__ out1, int k2,
-                                                                 int32_t* __restrict__ out2) {
+                                                                 int32_t* __restrict__ out2,
+                                                                 uint32_t* __restrict__ floor_out) {
   __shared__ SelShared sh;
   const int r = blockIdx.x;
+  if (floor_out && threadIdx.x == 0) floor_out[r] = 1u;   // no floor from this path
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   RowView row;
   row.layout = layout;
@@ -784,7 +801,8 @@ __global__ __launch_bounds__(kSelThreads) void select_mem_kernel(int layout, con
 
 hipError_t launch_select(int layout, const float* scores, int64_t stride, const int32_t* pool_blocks,
                          int64_t n_pool, const int32_t* n_visible, int R, int k1, int32_t* out1, int k2,
-                         int32_t* out2, const float* super_max, int64_t nsup_stride, hipStream_t stream) {
+                         int32_t* out2, const float* super_max, int64_t nsup_stride, hipStream_t stream,
+                         const uint32_t* floor_in, uint32_t* floor_out) {
   // the longest possible row decides the path
   const int64_t max_n = layout == kSelPool ? 8 * n_pool : stride;
   const int ka = out1 ? k1 : 0, kb = out2 ? k2 : 0;
@@ -792,7 +810,7 @@ hipError_t launch_select(int layout, const float* scores, int64_t stride, const 
   const dim3 grid((unsigned)R), block(kSelThreads);
 #define CSA2_REG(J, L)                                                                                      \
   hipLaunchKernelGGL((select_reg_kernel<J, L>), grid, block, 0, stream, scores, stride, pool_blocks, n_pool, \
-                     n_visible, k1, out1, k2, out2)
+                     n_visible, k1, out1, k2, out2, floor_in, floor_out)
 #define CSA2_REG_J(J)                   \
   if (layout == kSelBlocks)             \
     CSA2_REG(J, kSelBlocks);            \
@@ -811,16 +829,16 @@ hipError_t launch_select(int layout, const float* scores, int64_t stride, const 
                      reinterpret_cast<uintptr_t>(scores) % 32 == 0 && stride % 8 == 0;
     if (vec)
       hipLaunchKernelGGL((select_blocks3_kernel<true, true>), grid, block, 0, stream, scores, stride, super_max,
-                         nsup_stride, n_visible, k1, out1, k2, out2);
+                         nsup_stride, n_visible, k1, out1, k2, out2, floor_out);
     else if (super_max)
       hipLaunchKernelGGL((select_blocks3_kernel<true, false>), grid, block, 0, stream, scores, stride, super_max,
-                         nsup_stride, n_visible, k1, out1, k2, out2);
+                         nsup_stride, n_visible, k1, out1, k2, out2, floor_out);
     else
       hipLaunchKernelGGL((select_blocks3_kernel<false, false>), grid, block, 0, stream, scores, stride, super_max,
-                         nsup_stride, n_visible, k1, out1, k2, out2);
+                         nsup_stride, n_visible, k1, out1, k2, out2, floor_out);
   } else {
     hipLaunchKernelGGL(select_mem_kernel, grid, block, 0, stream, layout, scores, stride, pool_blocks, n_pool,
-                       n_visible, k1, out1, k2, out2);
+                       n_visible, k1, out1, k2, out2, floor_out);
   }
 #undef CSA2_REG_J
 #undef CSA2_REG
