@@ -25,11 +25,12 @@
 
 namespace csa2 {
 
-constexpr int kChunk = 64;                 // entries per LDS chunk
 constexpr int kKLd = 512 + 8;              // bf16 row stride of the row-major copy
-constexpr int kVLd = kChunk + 8;           // bf16 row stride of the transposed copy
+template <int CH>
+constexpr int vld() { return CH + 8; }     // bf16 row stride of the transposed copy
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kAttnTargetWorkgroups = 256;   // one per compute unit
+constexpr int kAttnChunk = 32;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -80,10 +81,12 @@ __device__ __forceinline__ bf16x8_t decode_fp8x8(uint32_t w0, uint32_t w1) {
 // Decode one chunk (64 entries x 512 dims) into the row-major and the
 // transposed LDS copies.  Thread tiles are 4 entries x 8 dims; for chunks of a
 // single row kind every gather of the thread is issued before any conversion.
-template <int NT, int KIND>
+template <int NT, int KIND, int CH>
 __device__ __forceinline__ void decode_chunk(const AttnParams& a, const int64_t* sOff, const int* sType,
                                              unsigned long long vmask, __bf16* sK, __bf16* sVt, int tid) {
-  constexpr int kTPT = (kChunk / 4) * 64 / NT;   // tiles per thread
+  constexpr int kVLd = vld<CH>();
+  constexpr int kEG = CH / 4;                     // entry groups of 4
+  constexpr int kTPT = kEG * 64 / NT;             // tiles per thread
   constexpr int kGroup = kTPT;                            // every tile's gathers in flight together
 #pragma unroll
   for (int j0 = 0; j0 < kTPT; j0 += kGroup) {
@@ -91,7 +94,7 @@ __device__ __forceinline__ void decode_chunk(const AttnParams& a, const int64_t*
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
       const int T = tid + (j0 + j) * NT;
-      const int eg = T & 15, dg = T >> 4;
+      const int eg = T % kEG, dg = T / kEG;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t off = sOff[4 * eg + i];
@@ -108,7 +111,7 @@ __device__ __forceinline__ void decode_chunk(const AttnParams& a, const int64_t*
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
       const int T = tid + (j0 + j) * NT;
-      const int eg = T & 15, dg = T >> 4;
+      const int eg = T % kEG, dg = T / kEG;
       bf16x8_t v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -139,14 +142,19 @@ __device__ __forceinline__ void decode_chunk(const AttnParams& a, const int64_t*
   }
 }
 
-// NP head groups of 16 per workgroup, ND waves per head group (each 512/ND dims)
-template <int NP, int ND>
-__global__ __launch_bounds__(NP * ND * 64, 1) void sparse_attn_kernel(AttnParams a) {
+// NP head groups of 16 per workgroup, ND waves per head group (each 512/ND
+// dims), CH entries per chunk
+template <int NP, int ND, int CH>
+__device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
+  constexpr int kChunk = CH;
+  constexpr int kVLd = vld<CH>();
   constexpr int NT = NP * ND * 64;
   constexpr int kDims = 512 / ND;     // dims per wave
   constexpr int kS = kDims / 32;      // K steps of S^T
   constexpr int kM = kDims / 16;      // dim tiles of O^T
-  static_assert(NP * ND * 64 * 16 * 4 <= kChunk * kKLd * 2, "S^T partials fit in the row-major copy");
+  constexpr int kT = CH / 16;         // entry tiles of S^T
+  constexpr int kJ = CH / 32;         // K steps of O^T
+  static_assert(NP * ND * 64 * kT * 16 <= kChunk * kKLd * 2, "S^T partials fit in the row-major copy");
   __shared__ __attribute__((aligned(16))) __bf16 sK[kChunk * kKLd];
   __shared__ __attribute__((aligned(16))) __bf16 sVt[512 * kVLd];
   __shared__ int64_t sOff[kChunk];
@@ -251,23 +259,23 @@ __global__ __launch_bounds__(NP * ND * 64, 1) void sparse_attn_kernel(AttnParams
 
     // 2. decode 4 entries x 8 dims per tile into both LDS copies
     if (ebase + kChunk <= a.k)
-      decode_chunk<NT, kLatentRows>(a, sOff, sType, vmask, sK, sVt, tid);
+      decode_chunk<NT, kLatentRows, CH>(a, sOff, sType, vmask, sK, sVt, tid);
     else if (ebase >= a.k)
-      decode_chunk<NT, kWindowRows>(a, sOff, sType, vmask, sK, sVt, tid);
+      decode_chunk<NT, kWindowRows, CH>(a, sOff, sType, vmask, sK, sVt, tid);
     else
-      decode_chunk<NT, kMixedRows>(a, sOff, sType, vmask, sK, sVt, tid);
+      decode_chunk<NT, kMixedRows, CH>(a, sOff, sType, vmask, sK, sVt, tid);
     __syncthreads();
 
     if (!q_ready) convert_query();
 
-    // 3. partial S^T[64 entries x 16 heads] over this wave's kDims dims
-    f32x4 sacc[4];
+    // 3. partial S^T[CH entries x 16 heads] over this wave's kDims dims
+    f32x4 sacc[kT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kT; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kS; ++s) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < kT; ++t) {
         const bf16x8_t A =
             *reinterpret_cast<const bf16x8_t*>(&sK[(16 * t + hl) * kKLd + dbase + 32 * s + 8 * g]);
         sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qhi[s], sacc[t], 0, 0, 0);
@@ -277,25 +285,25 @@ __global__ __launch_bounds__(NP * ND * 64, 1) void sparse_attn_kernel(AttnParams
     // the ND waves of a head group add their partial sums in part order,
     // through the row-major copy's LDS once every wave is done reading it
     __syncthreads();
-    f32x4* slots = reinterpret_cast<f32x4*>(sK);   // [NP][ND][64 lanes][4]
+    f32x4* slots = reinterpret_cast<f32x4*>(sK);   // [NP][ND][64 lanes][kT]
     {
-      f32x4* mine = slots + ((pr * ND + part) * 64 + lane) * 4;
+      f32x4* mine = slots + ((pr * ND + part) * 64 + lane) * kT;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) mine[t] = sacc[t];
+      for (int t = 0; t < kT; ++t) mine[t] = sacc[t];
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x4 acc = slots[((pr * ND + 0) * 64 + lane) * 4 + t];
+    for (int t = 0; t < kT; ++t) {
+      f32x4 acc = slots[((pr * ND + 0) * 64 + lane) * kT + t];
 #pragma unroll
-      for (int p = 1; p < ND; ++p) acc += slots[((pr * ND + p) * 64 + lane) * 4 + t];
+      for (int p = 1; p < ND; ++p) acc += slots[((pr * ND + p) * 64 + lane) * kT + t];
       sacc[t] = acc;
     }
 
     // 4. online softmax (lane holds entries 16t + 4g + i of head h)
     float mloc = -__builtin_inff();
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < kT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 16 * t + 4 * g + i;
@@ -308,7 +316,7 @@ __global__ __launch_bounds__(NP * ND * 64, 1) void sparse_attn_kernel(AttnParams
     const float alpha = exp2f(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < kT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = exp2f(sacc[t][i] - m_new);
@@ -320,9 +328,9 @@ __global__ __launch_bounds__(NP * ND * 64, 1) void sparse_attn_kernel(AttnParams
 #pragma unroll
     for (int m = 0; m < kM; ++m) oacc[m] *= alpha;
 
-    // 5. O^T[256 dims x 16 heads] += C^T P^T, two k-steps of 32 entries
+    // 5. O^T[kDims dims x 16 heads] += C^T P^T, k-steps of 32 entries
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kJ; ++j) {
       bf16x8_t bhi, blo;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -361,6 +369,19 @@ __global__ __launch_bounds__(NP * ND * 64, 1) void sparse_attn_kernel(AttnParams
     }
   }
 }
+
+// 8-wave workgroups (32 heads).  With 32-entry chunks two fit a compute unit
+// (78 KB of LDS each) when a wave keeps to 128 registers (a few spill), so one
+// workgroup's loads overlap the other's products: better once the grid holds
+// several workgroups per compute unit, worse for a grid that does not.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void sparse_attn_kernel_h32c32_2wg(
+    AttnParams a) {
+  sparse_attn_body<2, 4, 32>(a);
+}
+__global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h32c32(AttnParams a) { sparse_attn_body<2, 4, 32>(a); }
+__global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h32c64(AttnParams a) { sparse_attn_body<2, 4, 64>(a); }
+__global__ __launch_bounds__(256) void sparse_attn_kernel_h16c32(AttnParams a) { sparse_attn_body<1, 4, 32>(a); }
+__global__ __launch_bounds__(256, 1) void sparse_attn_kernel_h16c64(AttnParams a) { sparse_attn_body<1, 4, 64>(a); }
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // One workgroup per (row, head), one thread per output dim.  The splits' (m, l)
@@ -426,11 +447,21 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restri
 // Head groups of 16 heads per workgroup (32 when H allows).
 static int attn_group_heads(int H) { return H >= 32 ? 32 : 16; }
 
+// Entries per chunk: 32 keeps a workgroup's LDS at 78 KB, so two workgroups
+// share a compute unit and one's loads overlap the other's products.
+static int attn_chunk(int R, int H, int k_plus_win) {
+  (void)R;
+  (void)H;
+  (void)k_plus_win;
+  return kAttnChunk;
+}
+
 // Splits of a row's entry chunks: enough workgroups to give every compute unit
 // about one (a workgroup's LDS fills a compute unit), never more splits than
 // chunks, and chunks spread evenly over the splits.
 int attn_splits(int R, int H, int k_plus_win) {
-  const int n_chunks = (k_plus_win + kChunk - 1) / kChunk;
+  const int ch = attn_chunk(R, H, k_plus_win);
+  const int n_chunks = (k_plus_win + ch - 1) / ch;
   if (n_chunks <= 1) return 1;
   const int64_t groups = (int64_t)R * (H > 0 ? (H + attn_group_heads(H) - 1) / attn_group_heads(H) : 1);
   int64_t want = (kAttnTargetWorkgroups + groups - 1) / groups;
@@ -464,7 +495,8 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
   a.H = L.H;
   a.Tw = L.Tw;
   a.qscale = L.sm_scale * kLog2e;
-  a.n_chunks = (L.k + L.win_max + kChunk - 1) / kChunk;
+  const int ch = attn_chunk(R, L.H, L.k + L.win_max);
+  a.n_chunks = (L.k + L.win_max + ch - 1) / ch;
   a.splits = attn_splits(R, L.H, L.k + L.win_max);
   a.chunks_per_split = (a.n_chunks + a.splits - 1) / a.splits;
   if (a.n_chunks == 0) {
@@ -484,10 +516,17 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
   const int NP = attn_group_heads(L.H) / 16;
   if (L.H % (16 * NP) != 0) return hipErrorInvalidValue;
   dim3 grid((unsigned)a.splits, (unsigned)R, (unsigned)(L.H / (16 * NP)));
-  if (NP == 2)
-    hipLaunchKernelGGL((sparse_attn_kernel<2, 4>), grid, dim3(512), 0, stream, a);
+  const bool many = (int64_t)grid.x * grid.y * grid.z > 4 * kAttnTargetWorkgroups;
+  if (NP == 2 && ch == 32 && many)
+    hipLaunchKernelGGL(sparse_attn_kernel_h32c32_2wg, grid, dim3(512), 0, stream, a);
+  else if (NP == 2 && ch == 32)
+    hipLaunchKernelGGL(sparse_attn_kernel_h32c32, grid, dim3(512), 0, stream, a);
+  else if (NP == 2)
+    hipLaunchKernelGGL(sparse_attn_kernel_h32c64, grid, dim3(512), 0, stream, a);
+  else if (ch == 32)
+    hipLaunchKernelGGL(sparse_attn_kernel_h16c32, grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((sparse_attn_kernel<1, 4>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(sparse_attn_kernel_h16c64, grid, dim3(256), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.splits == 1) return err;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)L.H, (unsigned)R), dim3(512), 0, stream, a.part_o,
