@@ -31,6 +31,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP4_MFMA_PEAK_TFLOPS = 10100.0   # dense FP4 matrix-core peak of one MI355X
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of one MI355X
+LATENT_DIM = 512
+LATENT_ROW_BYTES = 256 + 16      # MXFP4 latent row: 256 B of E2M1 codes + 16 E8M0 scales
+WINDOW_ROW_BYTES = 512           # FP8 E4M3 window row
 INDEX_KEY_BYTES = 68          # 64 B of E2M1 codes + 4 E8M0 scale bytes per cached entry
 COUNTERS = os.path.join(ROOT, "profiles", "index_scan_kernel_c3_hbm_counters.txt")
 SCAN_SOURCES = ("hierarchical_sparse_attention_csa2_amd/csrc/scan.hip",
@@ -118,6 +123,20 @@ def measured_traffic(workload):
     return float(fields["traffic_bytes_per_launch"])
 
 
+def time_back_to_back(fn, n, torch):
+    """Average ms of n calls fn(0..n-1) issued back to back between one event pair
+    on the current stream (the dispatch overhead of recording events is paid once)."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
 def capture(fn, torch):
     """One HIP graph holding the launches fn() makes on the current stream."""
     g = torch.cuda.CUDAGraph()
@@ -178,7 +197,9 @@ def main():
     reps = replicate(cache, layers, n_rep, torch)
     st = pipeline.Step(w.layers, w.B, w.M, w.N, H=w.H, n_pool=w.n_pool, k=w.k, win_max=w.win_len,
                        staged=args.staged)
-    scan_bytes = INDEX_KEY_BYTES * int(np.sum(lays_np[0]["n_visible"].astype(np.int64)))
+    visible = int(np.sum(lays_np[0]["n_visible"].astype(np.int64)))
+    scan_bytes = INDEX_KEY_BYTES * visible
+    scan_flops = 2.0 * 128 * visible
     log(f"workload {w.name}: {w.notes}; {n_rep} replica(s); scan bytes/launch {scan_bytes / 1e6:.1f} MB")
 
     for i in range(args.warmup):
@@ -217,19 +238,36 @@ def main():
     # so the per-event dispatch overhead is amortised over all of them
     for i in range(n_rep):
         run_scan(i)
-    s_start = torch.cuda.Event(enable_timing=True)
-    s_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s_start.record()
-    for i in range(args.steps):
-        run_scan(i)
-    s_end.record()
-    torch.cuda.synchronize()
-    scan_ms = s_start.elapsed_time(s_end) / args.steps
+    scan_ms = time_back_to_back(run_scan, args.steps, torch)
+    # the attention kernel alone the same way, on the first layer's selection
+    run_attn = lambda i: st.attend_only(reps[i % n_rep][0], li0[i % n_rep])
+    for i in range(n_rep):
+        run_attn(i)
+    attn_ms = time_back_to_back(run_attn, args.steps, torch)
     queries_per_step = w.R * len(w.layers)
     value = queries_per_step / (ms_per_step / 1e3)
-    achieved = scan_bytes / (scan_ms / 1e3) / 1e9
-    log(f"step {ms_per_step * 1e3:.1f} us, scan {scan_ms * 1e3:.1f} us -> {achieved:.0f} GB/s")
+    if w.M < 16:
+        # decode: the scan streams every visible entry's 68 index-key bytes once
+        scan_roof = {"kernel": "index_scan_kernel", "bound": "hbm", "achieved": scan_bytes / (scan_ms / 1e3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": measured_traffic(args.workload),
+                     "traffic_unit": "bytes/launch", "algorithmic_bytes_per_launch": scan_bytes}
+    else:
+        # prefill: 2 x 128 FP4 products per (query, visible entry) pair on the matrix cores
+        scan_roof = {"kernel": "prefill_scan_kernel", "bound": "mfma",
+                     "achieved": scan_flops / (scan_ms / 1e3) / 1e12, "peak": FP4_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "traffic": None, "algorithmic_flops_per_launch": scan_flops}
+    scan_roof["frac"] = scan_roof["achieved"] / scan_roof["peak"]
+    scan_roof["avg_launch_us"] = scan_ms * 1e3
+    attn_rows = w.k + w.win_len
+    attn_flops = 4.0 * w.R * w.H * attn_rows * LATENT_DIM
+    attn_bytes = w.R * (w.k * LATENT_ROW_BYTES + w.win_len * WINDOW_ROW_BYTES + 2 * w.H * LATENT_DIM * 4)
+    attn = {"kernel": "sparse_attn_kernel + attn_combine_kernel", "avg_launch_us": attn_ms * 1e3,
+            "algorithmic_flops": attn_flops, "tflops": attn_flops / (attn_ms / 1e3) / 1e12,
+            "frac_bf16_mfma": attn_flops / (attn_ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "algorithmic_bytes": attn_bytes, "gbs": attn_bytes / (attn_ms / 1e3) / 1e9,
+            "frac_hbm": attn_bytes / (attn_ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+    log(f"step {ms_per_step * 1e3:.1f} us, scan {scan_ms * 1e3:.1f} us -> {scan_roof['achieved']:.0f} "
+        f"{scan_roof['unit']}, attention {attn_ms * 1e3:.1f} us -> {attn['tflops']:.0f} TFLOP/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -255,12 +293,8 @@ def main():
             "block": 8, "pool_blocks": w.n_pool, "top_k": w.k, "window": w.win_len, "heads": w.H,
             "replicas_in_rotation": n_rep, "launch": "hip_graph_replay" if args.graph else "eager",
         },
-        "roofline": {
-            "kernel": "index_scan_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
-            "traffic_unit": "bytes/launch",
-            "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": scan_ms * 1e3,
-        },
+        "roofline": scan_roof,
+        "attention": attn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

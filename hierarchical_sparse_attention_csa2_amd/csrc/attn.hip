@@ -14,8 +14,9 @@
 // Workgroup = (split, row, head group of 32): 8 waves.  Four waves own 16 heads;
 // each keeps the query (hi/lo) and the output accumulator O^T for its quarter of
 // the 512 dims in registers, and the four partial S^T tiles are summed through
-// LDS in a fixed order.  Entries stream through LDS in chunks of 64: each chunk is decoded
-// once into a row-major copy (operand A of S^T = C Q^T) and a transposed copy
+// LDS in a fixed order.  Entries stream through LDS in chunks of 32 or 64: each
+// chunk's rows are gathered into registers one chunk ahead, then decoded once
+// into a row-major copy (operand A of S^T = C Q^T) and a transposed copy
 // (operand A of O^T = C^T P^T).  S^T's accumulator layout gives each lane the
 // probabilities of exactly the entries it must feed as operand B of the second
 // product, so P never leaves registers.  An online softmax (log2 domain) runs
@@ -78,68 +79,112 @@ __device__ __forceinline__ bf16x8_t decode_fp8x8(uint32_t w0, uint32_t w1) {
                   (__bf16)f2[0], (__bf16)f2[1], (__bf16)f3[0], (__bf16)f3[1]};
 }
 
-// Decode one chunk (64 entries x 512 dims) into the row-major and the
-// transposed LDS copies.  Thread tiles are 4 entries x 8 dims; for chunks of a
-// single row kind every gather of the thread is issued before any conversion.
-template <int NT, int KIND, int CH>
-__device__ __forceinline__ void decode_chunk(const AttnParams& a, const int64_t* sOff, const int* sType,
-                                             unsigned long long vmask, __bf16* sK, __bf16* sVt, int tid) {
-  constexpr int kVLd = vld<CH>();
-  constexpr int kEG = CH / 4;                     // entry groups of 4
-  constexpr int kTPT = kEG * 64 / NT;             // tiles per thread
-  constexpr int kGroup = kTPT;                            // every tile's gathers in flight together
+// A thread covers 4 consecutive entries of a chunk (4*eg .. 4*eg+3, the same
+// four in every tile it owns) and 8 dims of each per tile (dims 8*dg .. +8).
+// Its entries' raw bytes are gathered into registers one chunk ahead of the
+// decode, so a chunk's row loads are in flight during the previous chunk's
+// products.
+template <int CH, int NT>
+struct Gathered {
+  static constexpr int kEG = CH / 4;            // entry groups of 4
+  static constexpr int kTPT = kEG * 64 / NT;    // tiles per thread
+  uint32_t w0[kTPT][4], w1[kTPT][4];            // latent: 4 code bytes, scale byte; window: 8 bytes
+};
+
+// Selected indices of this thread's entries of the chunk at ebase (-1 beyond k).
+__device__ __forceinline__ void load_entry_ids(const AttnParams& a, int r, int ebase, int eg, int32_t (&ix)[4]) {
 #pragma unroll
-  for (int j0 = 0; j0 < kTPT; j0 += kGroup) {
-    uint32_t raw0[kGroup][4], raw1[kGroup][4];
+  for (int i = 0; i < 4; ++i) {
+    const int e = ebase + 4 * eg + i;
+    ix[i] = e < a.k ? a.idx[(int64_t)r * a.k + e] : -1;
+  }
+}
+
+// Row offsets of this thread's entries (latent row seq*N_max + p, window row
+// seq*Tw + t) and their validity bits (bit i: entry 4*eg + i).
+__device__ __forceinline__ uint32_t entry_rows(const AttnParams& a, int64_t seq, int ws0, int E, int ebase, int eg,
+                                               const int32_t (&ix)[4], int64_t (&off)[4]) {
+  uint32_t vb = 0u;
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      const int T = tid + (j0 + j) * NT;
-      const int eg = T % kEG, dg = T / kEG;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t off = sOff[4 * eg + i];
-        if (KIND == kLatentRows) {
-          raw0[j][i] = *reinterpret_cast<const uint32_t*>(a.c_codes + off * 256 + 4 * dg);
-          raw1[j][i] = a.c_scales[off * 16 + (dg >> 2)];
-        } else if (KIND == kWindowRows) {
-          const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(a.win + off * 512 + 8 * dg);
-          raw0[j][i] = wb[0];
-          raw1[j][i] = wb[1];
-        }
-      }
+  for (int i = 0; i < 4; ++i) {
+    const int e = ebase + 4 * eg + i;
+    bool valid;
+    if (e < a.k) {
+      const int64_t p = ix[i];
+      valid = p >= 0 && p < a.N_max;
+      off[i] = seq * a.N_max + p;
+    } else {
+      const int64_t t = (int64_t)ws0 + (e - a.k);
+      valid = e < E && t >= 0 && t < a.Tw;
+      off[i] = seq * a.Tw + t;
     }
+    vb |= valid ? 1u << i : 0u;
+  }
+  return vb;
+}
+
+// Issue the loads of this thread's valid entries (invalid ones read nothing).
+template <int NT, int KIND, int CH>
+__device__ __forceinline__ void gather_chunk(const AttnParams& a, const int64_t (&off)[4], uint32_t vb, int ebase,
+                                             int tid, Gathered<CH, NT>& g) {
+  constexpr int kEG = Gathered<CH, NT>::kEG;
+  const int eg = tid % kEG;
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      const int T = tid + (j0 + j) * NT;
-      const int eg = T % kEG, dg = T / kEG;
-      bf16x8_t v[4];
+  for (int j = 0; j < Gathered<CH, NT>::kTPT; ++j) {
+    const int dg = (tid + j * NT) / kEG;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * eg + i;
-        if (!((vmask >> e) & 1ull)) {
-          v[i] = zero_bf16x8();
-        } else if (KIND == kLatentRows) {
-          v[i] = decode_latent8(raw0[j][i], raw1[j][i]);
-        } else if (KIND == kWindowRows) {
-          v[i] = decode_fp8x8(raw0[j][i], raw1[j][i]);
+    for (int i = 0; i < 4; ++i) {
+      uint32_t x0 = 0u, x1 = 0u;
+      if ((vb >> i) & 1u) {
+        const bool lat = KIND == kLatentRows || (KIND == kMixedRows && ebase + 4 * eg + i < a.k);
+        if (lat) {
+          x0 = *reinterpret_cast<const uint32_t*>(a.c_codes + off[i] * 256 + 4 * dg);
+          x1 = a.c_scales[off[i] * 16 + (dg >> 2)];
         } else {
-          const int64_t off = sOff[e];
-          if (sType[e] == 0) {
-            v[i] = decode_latent8(*reinterpret_cast<const uint32_t*>(a.c_codes + off * 256 + 4 * dg),
-                                  a.c_scales[off * 16 + (dg >> 2)]);
-          } else {
-            const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(a.win + off * 512 + 8 * dg);
-            v[i] = decode_fp8x8(wb[0], wb[1]);
-          }
+          const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(a.win + off[i] * 512 + 8 * dg);
+          x0 = wb[0];
+          x1 = wb[1];
         }
-        *reinterpret_cast<bf16x8_t*>(&sK[e * kKLd + 8 * dg]) = v[i];
       }
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-        *reinterpret_cast<bf16x4_t*>(&sVt[(8 * dg + d) * kVLd + 4 * eg]) =
-            bf16x4_t{v[0][d], v[1][d], v[2][d], v[3][d]};
+      g.w0[j][i] = x0;
+      g.w1[j][i] = x1;
     }
   }
+}
+
+// Decode the gathered bytes (zeros for invalid entries) into the row-major and
+// the transposed LDS copies.
+template <int NT, int KIND, int CH>
+__device__ __forceinline__ void store_chunk(const AttnParams& a, const Gathered<CH, NT>& g, uint32_t vb, int ebase,
+                                            int tid, __bf16* sK, __bf16* sVt) {
+  constexpr int kVLd = vld<CH>();
+  constexpr int kEG = Gathered<CH, NT>::kEG;
+  const int eg = tid % kEG;
+#pragma unroll
+  for (int j = 0; j < Gathered<CH, NT>::kTPT; ++j) {
+    const int dg = (tid + j * NT) / kEG;
+    bf16x8_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * eg + i;
+      const bool lat = KIND == kLatentRows || (KIND == kMixedRows && ebase + e < a.k);
+      if (!((vb >> i) & 1u))
+        v[i] = zero_bf16x8();
+      else if (lat)
+        v[i] = decode_latent8(g.w0[j][i], g.w1[j][i]);
+      else
+        v[i] = decode_fp8x8(g.w0[j][i], g.w1[j][i]);
+      *reinterpret_cast<bf16x8_t*>(&sK[e * kKLd + 8 * dg]) = v[i];
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      *reinterpret_cast<bf16x4_t*>(&sVt[(8 * dg + d) * kVLd + 4 * eg]) = bf16x4_t{v[0][d], v[1][d], v[2][d], v[3][d]};
+  }
+}
+
+// The chunk's row kind (uniform over the workgroup).
+__device__ __forceinline__ int chunk_kind(int ebase, int CHn, int k) {
+  return ebase + CHn <= k ? kLatentRows : (ebase >= k ? kWindowRows : kMixedRows);
 }
 
 // NP head groups of 16 per workgroup, ND waves per head group (each 512/ND
@@ -157,9 +202,6 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   static_assert(NP * ND * 64 * kT * 16 <= kChunk * kKLd * 2, "S^T partials fit in the row-major copy");
   __shared__ __attribute__((aligned(16))) __bf16 sK[kChunk * kKLd];
   __shared__ __attribute__((aligned(16))) __bf16 sVt[512 * kVLd];
-  __shared__ int64_t sOff[kChunk];
-  __shared__ int sType[kChunk];
-  __shared__ unsigned long long sMask;
 
   const int split = blockIdx.x;
   const int r = blockIdx.y;
@@ -173,6 +215,8 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   const int g = lane >> 4;     // lane group 0..3
   const int hl = lane & 15;
   const int h = 16 * NP * blockIdx.z + 16 * pr + hl;   // head groups of 16*NP heads across blockIdx.z
+  constexpr int kEG = Gathered<CH, NT>::kEG;
+  const int eg = tid % kEG;    // this thread's entry group (lanes 0..kEG-1 of every wave: groups 0..kEG-1)
 
   int wl = a.win_max > 0 ? a.win_len[r] : 0;
   wl = wl < 0 ? 0 : (wl > a.win_max ? a.win_max : wl);
@@ -183,14 +227,30 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   int c_end = c_begin + a.chunks_per_split;
   c_end = c_end < a.n_chunks ? c_end : a.n_chunks;
 
-  // The first chunk's selected indices load first (the entry table waits on
-  // them alone: the memory counter retires loads in order), then the query.
-  // The query is converted to bf16 hi/lo after the first chunk's gathers are in
-  // flight, so its load stays off the index -> gather -> decode path.
-  int64_t idx_next = -1;
-  if (tid < kChunk && c_begin < c_end) {
-    const int e = c_begin * kChunk + tid;
-    if (e < a.k) idx_next = a.idx[(int64_t)r * a.k + e];
+  // The first two chunks' selected indices load first, then the query; the
+  // first chunk's rows are gathered as soon as its indices arrive.  The query
+  // is converted to bf16 hi/lo after that, off the index -> gather -> decode path.
+  int32_t ix_next[4];
+  Gathered<CH, NT> gr;
+  uint32_t vb = 0u;       // validity of this thread's entries of the gathered chunk
+  uint32_t bm[4] = {0u, 0u, 0u, 0u};   // bit q of bm[i]: entry 4q + i of the gathered chunk is valid
+  {
+    int32_t ix0[4];
+    load_entry_ids(a, r, c_begin * kChunk, eg, ix0);
+    load_entry_ids(a, r, (c_begin + 1) * kChunk, eg, ix_next);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c_begin < c_end) {
+      int64_t off[4];
+      const int eb = c_begin * kChunk;
+      vb = entry_rows(a, seq, ws0, E, eb, eg, ix0, off);
+      const int kind = chunk_kind(eb, kChunk, a.k);
+      if (kind == kLatentRows)
+        gather_chunk<NT, kLatentRows, CH>(a, off, vb, eb, tid, gr);
+      else if (kind == kWindowRows)
+        gather_chunk<NT, kWindowRows, CH>(a, off, vb, eb, tid, gr);
+      else
+        gather_chunk<NT, kMixedRows, CH>(a, off, vb, eb, tid, gr);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   f32x4 qraw[2 * kS];
@@ -228,43 +288,40 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   for (int c = c_begin; c < c_end; ++c) {
     const int ebase = c * kChunk;
     if (ebase >= E) break;
-    __syncthreads();   // previous chunk's LDS reads are done
-    // 1. entry table
-    if (tid < kChunk) {
-      // masked entries keep a readable row (the sequence's first) and are zeroed
-      const int e = ebase + tid;
-      const int type = e < a.k ? 0 : 1;
-      int64_t off = type == 0 ? seq * a.N_max : seq * a.Tw;
-      bool valid = false;
-      const int64_t p = idx_next;
-      // prefetch the next chunk's indices
-      idx_next = -1;
-      if (c + 1 < c_end && e + kChunk < a.k) idx_next = a.idx[(int64_t)r * a.k + e + kChunk];
-      if (e < a.k) {
-        valid = p >= 0 && p < a.N_max;
-        if (valid) off += p;
-      } else if (e < E) {
-        const int64_t t = (int64_t)ws0 + (e - a.k);
-        valid = t >= 0 && t < a.Tw;
-        if (valid) off += t;
-      }
-      sOff[tid] = off;
-      sType[tid] = type;
-      const unsigned long long m = __ballot(valid);
-      if (tid == 0) sMask = m;
+    // this chunk's validity (the same in every wave: lanes 0..kEG-1 hold groups 0..kEG-1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      bm[i] = (uint32_t)__ballot((vb >> i) & 1u) & (kEG == 32 ? 0xFFFFFFFFu : ((1u << kEG) - 1u));
+    const bool any = (bm[0] | bm[1] | bm[2] | bm[3]) != 0u;
+    if (any) {
+      __syncthreads();   // previous chunk's LDS reads are done
+      const int kind = chunk_kind(ebase, kChunk, a.k);
+      if (kind == kLatentRows)
+        store_chunk<NT, kLatentRows, CH>(a, gr, vb, ebase, tid, sK, sVt);
+      else if (kind == kWindowRows)
+        store_chunk<NT, kWindowRows, CH>(a, gr, vb, ebase, tid, sK, sVt);
+      else
+        store_chunk<NT, kMixedRows, CH>(a, gr, vb, ebase, tid, sK, sVt);
+      __syncthreads();
     }
-    __syncthreads();
-    const unsigned long long vmask = sMask;
-    if (vmask == 0ull) continue;
-
-    // 2. decode 4 entries x 8 dims per tile into both LDS copies
-    if (ebase + kChunk <= a.k)
-      decode_chunk<NT, kLatentRows, CH>(a, sOff, sType, vmask, sK, sVt, tid);
-    else if (ebase >= a.k)
-      decode_chunk<NT, kWindowRows, CH>(a, sOff, sType, vmask, sK, sVt, tid);
-    else
-      decode_chunk<NT, kMixedRows, CH>(a, sOff, sType, vmask, sK, sVt, tid);
-    __syncthreads();
+    const uint32_t bmc[4] = {bm[0], bm[1], bm[2], bm[3]};
+    // the next chunk's rows, then the indices of the one after
+    if (c + 1 < c_end && ebase + kChunk < E) {
+      int64_t off[4];
+      const int eb = ebase + kChunk;
+      vb = entry_rows(a, seq, ws0, E, eb, eg, ix_next, off);
+      const int kind = chunk_kind(eb, kChunk, a.k);
+      if (kind == kLatentRows)
+        gather_chunk<NT, kLatentRows, CH>(a, off, vb, eb, tid, gr);
+      else if (kind == kWindowRows)
+        gather_chunk<NT, kWindowRows, CH>(a, off, vb, eb, tid, gr);
+      else
+        gather_chunk<NT, kMixedRows, CH>(a, off, vb, eb, tid, gr);
+      if (c + 2 < c_end) load_entry_ids(a, r, eb + kChunk, eg, ix_next);
+    } else {
+      vb = 0u;
+    }
+    if (!any) continue;
 
     if (!q_ready) convert_query();
 
@@ -306,8 +363,8 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
     for (int t = 0; t < kT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int e = 16 * t + 4 * g + i;
-        if (!((vmask >> e) & 1ull)) sacc[t][i] = -__builtin_inff();
+        // entry 16t + 4g + i: group 4t + g, member i
+        if (!((bmc[i] >> (4 * t + g)) & 1u)) sacc[t][i] = -__builtin_inff();
         mloc = fmaxf(mloc, sacc[t][i]);
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
@@ -384,11 +441,12 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel_h16c32(AttnParams a) {
 __global__ __launch_bounds__(256, 1) void sparse_attn_kernel_h16c64(AttnParams a) { sparse_attn_body<1, 4, 64>(a); }
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One workgroup per (row, head), one thread per output dim.  The splits' (m, l)
-// pairs are read once into LDS and turned into weights there; each thread then
-// reads only its own dim of every split's o, kCombineGroup loads in flight.
+// One workgroup per (row, head), one thread per output dim.  Wave 0 reads the
+// splits' (m, l) pairs and turns them into weights in LDS; every thread's own
+// dim of the first kCombineGroup splits' o is loaded before that, so the
+// weights and the partials arrive in one memory round trip.
 constexpr int kMaxSplits = kAttnTargetWorkgroups;   // attn_splits never exceeds it
-constexpr int kCombineGroup = 8;
+constexpr int kCombineGroup = 32;
 
 __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, int splits, int H,
@@ -399,10 +457,8 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restri
   const int h = blockIdx.x;
   const int d = threadIdx.x;
   const int64_t base = (int64_t)r * splits * H + h;     // slot of split s: base + s*H
+  float m[kMaxSplits / 64], l[kMaxSplits / 64];
   if (threadIdx.x < 64) {
-    // wave 0: M = max_s m_s, then the weights and L = sum_s w_s l_s in split order
-    float m[kMaxSplits / 64], l[kMaxSplits / 64];
-    float M = -__builtin_inff();
 #pragma unroll
     for (int j = 0; j < kMaxSplits / 64; ++j) {
       const int sidx = 64 * j + threadIdx.x;
@@ -412,11 +468,19 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restri
         m[j] = part_ml[2 * (base + (int64_t)sidx * H)];
         l[j] = part_ml[2 * (base + (int64_t)sidx * H) + 1];
       }
-      M = fmaxf(M, m[j]);
     }
+  }
+  float ov[kCombineGroup];
+#pragma unroll
+  for (int j = 0; j < kCombineGroup; ++j) ov[j] = j < splits ? part_o[(base + (int64_t)j * H) * 512 + d] : 0.f;
+  if (threadIdx.x < 64) {
+    // wave 0: M = max_s m_s, then the weights and L = sum_s w_s l_s in split order
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < kMaxSplits / 64; ++j) M = fmaxf(M, m[j]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    // L = sum_s w_s l_s: per lane in j order, then a fixed butterfly
+    // L: per lane in j order, then a fixed butterfly
     float L = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxSplits / 64; ++j) {
@@ -432,10 +496,11 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restri
   __syncthreads();
   float acc = 0.f;
   for (int s0 = 0; s0 < splits; s0 += kCombineGroup) {
-    float ov[kCombineGroup];
+    if (s0 > 0) {
 #pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j)
-      ov[j] = s0 + j < splits ? part_o[(base + (int64_t)(s0 + j) * H) * 512 + d] : 0.f;
+      for (int j = 0; j < kCombineGroup; ++j)
+        ov[j] = s0 + j < splits ? part_o[(base + (int64_t)(s0 + j) * H) * 512 + d] : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < kCombineGroup; ++j)
       if (s0 + j < splits) acc += sw[s0 + j] * ov[j];

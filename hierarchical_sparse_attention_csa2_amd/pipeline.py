@@ -102,6 +102,10 @@ class Step:
         csa2_index_scan(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, self.B, self.M,
                         self.N, self.block_max, scores=self.scores, super_max=self.super_max)
 
+    def attend_only(self, cache: Cache, li: LayerInputs):
+        """The first layer's attention alone, over its last selection."""
+        self.attend(cache, li, self.idx[0], self.out[0])
+
     def reindex(self, cache: Cache, li: LayerInputs, idx: torch.Tensor):
         csa2_index_pool(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, self.pool, li.n_visible,
                         self.B, self.M, self.N, self.pool_scores)
