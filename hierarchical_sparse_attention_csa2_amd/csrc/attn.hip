@@ -15,23 +15,34 @@
 // each keeps the query (hi/lo) and the output accumulator O^T for its quarter of
 // the 512 dims in registers, and the four partial S^T tiles are summed through
 // LDS in a fixed order.  Entries stream through LDS in chunks of 32 or 64: each
-// chunk's rows are gathered into registers one chunk ahead, then decoded once
-// into a row-major copy (operand A of S^T = C Q^T) and a transposed copy
-// (operand A of O^T = C^T P^T).  S^T's accumulator layout gives each lane the
-// probabilities of exactly the entries it must feed as operand B of the second
-// product, so P never leaves registers.  An online softmax (log2 domain) runs
-// across chunks; splits > 1 write partial (o, m, l) that a combine kernel merges.
+// chunk's rows are gathered whole (one row per wave load) into registers one
+// chunk ahead, then decoded once into a row-major LDS copy.  That copy is
+// operand A of S^T = C Q^T as is, and operand A of O^T = C^T P^T through the
+// transposing LDS reads of gfx950, so no transposed copy is written.  S^T's
+// accumulator layout gives each lane the probabilities of exactly the entries
+// it must feed as operand B of the second product, so P never leaves
+// registers.  An online softmax (log2 domain) runs across chunks; splits > 1
+// write partial (o, m, l) that a combine kernel merges.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace csa2 {
 
-constexpr int kKLd = 512 + 8;              // bf16 row stride of the row-major copy
-template <int CH>
-constexpr int vld() { return CH + 8; }     // bf16 row stride of the transposed copy
+constexpr int kKLd = 512 + 16;             // bf16 row stride of the row-major copy (two chunks of padding)
+constexpr float kLazyRescale = 8.0f;       // log2 growth of a running maximum that forces a rescale
+
+// The row-major copy stores 16-byte chunk c of entry row e at chunk
+// c ^ ((e >> 2) & 1) of a row padded by two chunks, so rows 0..3 of an aligned
+// four start 0, 2, 4, 6 chunks apart (mod 8) and rows 4..7 one chunk further.
+// Row writes (8 lanes: one row, 8 chunks), S^T operand reads (8 lanes: rows
+// 0..7 mod 8, one chunk) and transposing reads (16 lanes: 4 rows aligned to 4,
+// two adjacent chunks) each touch 32 distinct banks, and a lane's addresses
+// differ only by constants across its K steps and dim tiles.
+__device__ __forceinline__ int kofs(int e, int dim, int x) { return e * kKLd + (((dim >> 3) ^ x) << 3) + (dim & 7); }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kAttnTargetWorkgroups = 256;   // one per compute unit
 constexpr int kAttnChunk = 32;
+constexpr int kIdxCap = 1024;                 // staged indices per workgroup (splits keep within it)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -59,8 +70,6 @@ __device__ __forceinline__ bf16x8_t zero_bf16x8() {
   return z;
 }
 
-enum { kLatentRows = 0, kWindowRows = 1, kMixedRows = 2 };
-
 __device__ __forceinline__ bf16x8_t decode_latent8(uint32_t wcode, uint32_t scale_byte) {
   const float sc = e8m0_to_f32(scale_byte);
   const bf16x2_t p0 = fp4x2_to_bf16<0>(wcode, sc);
@@ -79,69 +88,64 @@ __device__ __forceinline__ bf16x8_t decode_fp8x8(uint32_t w0, uint32_t w1) {
                   (__bf16)f2[0], (__bf16)f2[1], (__bf16)f3[0], (__bf16)f3[1]};
 }
 
-// A thread covers 4 consecutive entries of a chunk (4*eg .. 4*eg+3, the same
-// four in every tile it owns) and 8 dims of each per tile (dims 8*dg .. +8).
-// Its entries' raw bytes are gathered into registers one chunk ahead of the
-// decode, so a chunk's row loads are in flight during the previous chunk's
-// products.
-template <int CH, int NT>
-struct Gathered {
-  static constexpr int kEG = CH / 4;            // entry groups of 4
-  static constexpr int kTPT = kEG * 64 / NT;    // tiles per thread
-  uint32_t w0[kTPT][4], w1[kTPT][4];            // latent: 4 code bytes, scale byte; window: 8 bytes
+// Entry rows of a chunk: lane l of every wave resolves entry l % CH (its row
+// offset and validity), so a ballot gives the chunk's validity mask and any
+// wave can read an entry's row offset from that lane.
+struct EntryRow {
+  int64_t off;   // latent row seq*N_max + p, or window row seq*Tw + t
+  bool valid;
 };
 
-// Selected indices of this thread's entries of the chunk at ebase (-1 beyond k).
-__device__ __forceinline__ void load_entry_ids(const AttnParams& a, int r, int ebase, int eg, int32_t (&ix)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = ebase + 4 * eg + i;
-    ix[i] = e < a.k ? a.idx[(int64_t)r * a.k + e] : -1;
+__device__ __forceinline__ EntryRow entry_row(const AttnParams& a, int64_t seq, int ws0, int E, int e, int32_t p) {
+  EntryRow x;
+  if (e < a.k) {
+    x.valid = p >= 0 && p < a.N_max;
+    x.off = seq * a.N_max + (x.valid ? p : 0);
+  } else {
+    const int64_t t = (int64_t)ws0 + (e - a.k);
+    x.valid = e < E && t >= 0 && t < a.Tw;
+    x.off = seq * a.Tw + (x.valid ? t : 0);
   }
+  return x;
 }
 
-// Row offsets of this thread's entries (latent row seq*N_max + p, window row
-// seq*Tw + t) and their validity bits (bit i: entry 4*eg + i).
-__device__ __forceinline__ uint32_t entry_rows(const AttnParams& a, int64_t seq, int ws0, int E, int ebase, int eg,
-                                               const int32_t (&ix)[4], int64_t (&off)[4]) {
-  uint32_t vb = 0u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = ebase + 4 * eg + i;
-    bool valid;
-    if (e < a.k) {
-      const int64_t p = ix[i];
-      valid = p >= 0 && p < a.N_max;
-      off[i] = seq * a.N_max + p;
-    } else {
-      const int64_t t = (int64_t)ws0 + (e - a.k);
-      valid = e < E && t >= 0 && t < a.Tw;
-      off[i] = seq * a.Tw + t;
-    }
-    vb |= valid ? 1u << i : 0u;
-  }
-  return vb;
+// A wave gathers whole rows: per tile it takes 4 entries (4*eg .. 4*eg+3, eg
+// uniform over the wave) and lane l their dims 8l .. 8l+7, so one load
+// instruction reads one 256-byte latent (or 512-byte window) row.  The bytes
+// stay in registers until the chunk is decoded, one chunk later.
+template <int CH, int NT>
+struct Gathered {
+  static constexpr int kTPT = CH * 16 / NT;   // 4-entry tiles per thread
+  uint32_t w0[kTPT][4], w1[kTPT][4];          // latent: 4 code bytes, scale byte; window: 8 bytes
+};
+
+// One gathered row as a buffer resource (scalar registers: the row's base and
+// its byte length), read at the lane's 32-bit offset: the per-lane address
+// needs no 64-bit register pair, and a read past the row returns zero.
+constexpr int kBufferConfig = 0x00020000;   // gfx9 buffer descriptor word 3 for raw dword loads
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* row, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(row), 0, bytes, kBufferConfig);
 }
 
-// Issue the loads of this thread's valid entries (invalid ones read nothing).
-template <int NT, int KIND, int CH>
-__device__ __forceinline__ void gather_chunk(const AttnParams& a, const int64_t (&off)[4], uint32_t vb, int ebase,
-                                             int tid, Gathered<CH, NT>& g) {
-  constexpr int kEG = Gathered<CH, NT>::kEG;
-  const int eg = tid % kEG;
+template <int CH, int NT>
+__device__ __forceinline__ void gather_chunk(const AttnParams& a, int64_t off, uint64_t mask, int ebase, int w,
+                                             int lane, Gathered<CH, NT>& g) {
+  const int off_lo = (int)(uint32_t)off, off_hi = (int)(off >> 32);
 #pragma unroll
   for (int j = 0; j < Gathered<CH, NT>::kTPT; ++j) {
-    const int dg = (tid + j * NT) / kEG;
+    const int eg = w + j * (NT / 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int e = 4 * eg + i;
+      const int64_t o = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(off_hi, e) << 32) |
+                                  (uint32_t)__builtin_amdgcn_readlane(off_lo, e));
       uint32_t x0 = 0u, x1 = 0u;
-      if ((vb >> i) & 1u) {
-        const bool lat = KIND == kLatentRows || (KIND == kMixedRows && ebase + 4 * eg + i < a.k);
-        if (lat) {
-          x0 = *reinterpret_cast<const uint32_t*>(a.c_codes + off[i] * 256 + 4 * dg);
-          x1 = a.c_scales[off[i] * 16 + (dg >> 2)];
+      if ((mask >> e) & 1ull) {
+        if (ebase + e < a.k) {
+          x0 = __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(a.c_codes + o * 256, 256), 4 * lane, 0, 0);
+          x1 = __builtin_amdgcn_raw_buffer_load_b8(row_rsrc(a.c_scales + o * 16, 16), lane >> 2, 0, 0);
         } else {
-          const u32x2_t wb = *reinterpret_cast<const u32x2_t*>(a.win + off[i] * 512 + 8 * dg);
+          const u32x2_t wb = __builtin_amdgcn_raw_buffer_load_b64(row_rsrc(a.win + o * 512, 512), 8 * lane, 0, 0);
           x0 = wb[0];
           x1 = wb[1];
         }
@@ -152,39 +156,32 @@ __device__ __forceinline__ void gather_chunk(const AttnParams& a, const int64_t 
   }
 }
 
-// Decode the gathered bytes (zeros for invalid entries) into the row-major and
-// the transposed LDS copies.
-template <int NT, int KIND, int CH>
-__device__ __forceinline__ void store_chunk(const AttnParams& a, const Gathered<CH, NT>& g, uint32_t vb, int ebase,
-                                            int tid, __bf16* sK, __bf16* sVt) {
-  constexpr int kVLd = vld<CH>();
-  constexpr int kEG = Gathered<CH, NT>::kEG;
-  const int eg = tid % kEG;
+// Decode the gathered bytes (zeros for invalid entries) into the row-major
+// LDS copy: lane l writes dims 8l .. 8l+7 of each of its entries.
+template <int CH, int NT>
+__device__ __forceinline__ void store_chunk(const AttnParams& a, const Gathered<CH, NT>& g, uint64_t mask,
+                                            int ebase, int w, int lane, __bf16* sK) {
 #pragma unroll
   for (int j = 0; j < Gathered<CH, NT>::kTPT; ++j) {
-    const int dg = (tid + j * NT) / kEG;
-    bf16x8_t v[4];
+    const int eg = w + j * (NT / 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * eg + i;
-      const bool lat = KIND == kLatentRows || (KIND == kMixedRows && ebase + e < a.k);
-      if (!((vb >> i) & 1u))
-        v[i] = zero_bf16x8();
-      else if (lat)
-        v[i] = decode_latent8(g.w0[j][i], g.w1[j][i]);
-      else
-        v[i] = decode_fp8x8(g.w0[j][i], g.w1[j][i]);
-      *reinterpret_cast<bf16x8_t*>(&sK[e * kKLd + 8 * dg]) = v[i];
+      bf16x8_t v = zero_bf16x8();
+      if ((mask >> e) & 1ull)
+        v = ebase + e < a.k ? decode_latent8(g.w0[j][i], g.w1[j][i]) : decode_fp8x8(g.w0[j][i], g.w1[j][i]);
+      *reinterpret_cast<bf16x8_t*>(&sK[kofs(e, 8 * lane, (e >> 2) & 1)]) = v;
     }
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-      *reinterpret_cast<bf16x4_t*>(&sVt[(8 * dg + d) * kVLd + 4 * eg]) = bf16x4_t{v[0][d], v[1][d], v[2][d], v[3][d]};
   }
 }
 
-// The chunk's row kind (uniform over the workgroup).
-__device__ __forceinline__ int chunk_kind(int ebase, int CHn, int k) {
-  return ebase + CHn <= k ? kLatentRows : (ebase >= k ? kWindowRows : kMixedRows);
+// Four bf16 of a transposed 16x4 tile: in each 16-lane group, lane i receives
+// element i % 4 of the 8 bytes that lane 4x + i / 4 addresses, in slot x.
+__device__ __forceinline__ bf16x4_t lds_read_tr4(const __bf16* p) {
+  typedef __bf16 bf16v4 __attribute__((vector_size(8)));
+  typedef __attribute__((address_space(3))) bf16v4 lds_bf16v4;
+  const bf16v4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16v4*)(p));
+  return bf16x4_t{v[0], v[1], v[2], v[3]};
 }
 
 // NP head groups of 16 per workgroup, ND waves per head group (each 512/ND
@@ -192,31 +189,31 @@ __device__ __forceinline__ int chunk_kind(int ebase, int CHn, int k) {
 template <int NP, int ND, int CH>
 __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   constexpr int kChunk = CH;
-  constexpr int kVLd = vld<CH>();
   constexpr int NT = NP * ND * 64;
   constexpr int kDims = 512 / ND;     // dims per wave
   constexpr int kS = kDims / 32;      // K steps of S^T
   constexpr int kM = kDims / 16;      // dim tiles of O^T
   constexpr int kT = CH / 16;         // entry tiles of S^T
   constexpr int kJ = CH / 32;         // K steps of O^T
-  static_assert(NP * ND * 64 * kT * 16 <= kChunk * kKLd * 2, "S^T partials fit in the row-major copy");
+  constexpr uint64_t kChunkBits = CH == 64 ? ~0ull : ((1ull << CH) - 1ull);
+  static_assert(CH == 32 || CH == 64, "chunk of 32 or 64 entries");
   __shared__ __attribute__((aligned(16))) __bf16 sK[kChunk * kKLd];
-  __shared__ __attribute__((aligned(16))) __bf16 sVt[512 * kVLd];
+  __shared__ f32x4 sX[NP * ND * 64 * kT];   // partial S^T tiles of the ND waves of each head group
+  __shared__ int32_t sIdx[kIdxCap];         // the split's selected indices after its first chunk
 
   const int split = blockIdx.x;
   const int r = blockIdx.y;
   const int64_t seq = r / a.M;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pr = w % NP;       // head group of 16
   const int part = w / NP;     // dims [kDims * part, kDims * (part + 1))
   const int dbase = kDims * part;
   const int g = lane >> 4;     // lane group 0..3
   const int hl = lane & 15;
   const int h = 16 * NP * blockIdx.z + 16 * pr + hl;   // head groups of 16*NP heads across blockIdx.z
-  constexpr int kEG = Gathered<CH, NT>::kEG;
-  const int eg = tid % kEG;    // this thread's entry group (lanes 0..kEG-1 of every wave: groups 0..kEG-1)
+  const int le = lane % kChunk;                          // this lane's entry of a chunk
 
   int wl = a.win_max > 0 ? a.win_len[r] : 0;
   wl = wl < 0 ? 0 : (wl > a.win_max ? a.win_max : wl);
@@ -227,57 +224,56 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   int c_end = c_begin + a.chunks_per_split;
   c_end = c_end < a.n_chunks ? c_end : a.n_chunks;
 
-  // The first two chunks' selected indices load first, then the query; the
-  // first chunk's rows are gathered as soon as its indices arrive.  The query
-  // is converted to bf16 hi/lo after that, off the index -> gather -> decode path.
-  int32_t ix_next[4];
+  // The first chunk's indices load first and its rows are gathered as soon as
+  // they arrive; later chunks' indices are staged in LDS (visible after the
+  // first chunk's decode barrier), so no chunk waits on a global index load in
+  // the loop.  The query loads after the first gathers.
   Gathered<CH, NT> gr;
-  uint32_t vb = 0u;       // validity of this thread's entries of the gathered chunk
-  uint32_t bm[4] = {0u, 0u, 0u, 0u};   // bit q of bm[i]: entry 4q + i of the gathered chunk is valid
+  uint64_t mask = 0ull;   // validity of the gathered chunk's entries (uniform)
+  const int staged0 = (c_begin + 1) * kChunk;                         // first staged entry
+  int n_staged = (c_end - c_begin - 1) * kChunk;
+  n_staged = n_staged < a.k - staged0 ? n_staged : a.k - staged0;     // latent entries only
+  n_staged = n_staged < kIdxCap ? n_staged : kIdxCap;                 // (a longer split loads the rest)
   {
-    int32_t ix0[4];
-    load_entry_ids(a, r, c_begin * kChunk, eg, ix0);
-    load_entry_ids(a, r, (c_begin + 1) * kChunk, eg, ix_next);
+    const int e0 = c_begin * kChunk + le;
+    const int32_t p0 = (c_begin < c_end && e0 < a.k) ? a.idx[(int64_t)r * a.k + e0] : -1;
+    int32_t st[kIdxCap / NT];
+#pragma unroll
+    for (int j = 0; j < kIdxCap / NT; ++j) {
+      const int t = tid + j * NT;
+      st[j] = t < n_staged ? a.idx[(int64_t)r * a.k + staged0 + t] : -1;
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (c_begin < c_end) {
-      int64_t off[4];
-      const int eb = c_begin * kChunk;
-      vb = entry_rows(a, seq, ws0, E, eb, eg, ix0, off);
-      const int kind = chunk_kind(eb, kChunk, a.k);
-      if (kind == kLatentRows)
-        gather_chunk<NT, kLatentRows, CH>(a, off, vb, eb, tid, gr);
-      else if (kind == kWindowRows)
-        gather_chunk<NT, kWindowRows, CH>(a, off, vb, eb, tid, gr);
-      else
-        gather_chunk<NT, kMixedRows, CH>(a, off, vb, eb, tid, gr);
+      const EntryRow x = entry_row(a, seq, ws0, E, e0, p0);
+      mask = __ballot(x.valid) & kChunkBits;
+      gather_chunk<CH, NT>(a, x.off, mask, c_begin * kChunk, w, lane, gr);
+    }
+#pragma unroll
+    for (int j = 0; j < kIdxCap / NT; ++j) {
+      const int t = tid + j * NT;
+      if (t < n_staged) sIdx[t] = st[j];
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  f32x4 qraw[2 * kS];
+  // query operands (B of S^T = C Q^T): head h, dims dbase + 32s + 8g .. +8,
+  // prescaled and split into bf16 hi + lo
+  bf16x8_t qhi[kS], qlo[kS];
   {
     const float* qp = a.q + ((int64_t)r * a.H + h) * 512 + dbase + 8 * g;
 #pragma unroll
     for (int s = 0; s < kS; ++s) {
-      qraw[2 * s] = *reinterpret_cast<const f32x4*>(qp + 32 * s);
-      qraw[2 * s + 1] = *reinterpret_cast<const f32x4*>(qp + 32 * s + 4);
-    }
-  }
-  // query operands (B of S^T = C Q^T): head h, dims dbase + 32s + 8g .. +8, prescaled
-  bf16x8_t qhi[kS], qlo[kS];
-  bool q_ready = false;
-  auto convert_query = [&]() {
-#pragma unroll
-    for (int s = 0; s < kS; ++s) {
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(qp + 32 * s);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(qp + 32 * s + 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = qraw[2 * s + (e >> 2)][e & 3] * a.qscale;
+        const float v = (e < 4 ? q0[e] : q1[e - 4]) * a.qscale;
         const __bf16 hi = (__bf16)v;
         qhi[s][e] = hi;
         qlo[s][e] = (__bf16)(v - (float)hi);
       }
     }
-    q_ready = true;
-  };
+  }
 
   f32x4 oacc[kM];
 #pragma unroll
@@ -288,44 +284,32 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   for (int c = c_begin; c < c_end; ++c) {
     const int ebase = c * kChunk;
     if (ebase >= E) break;
-    // this chunk's validity (the same in every wave: lanes 0..kEG-1 hold groups 0..kEG-1)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      bm[i] = (uint32_t)__ballot((vb >> i) & 1u) & (kEG == 32 ? 0xFFFFFFFFu : ((1u << kEG) - 1u));
-    const bool any = (bm[0] | bm[1] | bm[2] | bm[3]) != 0u;
-    if (any) {
+    const uint64_t cm = mask;   // this chunk's validity
+    if (cm != 0ull) {
       __syncthreads();   // previous chunk's LDS reads are done
-      const int kind = chunk_kind(ebase, kChunk, a.k);
-      if (kind == kLatentRows)
-        store_chunk<NT, kLatentRows, CH>(a, gr, vb, ebase, tid, sK, sVt);
-      else if (kind == kWindowRows)
-        store_chunk<NT, kWindowRows, CH>(a, gr, vb, ebase, tid, sK, sVt);
-      else
-        store_chunk<NT, kMixedRows, CH>(a, gr, vb, ebase, tid, sK, sVt);
+      store_chunk<CH, NT>(a, gr, cm, ebase, w, lane, sK);
       __syncthreads();
+    } else if (c == c_begin) {
+      __syncthreads();   // the staged indices are visible
     }
-    const uint32_t bmc[4] = {bm[0], bm[1], bm[2], bm[3]};
-    // the next chunk's rows, then the indices of the one after
+    // the next chunk's rows: in flight during this chunk's products
+    mask = 0ull;
     if (c + 1 < c_end && ebase + kChunk < E) {
-      int64_t off[4];
-      const int eb = ebase + kChunk;
-      vb = entry_rows(a, seq, ws0, E, eb, eg, ix_next, off);
-      const int kind = chunk_kind(eb, kChunk, a.k);
-      if (kind == kLatentRows)
-        gather_chunk<NT, kLatentRows, CH>(a, off, vb, eb, tid, gr);
-      else if (kind == kWindowRows)
-        gather_chunk<NT, kWindowRows, CH>(a, off, vb, eb, tid, gr);
-      else
-        gather_chunk<NT, kMixedRows, CH>(a, off, vb, eb, tid, gr);
-      if (c + 2 < c_end) load_entry_ids(a, r, eb + kChunk, eg, ix_next);
-    } else {
-      vb = 0u;
+      const int e = ebase + kChunk + le;
+      const int t = e - staged0;
+      int32_t p = -1;
+      if (t >= n_staged && e < a.k) p = a.idx[(int64_t)r * a.k + e];
+      const int32_t ps = t < n_staged ? sIdx[t < kIdxCap ? t : 0] : -1;
+      p = t < n_staged ? ps : p;
+      const EntryRow x = entry_row(a, seq, ws0, E, e, p);
+      mask = __ballot(x.valid) & kChunkBits;
+      gather_chunk<CH, NT>(a, x.off, mask, ebase + kChunk, w, lane, gr);
     }
-    if (!any) continue;
-
-    if (!q_ready) convert_query();
+    if (cm == 0ull) continue;
 
     // 3. partial S^T[CH entries x 16 heads] over this wave's kDims dims
+    // (row 16t + hl, dims dbase + 32s + 8g .. +8: chunk g of K step s, stored at chunk g ^ x)
+    const int s_base = hl * kKLd + dbase + 8 * (g ^ ((hl >> 2) & 1));
     f32x4 sacc[kT];
 #pragma unroll
     for (int t = 0; t < kT; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -334,58 +318,69 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
         const bf16x8_t A =
-            *reinterpret_cast<const bf16x8_t*>(&sK[(16 * t + hl) * kKLd + dbase + 32 * s + 8 * g]);
+            *reinterpret_cast<const bf16x8_t*>(&sK[s_base + t * 16 * kKLd + 32 * s]);
         sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qhi[s], sacc[t], 0, 0, 0);
         sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qlo[s], sacc[t], 0, 0, 0);
       }
     }
-    // the ND waves of a head group add their partial sums in part order,
-    // through the row-major copy's LDS once every wave is done reading it
-    __syncthreads();
-    f32x4* slots = reinterpret_cast<f32x4*>(sK);   // [NP][ND][64 lanes][kT]
+    // the ND waves of a head group add their partial sums in part order
     {
-      f32x4* mine = slots + ((pr * ND + part) * 64 + lane) * kT;
+      f32x4* mine = sX + (pr * ND + part) * kT * 64 + lane;
 #pragma unroll
-      for (int t = 0; t < kT; ++t) mine[t] = sacc[t];
+      for (int t = 0; t < kT; ++t) mine[64 * t] = sacc[t];
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < kT; ++t) {
-      f32x4 acc = slots[((pr * ND + 0) * 64 + lane) * kT + t];
+      f32x4 acc = sX[((pr * ND + 0) * kT + t) * 64 + lane];
 #pragma unroll
-      for (int p = 1; p < ND; ++p) acc += slots[((pr * ND + p) * 64 + lane) * kT + t];
+      for (int p = 1; p < ND; ++p) acc += sX[((pr * ND + p) * kT + t) * 64 + lane];
       sacc[t] = acc;
     }
 
-    // 4. online softmax (lane holds entries 16t + 4g + i of head h)
+    // 4. online softmax (lane holds entries 16t + 4g + i of head h).  The
+    // running maximum m_run only moves when a head's chunk maximum exceeds it
+    // by more than 2^kLazyRescale (then every lane of the wave rescales): the
+    // probabilities stay below 2^kLazyRescale, and l and the partials carry
+    // the same m_run, so the result is the same softmax.
+    if (cm != kChunkBits) {
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((cm >> (16 * t + 4 * g + i)) & 1ull)) sacc[t][i] = -__builtin_inff();
+    }
     float mloc = -__builtin_inff();
 #pragma unroll
     for (int t = 0; t < kT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // entry 16t + 4g + i: group 4t + g, member i
-        if (!((bmc[i] >> (4 * t + g)) & 1u)) sacc[t][i] = -__builtin_inff();
-        mloc = fmaxf(mloc, sacc[t][i]);
-      }
+      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sacc[t][i]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
+    if (__ballot(mloc > m_run + kLazyRescale) != 0ull) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int m = 0; m < kM; ++m) oacc[m] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < kT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sacc[t][i] - m_new);
+        const float p = exp2f(sacc[t][i] - m_run);
         sacc[t][i] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int m = 0; m < kM; ++m) oacc[m] *= alpha;
+    l_run += psum;
 
-    // 5. O^T[kDims dims x 16 heads] += C^T P^T, k-steps of 32 entries
+    // 5. O^T[kDims dims x 16 heads] += C^T P^T, k-steps of 32 entries.  The
+    // operand C^T is read from the row-major copy with transposing LDS reads:
+    // lane (g, hl) receives dim dbase + 16m + hl of entries 32j + 4g + 0..3
+    // (elements 0..3) and 32j + 16 + 4g + 0..3 (elements 4..7), the entries whose
+    // probabilities it holds.
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       bf16x8_t bhi, blo;
@@ -396,14 +391,23 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
         bhi[i] = hi;
         blo[i] = (__bf16)(p - (float)hi);
       }
+      // rows e0 and e0 + 16 (both with (e >> 2) & 1 = g & 1), dims dbase + 16m +
+      // 4 (hl & 3) .. +4: chunk 2m + ((hl & 3) >> 1), stored at that chunk ^ (g & 1)
+      const int e0 = 32 * j + 4 * g + (hl >> 2);
+      const int v_base = e0 * kKLd + dbase + 8 * (((hl & 3) >> 1) ^ (g & 1)) + 4 * (hl & 1);
 #pragma unroll
       for (int m = 0; m < kM; ++m) {
-        const __bf16* vrow = &sVt[(dbase + 16 * m + hl) * kVLd + 32 * j + 4 * g];
-        const bf16x4_t lo4 = *reinterpret_cast<const bf16x4_t*>(vrow);
-        const bf16x4_t hi4 = *reinterpret_cast<const bf16x4_t*>(vrow + 16);
+        const bf16x4_t lo4 = lds_read_tr4(&sK[v_base + 16 * m]);
+        const bf16x4_t hi4 = lds_read_tr4(&sK[v_base + 16 * kKLd + 16 * m]);
         const bf16x8_t A = bf16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bhi, oacc[m], 0, 0, 0);
         oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, blo, oacc[m], 0, 0, 0);
+      }
+      // two transposing reads ahead of each pair of products, no further
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
     }
   }
@@ -428,7 +432,7 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
 }
 
 // 8-wave workgroups (32 heads).  With 32-entry chunks two fit a compute unit
-// (78 KB of LDS each) when a wave keeps to 128 registers (a few spill), so one
+// (54 KB of LDS each) when a wave keeps to 128 registers (a few spill), so one
 // workgroup's loads overlap the other's products: better once the grid holds
 // several workgroups per compute unit, worse for a grid that does not.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void sparse_attn_kernel_h32c32_2wg(
@@ -512,7 +516,7 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restri
 // Head groups of 16 heads per workgroup (32 when H allows).
 static int attn_group_heads(int H) { return H >= 32 ? 32 : 16; }
 
-// Entries per chunk: 32 keeps a workgroup's LDS at 78 KB, so two workgroups
+// Entries per chunk: 32 keeps a workgroup's LDS at 54 KB, so two workgroups
 // share a compute unit and one's loads overlap the other's products.
 static int attn_chunk(int R, int H, int k_plus_win) {
   (void)R;

@@ -221,6 +221,27 @@ def test_sparse_attn_vs_oracle(H, k, win_lens):
     assert err <= ATOL
 
 
+@pytest.mark.parametrize("B,M,k,H", [
+    (2, 64, 1500, 64),    # one split per row, over 1,024 later-chunk indices (the rest load directly)
+    (4, 130, 200, 64),    # more than 1,024 workgroups (two per compute unit), a chunk mixing both row kinds
+    (1, 700, 96, 32),     # 700 workgroups of 32 heads
+])
+def test_sparse_attn_many_rows_long_rows(B, M, k, H):
+    w = Workload("attnR", 1000 + B * M + k, B=B, M=M, N=2500, H=H, k=k)
+    cache, (lay,) = host_inputs(w)
+    rng = np.random.default_rng(B * M + k)
+    lay["win_len"] = rng.integers(0, 129, size=w.R).astype(np.int32)
+    idx = np.sort(rng.choice(w.N, size=(w.R, k), replace=True), axis=1).astype(np.int32)
+    idx[::7, k // 3:] = -1            # padded rows
+    say(f"attn B={B} M={M} k={k} H={H}")
+    got = _attn_case(w, cache, lay, idx, 128)
+    ref = oracle_attn(w, cache, lay, idx)
+    err = np.max(np.abs(got - ref))
+    say(f"  max abs err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= ATOL
+
+
 def test_sparse_attn_no_window_and_empty():
     w = Workload("attn0", 5, B=2, N=500, H=64, k=64, win_len=0)
     cache, (lay,) = host_inputs(w)
