@@ -445,21 +445,25 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel_h16c32(AttnParams a) {
 __global__ __launch_bounds__(256, 1) void sparse_attn_kernel_h16c64(AttnParams a) { sparse_attn_body<1, 4, 64>(a); }
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One workgroup per (row, head), one thread per output dim.  Wave 0 reads the
-// splits' (m, l) pairs and turns them into weights in LDS; every thread's own
-// dim of the first kCombineGroup splits' o is loaded before that, so the
-// weights and the partials arrive in one memory round trip.
+// One workgroup per (row, head), V consecutive output dims per thread (512 / V
+// threads).  Wave 0 reads the splits' (m, l) pairs and turns them into weights
+// in LDS; every thread's dims of the first 32 / V splits are loaded before
+// that, so the weights and the partials arrive in one memory round trip.  Few
+// splits take V = 4 (small workgroups: a grid of many rows is resident at
+// once), many splits V = 1 (all of them in flight per thread).
 constexpr int kMaxSplits = kAttnTargetWorkgroups;   // attn_splits never exceeds it
-constexpr int kCombineGroup = 32;
 
-__global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml, int splits, int H,
-                                                           float* __restrict__ out) {
+template <int V>
+__global__ __launch_bounds__(512 / V) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                               const float* __restrict__ part_ml, int splits,
+                                                               int H, float* __restrict__ out) {
+  constexpr int kGroup = 32 / V;
+  typedef float vec_t __attribute__((ext_vector_type(V)));
   __shared__ float sw[kMaxSplits];   // 2^(m_s - M), 0 for splits that saw nothing
   __shared__ float sL;
   const int r = blockIdx.y;
   const int h = blockIdx.x;
-  const int d = threadIdx.x;
+  const int d = V * threadIdx.x;
   const int64_t base = (int64_t)r * splits * H + h;     // slot of split s: base + s*H
   float m[kMaxSplits / 64], l[kMaxSplits / 64];
   if (threadIdx.x < 64) {
@@ -474,9 +478,10 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restri
       }
     }
   }
-  float ov[kCombineGroup];
+  vec_t ov[kGroup];
 #pragma unroll
-  for (int j = 0; j < kCombineGroup; ++j) ov[j] = j < splits ? part_o[(base + (int64_t)j * H) * 512 + d] : 0.f;
+  for (int j = 0; j < kGroup; ++j)
+    ov[j] = j < splits ? *reinterpret_cast<const vec_t*>(part_o + (base + (int64_t)j * H) * 512 + d) : vec_t(0.f);
   if (threadIdx.x < 64) {
     // wave 0: M = max_s m_s, then the weights and L = sum_s w_s l_s in split order
     float M = -__builtin_inff();
@@ -498,19 +503,20 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restri
     if (threadIdx.x == 0) sL = L;
   }
   __syncthreads();
-  float acc = 0.f;
-  for (int s0 = 0; s0 < splits; s0 += kCombineGroup) {
+  vec_t acc = vec_t(0.f);
+  for (int s0 = 0; s0 < splits; s0 += kGroup) {
     if (s0 > 0) {
 #pragma unroll
-      for (int j = 0; j < kCombineGroup; ++j)
-        ov[j] = s0 + j < splits ? part_o[(base + (int64_t)(s0 + j) * H) * 512 + d] : 0.f;
+      for (int j = 0; j < kGroup; ++j)
+        ov[j] = s0 + j < splits ? *reinterpret_cast<const vec_t*>(part_o + (base + (int64_t)(s0 + j) * H) * 512 + d)
+                                : vec_t(0.f);
     }
 #pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j)
+    for (int j = 0; j < kGroup; ++j)
       if (s0 + j < splits) acc += sw[s0 + j] * ov[j];
   }
   const float L = sL;
-  out[((int64_t)r * H + h) * 512 + d] = L > 0.f ? acc / L : 0.f;
+  *reinterpret_cast<vec_t*>(out + ((int64_t)r * H + h) * 512 + d) = L > 0.f ? acc / L : vec_t(0.f);
 }
 
 // Head groups of 16 heads per workgroup (32 when H allows).
@@ -598,8 +604,13 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
     hipLaunchKernelGGL(sparse_attn_kernel_h16c64, grid, dim3(256), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.splits == 1) return err;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)L.H, (unsigned)R), dim3(512), 0, stream, a.part_o,
-                     a.part_ml, a.splits, L.H, L.out);
+  const dim3 cgrid((unsigned)L.H, (unsigned)R);
+  if (a.splits <= 8)
+    hipLaunchKernelGGL(attn_combine_kernel<4>, cgrid, dim3(128), 0, stream, a.part_o, a.part_ml, a.splits, L.H, L.out);
+  else if (a.splits <= 16)
+    hipLaunchKernelGGL(attn_combine_kernel<2>, cgrid, dim3(256), 0, stream, a.part_o, a.part_ml, a.splits, L.H, L.out);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<1>, cgrid, dim3(512), 0, stream, a.part_o, a.part_ml, a.splits, L.H, L.out);
   return hipGetLastError();
 }
 

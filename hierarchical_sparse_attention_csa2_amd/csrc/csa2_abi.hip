@@ -30,6 +30,13 @@ inline FullWs full_ws(int64_t R, int64_t N_max, int k) {
   return w;
 }
 
+// Every tensor pointer the caller passes must be 16-byte aligned (NULL passes).
+inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+template <typename... P>
+inline bool any_misaligned(const P*... p) {
+  return (misaligned(p) || ...);
+}
+
 constexpr int64_t kMaxRows = 1 << 24;
 constexpr int64_t kMaxN = (int64_t)1 << 30;   // ids are int32; 8*blocks must fit
 constexpr int kMaxPool = 1 << 20;
@@ -53,6 +60,8 @@ int csa2_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
                     const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
                     float* scores, float* block_max, float* super_max, void* stream) {
   if (!q_codes || !q_scales || !k_codes || !k_scales || !n_visible || !block_max) return CSA2_ERR_INVALID;
+  if (any_misaligned(q_codes, q_scales, k_codes, k_scales, n_visible, scores, block_max, super_max))
+    return CSA2_ERR_INVALID;
   if (B < 1 || M < 1 || N_max < 1 || N_max > kMaxN || (int64_t)B * M > kMaxRows) return CSA2_ERR_INVALID;
   return hip_status(csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, scores,
                                             block_max, (N_max + 7) / 8, super_max, (N_max + 63) / 64,
@@ -63,6 +72,7 @@ int csa2_select_blocks(const float* block_max, const float* super_max, int64_t n
                        const int32_t* n_visible, int R, int n_pool, int32_t* pool_blocks, int k_blocks,
                        int32_t* topk_blocks, void* stream) {
   if (!block_max || !n_visible || !pool_blocks) return CSA2_ERR_INVALID;
+  if (any_misaligned(block_max, super_max, n_visible, pool_blocks, topk_blocks)) return CSA2_ERR_INVALID;
   if (R < 1 || R > kMaxRows || n_pool < 1 || n_pool > kMaxPool || k_blocks < 0 || k_blocks > kMaxPool ||
       nblk_stride < 1 || nblk_stride > kMaxN / 8)
     return CSA2_ERR_INVALID;
@@ -77,6 +87,8 @@ int csa2_index_pool(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
                     int B, int M, int64_t N_max, float* pool_scores, void* stream) {
   if (!q_codes || !q_scales || !k_codes || !k_scales || !pool_blocks || !n_visible || !pool_scores)
     return CSA2_ERR_INVALID;
+  if (any_misaligned(q_codes, q_scales, k_codes, k_scales, pool_blocks, n_visible, pool_scores))
+    return CSA2_ERR_INVALID;
   if (B < 1 || M < 1 || N_max < 1 || N_max > kMaxN || (int64_t)B * M > kMaxRows || n_pool < 1 ||
       n_pool > kMaxPool)
     return CSA2_ERR_INVALID;
@@ -87,6 +99,7 @@ int csa2_index_pool(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
 int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, const int32_t* n_visible, int R,
               int k, int32_t* idx, void* stream) {
   if (!scores || !n_visible || !idx) return CSA2_ERR_INVALID;
+  if (any_misaligned(scores, pool_blocks, n_visible, idx)) return CSA2_ERR_INVALID;
   if (R < 1 || R > kMaxRows || n_pool < 1 || k < 0 || k > kMaxPool) return CSA2_ERR_INVALID;
   if (pool_blocks ? n_pool > kMaxPool : n_pool > kMaxN) return CSA2_ERR_INVALID;
   if (k == 0) return CSA2_OK;
@@ -100,6 +113,9 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
                     int k, float* scores, float* block_max, int32_t* pool_blocks, int32_t* idx, void* workspace,
                     size_t workspace_bytes, void* stream) {
   if (!q_codes || !q_scales || !k_codes || !k_scales || !n_visible || !pool_blocks) return CSA2_ERR_INVALID;
+  if (any_misaligned(q_codes, q_scales, k_codes, k_scales, n_visible, scores, block_max, pool_blocks, idx,
+                     static_cast<const char*>(workspace)))
+    return CSA2_ERR_INVALID;
   if (B < 1 || M < 1 || N_max < 1 || N_max > kMaxN || (int64_t)B * M > kMaxRows || n_pool < 1 ||
       n_pool > kMaxPool || k < 0 || k > kMaxPool)
     return CSA2_ERR_INVALID;
@@ -142,6 +158,8 @@ int csa2_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_sc
                      int M, int64_t N_max, int H, int Tw, float sm_scale, float* out, void* workspace,
                      size_t workspace_bytes, void* stream) {
   if (!q || !out) return CSA2_ERR_INVALID;
+  if (any_misaligned(q, c_codes, c_scales, idx, win, win_start, win_len, out, static_cast<const char*>(workspace)))
+    return CSA2_ERR_INVALID;
   if (B < 1 || M < 1 || (int64_t)B * M > kMaxRows || k < 0 || k > kMaxPool || win_max < 0 || Tw < 0 ||
       win_max > Tw || N_max < 0 || N_max > kMaxN)
     return CSA2_ERR_INVALID;

@@ -16,6 +16,9 @@
  * Conventions shared by every entry point
  *   - All tensor arguments are DEVICE pointers to caller-owned memory; the library
  *     allocates nothing and keeps no state between calls.
+ *   - Every non-NULL tensor pointer must be 16-byte aligned (device allocations
+ *     are): the kernels move codes, queries, outputs and partials in 16-byte
+ *     vectors.  A misaligned pointer is an argument error (CSA2_ERR_INVALID).
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
  *     default stream).  Calls return before the work finishes: results are valid
  *     once the caller synchronises the stream.
@@ -171,7 +174,7 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales,
  * decoded values exact in bf16), accumulation in fp32.
  *   H: 16, 32 or 64.   win_max: 0 <= win_max <= Tw (0: no window;
  *   win, win_start and win_len may then be NULL).
- *   win_start[r] + min(win_len[r], win_max) <= Tw is required (not checked).
+ *   Window rows outside [0, Tw) are skipped like entries outside [0, N_max).
  *   workspace: csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, M, 0, H, k + win_max)
  * Returns CSA2_OK, CSA2_ERR_INVALID, CSA2_ERR_UNSUPPORTED (H), CSA2_ERR_WORKSPACE,
  * CSA2_ERR_HIP.

@@ -78,6 +78,21 @@ def test_validation_rejects_before_launch():
                               1 << 20, NULL) == -1
 
 
+def test_validation_rejects_misaligned_pointers():
+    """Tensor pointers must be 16-byte aligned; the check runs before any launch."""
+    L = csa2.load_library()
+    Q = ctypes.c_void_p(0x1004)
+    f = ctypes.c_float(0.04)
+    assert L.csa2_index_scan(Q, P, P, P, P, 1, 1, 16, NULL, P, NULL, NULL) == -1
+    assert L.csa2_index_scan(P, P, P, P, P, 1, 1, 16, NULL, Q, NULL, NULL) == -1
+    assert L.csa2_select_blocks(P, Q, 2, P, 1, 4, P, 0, NULL, NULL) == -1
+    assert L.csa2_index_pool(P, P, Q, P, P, 4, P, 1, 1, 16, P, NULL) == -1
+    assert L.csa2_topk(P, NULL, 4, P, 1, 8, Q, NULL) == -1
+    assert L.csa2_index_full(P, P, P, P, P, 1, 1, 64, 4, 8, NULL, NULL, P, P, Q, 1 << 20, NULL) == -1
+    assert L.csa2_sparse_attn(Q, P, P, P, 8, P, P, P, 4, 1, 1, 64, 64, 8, f, P, P, 1 << 20, NULL) == -1
+    assert L.csa2_sparse_attn(P, P, P, P, 8, P, P, P, 4, 1, 1, 64, 64, 8, f, Q, P, 1 << 20, NULL) == -1
+
+
 def test_workspace_bytes():
     L = csa2.load_library()
     # index_full: block maxima + the first k blocks + their scores
