@@ -12,12 +12,17 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ER
 
 inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Decode calls (fewer than this many queries per sequence) store every score
+// and take the top-k from those of the pool's first blocks; prefill calls
+// rescore those blocks instead of storing M scores per entry.
+constexpr int kStoreScoresBelowM = 16;
+
 // index_full workspace carve-up
 struct FullWs {
-  size_t block_max, super_max, topk_blocks, topk_scores, key_floor, total;
+  size_t block_max, super_max, topk_blocks, topk_scores, key_floor, scores, total;
 };
 
-inline FullWs full_ws(int64_t R, int64_t N_max, int k) {
+inline FullWs full_ws(int64_t R, int M, int64_t N_max, int k) {
   FullWs w;
   const int64_t nblk = (N_max + 7) / 8;
   const int64_t nsup = (N_max + 63) / 64;
@@ -26,7 +31,9 @@ inline FullWs full_ws(int64_t R, int64_t N_max, int k) {
   w.topk_blocks = align_up(w.super_max + (size_t)R * nsup * sizeof(float));
   w.topk_scores = align_up(w.topk_blocks + (size_t)R * (k > 0 ? k : 0) * sizeof(int32_t));
   w.key_floor = align_up(w.topk_scores + (size_t)R * (k > 0 ? k : 0) * 8 * sizeof(float));
-  w.total = align_up(w.key_floor + (size_t)R * sizeof(uint32_t));
+  w.scores = align_up(w.key_floor + (size_t)R * sizeof(uint32_t));
+  const bool store = M < kStoreScoresBelowM && k > 0;
+  w.total = align_up(w.scores + (store ? (size_t)R * N_max * sizeof(float) : 0));
   return w;
 }
 
@@ -122,7 +129,7 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
   if (k > 0 && !idx) return CSA2_ERR_INVALID;
   const int64_t R = (int64_t)B * M;
   const int64_t nblk = (N_max + 7) / 8;
-  const FullWs w = full_ws(R, N_max, k);
+  const FullWs w = full_ws(R, M, N_max, k);
   if (!workspace || workspace_bytes < w.total) return CSA2_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   float* bmax = block_max ? block_max : reinterpret_cast<float*>(ws + w.block_max);
@@ -131,17 +138,32 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
   float* smax = reinterpret_cast<float*>(ws + w.super_max);
   const int64_t nsup = (N_max + 63) / 64;
   hipStream_t s = as_stream(stream);
-  hipError_t e = csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, scores, bmax,
-                                         nblk, smax, nsup, s);
-  if (e != hipSuccess) return CSA2_ERR_HIP;
-  // the pool's top-k lies in the pool's first min(k, n_pool) blocks: rescore only those
+  // the pool's top-k lies in the pool's first min(k, n_pool) blocks
   const int kb = k < n_pool ? k : n_pool;
+  if (M < kStoreScoresBelowM && k > 0) {
+    // decode: the scan stores every score; one workgroup per row then builds the
+    // pool and takes the top-k from the stored scores of its first kb blocks
+    float* sc = scores ? scores : reinterpret_cast<float*>(ws + w.scores);
+    hipError_t e = csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, sc, bmax,
+                                           nblk, smax, nsup, s);
+    if (e != hipSuccess) return CSA2_ERR_HIP;
+    e = csa2::launch_select_topk(bmax, nblk, smax, nsup, n_visible, (int)R, n_pool, pool_blocks, kb, sc, N_max, k,
+                                 idx, s);
+    if (e != hipErrorNotSupported) return hip_status(e);
+    // shapes the fused kernel does not cover: the staged selection below (the
+    // scan's outputs are in place)
+  } else {
+    const hipError_t e = csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max,
+                                                 scores, bmax, nblk, smax, nsup, s);
+    if (e != hipSuccess) return CSA2_ERR_HIP;
+  }
+  // rescore only the first kb pool blocks
   // When the first kb = k blocks are the k best of the row, the k-th best block
   // maximum (the selection's floor) is at most the k-th best position score:
   // those k block maxima are k positions reaching it.  The top-k then drops
   // every slot below that floor unexamined.
   uint32_t* key_floor = reinterpret_cast<uint32_t*>(ws + w.key_floor);
-  e = csa2::launch_select(csa2::kSelBlocks, bmax, nblk, nullptr, 0, n_visible, (int)R, n_pool, pool_blocks,
+  hipError_t e = csa2::launch_select(csa2::kSelBlocks, bmax, nblk, nullptr, 0, n_visible, (int)R, n_pool, pool_blocks,
                           kb, k > 0 ? topk_blocks : nullptr, smax, nsup, s, nullptr, key_floor);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   if (k == 0) return CSA2_OK;
@@ -197,7 +219,7 @@ size_t csa2_workspace_bytes(int op, int B, int M, int64_t N_max, int H, int k) {
   const int64_t R = (int64_t)B * M;
   if (op == CSA2_OP_INDEX_FULL) {
     if (N_max < 1) return 0;
-    return full_ws(R, N_max, k).total;
+    return full_ws(R, M, N_max, k).total;
   }
   if (op == CSA2_OP_SPARSE_ATTN) {
     if (H != 16 && H != 32 && H != 64) return 0;

@@ -38,6 +38,14 @@ hipError_t launch_select(int layout, const float* scores, int64_t stride, const 
                          int32_t* out2, const float* super_max, int64_t nsup_stride, hipStream_t stream,
                          const uint32_t* floor_in = nullptr, uint32_t* floor_out = nullptr);
 
+// Full layer, decode: pool (n_pool <= 2048) and the top-k over the pool's first
+// kb blocks in one workgroup per row, from the scan's block maxima (row stride
+// `stride`), super-block maxima and stored scores (row stride n_max).
+// hipErrorNotSupported (nothing launched) outside the shapes it covers.
+hipError_t launch_select_topk(const float* bmax, int64_t stride, const float* super_max, int64_t nsup_stride,
+                              const int32_t* n_visible, int R, int n_pool, int32_t* pool_out, int kb,
+                              const float* scores, int64_t n_max, int k, int32_t* idx, hipStream_t stream);
+
 struct AttnLaunch {
   const float* q;
   const uint8_t* c_codes;

@@ -429,17 +429,14 @@ __device__ __forceinline__ void select_targets(SelShared& sh, const RowView row,
 // floor_in (may be null): keys below floor_in[r] cannot be selected and are
 // dropped; floor_out (may be null): the key of target 1's K1-th item, or 1 when
 // the row has at most K1 items.
+// Row r of the register path.  o0 / o1: this row's outputs (may be null);
+// floor_out: this row's floor slot (may be null).
 template <int J, int LAYOUT>
-__global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __restrict__ scores, int64_t stride,
-                                                                 const int32_t* __restrict__ pool_blocks,
-                                                                 int64_t n_pool,
-                                                                 const int32_t* __restrict__ n_visible, int K0,
-                                                                 int32_t* __restrict__ out0, int K1,
-                                                                 int32_t* __restrict__ out1,
-                                                                 const uint32_t* __restrict__ floor_in,
-                                                                 uint32_t* __restrict__ floor_out) {
-  __shared__ RegShared sh;
-  const int r = blockIdx.x;
+__device__ __forceinline__ void select_reg_row(RegShared& sh, int r, const float* __restrict__ scores,
+                                               int64_t stride, const int32_t* __restrict__ pool_blocks,
+                                               int64_t n_pool, const int32_t* __restrict__ n_visible, int K0,
+                                               int32_t* o0, int K1, int32_t* o1,
+                                               const uint32_t* __restrict__ floor_in, uint32_t* floor_out) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cap = (int)(LAYOUT == kSelPool ? 8 * n_pool : stride);
   const int Jp = (cap + 1023) >> 10;
@@ -473,10 +470,8 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
     const uint32_t key = order_key(x[j]);
     k[j] = ok && key >= fl ? key : 0u;
   }
-  int32_t* o0 = out0 ? out0 + (int64_t)r * K0 : nullptr;
-  int32_t* o1 = out1 ? out1 + (int64_t)r * K1 : nullptr;
-  if (!out0) K0 = 0;
-  if (!out1) K1 = 0;
+  if (!o0) K0 = 0;
+  if (!o1) K1 = 0;
   hist_zero(sh.c);
   if (threadIdx.x == 0) {
     sh.s.cnt[0] = 0;
@@ -487,7 +482,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
   key_range(sh.s, k, Jp, valid, kmin, kmax);
   Thr th0, th1;
   select_thresholds(sh.c, sh.s, k, Jp, valid, kmin, kmax, K0, K1, 0, th0, th1);
-  if (floor_out && threadIdx.x == 0) floor_out[r] = (K1 > 0 && th1.keff == K1 && valid > K1) ? th1.T : 1u;
+  if (floor_out && threadIdx.x == 0) *floor_out = (K1 > 0 && th1.keff == K1 && valid > K1) ? th1.T : 1u;
   emit_sel(
       sh.s, k, Jp, th0, th1,
       [&](int t, int pos, int j, int i) {
@@ -496,6 +491,22 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
         (t ? o1 : o0)[pos] = id;
       },
       [&](int t, int p) { (t ? o1 : o0)[p] = -1; });
+}
+
+template <int J, int LAYOUT>
+__global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                 const int32_t* __restrict__ pool_blocks,
+                                                                 int64_t n_pool,
+                                                                 const int32_t* __restrict__ n_visible, int K0,
+                                                                 int32_t* __restrict__ out0, int K1,
+                                                                 int32_t* __restrict__ out1,
+                                                                 const uint32_t* __restrict__ floor_in,
+                                                                 uint32_t* __restrict__ floor_out) {
+  __shared__ RegShared sh;
+  const int r = blockIdx.x;
+  select_reg_row<J, LAYOUT>(sh, r, scores, stride, pool_blocks, n_pool, n_visible, K0,
+                            out0 ? out0 + (int64_t)r * K0 : nullptr, K1, out1 ? out1 + (int64_t)r * K1 : nullptr,
+                            floor_in, floor_out ? floor_out + r : nullptr);
 }
 
 // Block rows of up to 65,536 blocks, targets of at most 2048 blocks.
@@ -520,6 +531,7 @@ struct Blocks3Shared {
   int32_t sbsel[kKeepCap];      // kept super-blocks, id order
   int wsum[4][kSelWaves];       // per-wave totals of the prefix sums
   Small s;
+  uint32_t floor;               // the fused top-k's floor
 };
 
 // Exclusive prefix sum of x over the workgroup in thread order, and the total.
@@ -563,26 +575,21 @@ __device__ __forceinline__ void blocks_level2(Blocks3Shared& sh, int m2, uint32_
 // kVec: super_max rows 16-byte aligned and block rows 32-byte aligned, so a
 // thread's 8 super maxima and a super-block's 8 block maxima are two 16-byte
 // loads each.
+// Row r of the two-level block filter.  o0 / o1: this row's outputs (may be
+// null); floor_out: this row's floor slot (may be null).
 template <bool kHaveSuper, bool kVec>
-__global__ __launch_bounds__(kSelThreads) void select_blocks3_kernel(const float* __restrict__ bmax, int64_t stride,
-                                                                     const float* __restrict__ super_max,
-                                                                     int64_t nsup_stride,
-                                                                     const int32_t* __restrict__ n_visible, int K0,
-                                                                     int32_t* __restrict__ out0, int K1,
-                                                                     int32_t* __restrict__ out1,
-                                                                     uint32_t* __restrict__ floor_out) {
-  __shared__ Blocks3Shared sh;
-  const int r = blockIdx.x;
+__device__ __forceinline__ void select_blocks3_row(Blocks3Shared& sh, int r, const float* __restrict__ bmax,
+                                                   int64_t stride, const float* __restrict__ super_max,
+                                                   int64_t nsup_stride, const int32_t* __restrict__ n_visible,
+                                                   int K0, int32_t* o0, int K1, int32_t* o1, uint32_t* floor_out) {
   const int t = threadIdx.x;
   const float* row = bmax + (int64_t)r * stride;
   const int nsup_cap = (int)((stride + 7) >> 3);   // <= 8192
-  int32_t* o0 = out0 ? out0 + (int64_t)r * K0 : nullptr;
-  int32_t* o1 = out1 ? out1 + (int64_t)r * K1 : nullptr;
-  if (!out0) K0 = 0;
-  if (!out1) K1 = 0;
+  if (!o0) K0 = 0;
+  if (!o1) K1 = 0;
   const int kmaxK = K0 > K1 ? K0 : K1;
   if (kmaxK == 0) {
-    if (floor_out && t == 0) floor_out[r] = 1u;
+    if (floor_out && t == 0) *floor_out = 1u;
     return;
   }
 
@@ -745,9 +752,115 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks3_kernel(const float
   // level 2 over the m2 survivors (item order = id order), all within [T1, kmax1];
   // registers sized to the count (a typical row keeps 2,000-3,000)
   if (m2 <= 4 * kSelThreads)
-    blocks_level2<4>(sh, m2, T1, kmax1, K0, o0, K1, o1, floor_out ? floor_out + r : nullptr);
+    blocks_level2<4>(sh, m2, T1, kmax1, K0, o0, K1, o1, floor_out);
   else
-    blocks_level2<16>(sh, m2, T1, kmax1, K0, o0, K1, o1, floor_out ? floor_out + r : nullptr);
+    blocks_level2<16>(sh, m2, T1, kmax1, K0, o0, K1, o1, floor_out);
+}
+
+template <bool kHaveSuper, bool kVec>
+__global__ __launch_bounds__(kSelThreads) void select_blocks3_kernel(const float* __restrict__ bmax, int64_t stride,
+                                                                     const float* __restrict__ super_max,
+                                                                     int64_t nsup_stride,
+                                                                     const int32_t* __restrict__ n_visible, int K0,
+                                                                     int32_t* __restrict__ out0, int K1,
+                                                                     int32_t* __restrict__ out1,
+                                                                     uint32_t* __restrict__ floor_out) {
+  __shared__ Blocks3Shared sh;
+  const int r = blockIdx.x;
+  select_blocks3_row<kHaveSuper, kVec>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, K0,
+                                       out0 ? out0 + (int64_t)r * K0 : nullptr, K1,
+                                       out1 ? out1 + (int64_t)r * K1 : nullptr, floor_out ? floor_out + r : nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// Full layer, decode: the block filter and the top-k in one workgroup per row.
+// The filter leaves the row's first kb blocks (ids ascending, -1 padded) and
+// its floor in LDS; the top-k then reads the scan's stored scores of those
+// blocks' 8*kb positions (the row's top-k lies there: the pool lemma) and
+// ranks them by (score desc, position asc).  When kb == k the k-th block key
+// is at most the k-th position score (those k block maxima are k positions
+// reaching it), so positions below it are dropped unexamined.
+// ---------------------------------------------------------------------------
+constexpr int kFusedMaxKb = 2048;
+
+template <int JT>
+__device__ __forceinline__ void topk_from_blocks(Core& c, Small& s, const int32_t* blk, int kb,
+                                                 const float* __restrict__ srow, int64_t n_lim, uint32_t floor,
+                                                 int k, int32_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int cap = 8 * kb;
+  const int Jp = (cap + 1023) >> 10;
+  int32_t pos[JT];
+#pragma unroll
+  for (int j = 0; j < JT; ++j) {
+    const int i = (w * Jp + j) * 64 + lane;
+    const int32_t b = (j < Jp && i < cap) ? blk[i >> 3] : -1;
+    const int64_t p = 8 * (int64_t)b + (i & 7);
+    pos[j] = (b >= 0 && p < n_lim) ? (int32_t)p : -1;
+  }
+  float x[JT];
+#pragma unroll
+  for (int j = 0; j < JT; ++j) x[j] = pos[j] >= 0 ? srow[pos[j]] : 0.0f;
+  uint32_t key[JT];
+#pragma unroll
+  for (int j = 0; j < JT; ++j) {
+    const uint32_t kk = order_key(x[j]);
+    key[j] = (pos[j] >= 0 && kk >= floor) ? kk : 0u;
+  }
+  hist_zero(c);
+  if (threadIdx.x == 0) {
+    s.cnt[0] = 0;
+    s.cnt[1] = 0;
+  }
+  int valid;
+  uint32_t kmin, kmax;
+  key_range(s, key, Jp, valid, kmin, kmax);
+  Thr th0, th1;
+  select_thresholds(c, s, key, Jp, valid, kmin, kmax, k, 0, 0, th0, th1);
+  emit_sel(
+      s, key, Jp, th0, th1, [&](int, int p, int j, int) { out[p] = pos[j]; }, [&](int, int p) { out[p] = -1; });
+}
+
+struct RegTopkShared {
+  RegShared rs;
+  int32_t blk[kFusedMaxKb];
+  uint32_t floor;
+};
+
+// Block rows of at most 1024*J blocks (register filter), kb <= 128*JT.
+template <int J, int JT>
+__global__ __launch_bounds__(kSelThreads) void select_reg_topk_kernel(
+    const float* __restrict__ bmax, int64_t stride, const int32_t* __restrict__ n_visible, int n_pool,
+    int32_t* __restrict__ pool_out, int kb, const float* __restrict__ scores, int64_t n_max, int k,
+    int32_t* __restrict__ idx) {
+  __shared__ RegTopkShared sh;
+  const int r = blockIdx.x;
+  select_reg_row<J, kSelBlocks>(sh.rs, r, bmax, stride, nullptr, 0, n_visible, n_pool, pool_out + (int64_t)r * n_pool,
+                                kb, sh.blk, nullptr, &sh.floor);
+  __syncthreads();
+  int64_t nv = n_visible[r];
+  nv = nv < 0 ? 0 : (nv < n_max ? nv : n_max);
+  topk_from_blocks<JT>(sh.rs.c, sh.rs.s, sh.blk, kb, scores + (int64_t)r * n_max, nv, kb == k ? sh.floor : 1u, k,
+                       idx + (int64_t)r * k);
+}
+
+// Block rows of up to 65,536 blocks (two-level filter), kb <= 128*JT.  The
+// filter's kept-super-block list is free once level 2 runs: it holds the kb
+// block ids.
+template <bool kVec, int JT>
+__global__ __launch_bounds__(kSelThreads) void select_blocks3_topk_kernel(
+    const float* __restrict__ bmax, int64_t stride, const float* __restrict__ super_max, int64_t nsup_stride,
+    const int32_t* __restrict__ n_visible, int n_pool, int32_t* __restrict__ pool_out, int kb,
+    const float* __restrict__ scores, int64_t n_max, int k, int32_t* __restrict__ idx) {
+  __shared__ Blocks3Shared sh;
+  const int r = blockIdx.x;
+  select_blocks3_row<true, kVec>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, n_pool,
+                                 pool_out + (int64_t)r * n_pool, kb, sh.sbsel, &sh.floor);
+  __syncthreads();
+  int64_t nv = n_visible[r];
+  nv = nv < 0 ? 0 : (nv < n_max ? nv : n_max);
+  topk_from_blocks<JT>(sh.c, sh.s, sh.sbsel, kb, scores + (int64_t)r * n_max, nv, kb == k ? sh.floor : 1u, k,
+                       idx + (int64_t)r * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -842,6 +955,50 @@ hipError_t launch_select(int layout, const float* scores, int64_t stride, const 
   }
 #undef CSA2_REG_J
 #undef CSA2_REG
+  return hipGetLastError();
+}
+
+hipError_t launch_select_topk(const float* bmax, int64_t stride, const float* super_max, int64_t nsup_stride,
+                              const int32_t* n_visible, int R, int n_pool, int32_t* pool_out, int kb,
+                              const float* scores, int64_t n_max, int k, int32_t* idx, hipStream_t stream) {
+  if (kb < 1 || kb > kFusedMaxKb || k < 1 || n_pool < kb || n_pool > 2048 || !super_max)
+    return hipErrorNotSupported;
+  const dim3 grid((unsigned)R), block(kSelThreads);
+  const bool small_kb = kb <= 512;
+#define CSA2_REGT(J)                                                                                          \
+  do {                                                                                                        \
+    if (small_kb)                                                                                             \
+      hipLaunchKernelGGL((select_reg_topk_kernel<J, 4>), grid, block, 0, stream, bmax, stride, n_visible,     \
+                         n_pool, pool_out, kb, scores, n_max, k, idx);                                        \
+    else                                                                                                      \
+      hipLaunchKernelGGL((select_reg_topk_kernel<J, 16>), grid, block, 0, stream, bmax, stride, n_visible,    \
+                         n_pool, pool_out, kb, scores, n_max, k, idx);                                        \
+  } while (0)
+  if (stride <= 4096) {
+    CSA2_REGT(4);
+  } else if (stride <= 8192) {
+    CSA2_REGT(8);
+  } else if (stride <= 16384) {
+    CSA2_REGT(16);
+  } else if ((stride + 7) / 8 <= 8192) {
+    const bool vec = reinterpret_cast<uintptr_t>(super_max) % 16 == 0 && nsup_stride % 4 == 0 &&
+                     reinterpret_cast<uintptr_t>(bmax) % 32 == 0 && stride % 8 == 0;
+    if (vec && small_kb)
+      hipLaunchKernelGGL((select_blocks3_topk_kernel<true, 4>), grid, block, 0, stream, bmax, stride, super_max,
+                         nsup_stride, n_visible, n_pool, pool_out, kb, scores, n_max, k, idx);
+    else if (vec)
+      hipLaunchKernelGGL((select_blocks3_topk_kernel<true, 16>), grid, block, 0, stream, bmax, stride, super_max,
+                         nsup_stride, n_visible, n_pool, pool_out, kb, scores, n_max, k, idx);
+    else if (small_kb)
+      hipLaunchKernelGGL((select_blocks3_topk_kernel<false, 4>), grid, block, 0, stream, bmax, stride, super_max,
+                         nsup_stride, n_visible, n_pool, pool_out, kb, scores, n_max, k, idx);
+    else
+      hipLaunchKernelGGL((select_blocks3_topk_kernel<false, 16>), grid, block, 0, stream, bmax, stride, super_max,
+                         nsup_stride, n_visible, n_pool, pool_out, kb, scores, n_max, k, idx);
+  } else {
+    return hipErrorNotSupported;
+  }
+#undef CSA2_REGT
   return hipGetLastError();
 }
 

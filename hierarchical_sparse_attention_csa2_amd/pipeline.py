@@ -98,9 +98,15 @@ class Step:
         csa2_topk(self.topk_scores, li.n_visible, self.k, idx, pool_blocks=self.topk_blocks)
 
     def scan_only(self, cache: Cache, li: LayerInputs):
-        """The Full layer's scan alone (block maxima into this step's buffer)."""
+        """The Full layer's scan alone, as csa2_index_full runs it: with fewer than
+        16 queries per sequence it also stores every score."""
+        scores = self.scores
+        if scores is None and self.M < 16:
+            if getattr(self, "_scan_scores", None) is None:
+                self._scan_scores = torch.empty((self.R, self.N), dtype=torch.float32, device=self.block_max.device)
+            scores = self._scan_scores
         csa2_index_scan(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, self.B, self.M,
-                        self.N, self.block_max, scores=self.scores, super_max=self.super_max)
+                        self.N, self.block_max, scores=scores, super_max=self.super_max)
 
     def attend_only(self, cache: Cache, li: LayerInputs):
         """The first layer's attention alone, over its last selection."""

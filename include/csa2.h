@@ -148,7 +148,10 @@ int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, c
  * pool equals its top-k over the pool's kb best blocks (every block ranked ahead
  * of a block holding a selected position contributes its own best position to
  * the selection, so such a block ranks within the first k), which is why only
- * those are rescored.
+ * those are rescored.  With fewer than 16 queries per sequence (decode) the scan
+ * stores every score instead (into `scores`, else the workspace) and one
+ * workgroup per row builds the pool and ranks the stored scores of its first kb
+ * blocks; the results are the same.
  *   scores, block_max  optional outputs (NULL to skip; block_max then lives in
  *                      the workspace).
  *   pool_blocks  i32[R][n_pool] required;  idx i32[R][k] or NULL (k = 0 skips).
