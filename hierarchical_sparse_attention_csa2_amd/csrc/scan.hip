@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8,
   }
   const int64_t key = p0 + lane;
   const bool vis = key < nv;
-  if (kScores && vis) scores[(int64_t)r * N_max + key] = s;
+  if (kScores && vis) __builtin_nontemporal_store(s, &scores[(int64_t)r * N_max + key]);
   const uint32_t m8 = group8_max_u32(vis ? order_key(s) : 0u);
   if ((lane & 7) == 0 && vis) block_max[(int64_t)r * nblk_stride + (key >> 3)] = key_to_float(m8);
   if (kSuper) {
