@@ -423,10 +423,11 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
     const int64_t slot = ((int64_t)r * a.splits + split) * a.H + h;
     float* op = a.part_o + slot * 512 + dbase + 4 * g;
 #pragma unroll
-    for (int m = 0; m < kM; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = oacc[m];
+    // streaming stores: the partials are read once, by the combine
+    for (int m = 0; m < kM; ++m) __builtin_nontemporal_store(oacc[m], reinterpret_cast<f32x4*>(op + 16 * m));
     if (g == 0 && part == 0) {
-      a.part_ml[2 * slot] = m_run;
-      a.part_ml[2 * slot + 1] = l_tot;
+      __builtin_nontemporal_store(m_run, &a.part_ml[2 * slot]);
+      __builtin_nontemporal_store(l_tot, &a.part_ml[2 * slot + 1]);
     }
   }
 }
