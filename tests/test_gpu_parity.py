@@ -108,6 +108,8 @@ def test_prefill_scan_bitexact(kind, B, M, N):
     (2000, 16, 512, [2000, 1999, 5]),           # pool smaller than k
     (300, 8, 64, [300, 64, 9]),
     (150000, 2048, 512, [150000, 131071, 65537]),
+    (40000, 2048, 1000, [40000, 0, 17]),       # first 1000 blocks (wide top-k tile), an empty row
+    (196608, 2048, 512, [196608, 196600, 100]),  # two-level filter with 16-byte loads
 ])
 def test_index_full_bitexact(kind, N, n_pool, k, nv):
     w = Workload("full", 99 + N + n_pool, B=3, N=N, n_pool=n_pool, k=k)
