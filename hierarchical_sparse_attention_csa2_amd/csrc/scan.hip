@@ -109,6 +109,100 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8,
   }
 }
 
+// Several queries per sequence (2 <= M < 16, e.g. a verify step over draft
+// tokens).  Grid (ceil(N_max / 256), 1, B); 7 waves per SIMD leave the loop
+// over the rows 72 registers (no spills).  Each wave loads 64 consecutive keys
+// once and scores them against all M query rows of the sequence, rows
+// r = seq * M + m: a multi-token decode reads every key once, not M times.  The
+// rows' query blocks travel in registers (lane l holds row l / 4, block l % 4)
+// and reach the matrix-core operand layout by lane shuffles, so the loop over
+// the rows issues no memory loads.  All loads are issued before any arithmetic.
+// Outputs per row: block maxima, optional super-block maxima (8 blocks) and
+// optional per-position scores.
+template <bool kScores, bool kSuper>
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(7, 7))) void index_scan_multi_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+    const int32_t* __restrict__ n_visible, int M, int64_t N_max, int64_t nblk_stride, int64_t nsup_stride,
+    float* __restrict__ scores, float* __restrict__ block_max, float* __restrict__ super_max) {
+  const int64_t seq = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15;   // key within a 16-position group (B column)
+  const int g = lane >> 4;   // block held by this lane (B K group)
+  // lane m < M: row m's visible count and scale bytes; lane l < 4M: row l / 4's
+  // query block l % 4
+  int nvl = 0;
+  uint32_t qsl = 0u;
+  u32x4_t qpiece = {0u, 0u, 0u, 0u};
+  if (lane < M) {
+    int64_t v = n_visible[seq * M + lane];
+    nvl = (int)(v < 0 ? 0 : (v > N_max ? N_max : v));
+    qsl = *reinterpret_cast<const uint32_t*>(q_scales + (seq * M + lane) * 4);
+  }
+  if (lane < 4 * M) qpiece = *reinterpret_cast<const u32x4_t*>(q_codes + (seq * M + (lane >> 2)) * 64 + 16 * (lane & 3));
+  const int64_t nv_all = (int64_t)wave_max_u32((uint32_t)nvl);   // the widest row: keys loaded for all rows
+  const int64_t p0 = (int64_t)blockIdx.x * kScanChunk + (int64_t)wave * 64;
+  if (p0 >= nv_all) return;   // no barriers below: waves leave independently
+
+  const uint8_t* kc = k_codes + seq * N_max * 64;
+  const uint8_t* ks = k_scales + seq * N_max * 4;
+  u32x4_t kb[4];
+  uint32_t ek[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int64_t p = p0 + 16 * u + c;
+    p = p < nv_all ? p : nv_all - 1;   // tail lanes re-read a visible row
+    kb[u] = load_codes16(kc + p * 64 + 16 * g);
+    ek[u] = ks[p * 4 + g];
+  }
+
+  // a row's outputs for this wave's 64 keys
+  auto emit = [&](int64_t r, int64_t nv, float s) {
+    const int64_t key = p0 + lane;
+    const bool vis = key < nv;
+    if (kScores && vis) __builtin_nontemporal_store(s, &scores[r * N_max + key]);
+    const uint32_t m8 = group8_max_u32(vis ? order_key(s) : 0u);
+    if ((lane & 7) == 0 && vis) block_max[r * nblk_stride + (key >> 3)] = key_to_float(m8);
+    if (kSuper) {
+      const uint32_t mx = wave_max_u32(m8);
+      if (lane == 0) super_max[r * nsup_stride + (p0 >> 6)] = key_to_float(mx);
+    }
+  };
+  // rows whose visible block exponents all lie in [-124, 114]: the matrix
+  // cores; the others are scored on the vector ALUs after this loop, once the
+  // keys' registers are free
+  uint32_t valu_rows = 0u;
+  for (int m = 0; m < M; ++m) {
+    const int64_t nv = __builtin_amdgcn_readlane(nvl, m);
+    if (p0 >= nv) continue;   // uniform over the wave
+    const int eq = (int)((__builtin_amdgcn_readlane(qsl, m) >> (8 * g)) & 0xFFu);
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) bad |= p0 + 16 * u + c < nv && exponent_out_of_range(eq, ek[u]);
+    if (__ballot(bad) != 0ull) {
+      valu_rows |= 1u << m;
+      continue;
+    }
+    // A operand: lane 16g + i (row i, K group g) holds query block g when i % 4 == g
+    const int src = 4 * m + g;   // the lane holding row m's block g
+    u32x4_t qa;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qa[e] = (uint32_t)__shfl((int)qpiece[e], src, 64);
+    if ((lane & 3) != g) qa = u32x4_t{0u, 0u, 0u, 0u};
+    emit(seq * M + m, nv, score_groups_mfma(qa, eq, kb, ek));
+  }
+  while (valu_rows) {
+    const int m = __builtin_ctz(valu_rows);
+    valu_rows &= valu_rows - 1u;
+    const int64_t r = seq * M + m;
+    const int64_t nv = __builtin_amdgcn_readlane(nvl, m);
+    int64_t p = p0 + lane;
+    p = p < nv ? p : nv - 1;
+    emit(r, nv, score_key_valu(q_codes + r * 64, q_scales + r * 4, kc + p * 64, ks + p * 4));
+  }
+}
+
 // Pool scan: one wave scores 8 pool blocks (64 positions) on the matrix cores,
 // with the operand layout of the Full-layer scan (group u = pool blocks 2u and
 // 2u + 1; lane 16g + c holds block g of position c & 7 of pool block
@@ -185,10 +279,21 @@ hipError_t launch_index_scan(const uint8_t* q_codes, const uint8_t* q_scales, co
     return launch_prefill_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, scores, block_max,
                                nblk_stride, super_max, nsup_stride, stream);
   if (M > 65535 || B > 65535) return hipErrorInvalidConfiguration;
-  dim3 grid((unsigned)((N_max + kScanChunk - 1) / kScanChunk), (unsigned)M, (unsigned)B);
-#define CSA2_SCAN(S, P)                                                                                        \
-  hipLaunchKernelGGL((index_scan_kernel<S, P>), grid, dim3(kScanThreads), 0, stream, q_codes, q_scales, k_codes, \
-                     k_scales, n_visible, M, N_max, nblk_stride, nsup_stride, scores, block_max, super_max)
+  const unsigned chunks = (unsigned)((N_max + kScanChunk - 1) / kScanChunk);
+  // one query per sequence: one row per workgroup; several: every key once for all rows
+  const bool multi = M > 1;
+  const dim3 grid(chunks, multi ? 1u : (unsigned)M, (unsigned)B);
+#define CSA2_SCAN(S, P)                                                                                          \
+  do {                                                                                                           \
+    if (multi)                                                                                                   \
+      hipLaunchKernelGGL((index_scan_multi_kernel<S, P>), grid, dim3(kScanThreads), 0, stream, q_codes, q_scales, \
+                         k_codes, k_scales, n_visible, M, N_max, nblk_stride, nsup_stride, scores, block_max,     \
+                         super_max);                                                                             \
+    else                                                                                                         \
+      hipLaunchKernelGGL((index_scan_kernel<S, P>), grid, dim3(kScanThreads), 0, stream, q_codes, q_scales,      \
+                         k_codes, k_scales, n_visible, M, N_max, nblk_stride, nsup_stride, scores, block_max,     \
+                         super_max);                                                                             \
+  } while (0)
   if (scores && super_max) CSA2_SCAN(true, true);
   else if (scores) CSA2_SCAN(true, false);
   else if (super_max) CSA2_SCAN(false, true);

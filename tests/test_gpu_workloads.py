@@ -16,7 +16,8 @@ from gpu_cases import dev, oracle_attn, oracle_full, say
 pytestmark = pytest.mark.gpu
 ATOL = 1e-3
 
-SAMPLES = {"c1": None, "c2": None, "c3": None, "c4": [0, 1, 31, 62, 63], "c5": [0, 1, 1000, 2047, 4094, 4095]}
+SAMPLES = {"c1": None, "c2": None, "c3": None, "c4": [0, 1, 31, 62, 63], "c5": [0, 1, 1000, 2047, 4094, 4095],
+           "v3": [0, 3, 5, 10, 15]}
 
 
 @pytest.fixture(autouse=True)
@@ -26,7 +27,7 @@ def _need_gpu():
     csa2.load_library()
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "v3"])
 def test_workload_parity(name):
     w = synth.WORKLOADS[name]
     say(f"workload {name}: {w.notes}")
