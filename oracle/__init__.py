@@ -44,6 +44,12 @@ def lib():
         L.orc_e4m3_encode.argtypes = [ctypes.c_double]
         L.orc_e4m3_encode.restype = ctypes.c_uint8
         L.orc_mxfp4_encode_block.argtypes = [vp, vp, vp]
+        L.orc_merge_f32.argtypes = [vp, vp, i64, i32, i32, vp]
+        L.orc_merge_f32.restype = ctypes.c_int
+        L.orc_cache_write_mxfp4.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+        L.orc_cache_write_mxfp4.restype = ctypes.c_int
+        L.orc_cache_write_e4m3.argtypes = [vp, i64, vp]
+        L.orc_cache_write_e4m3.restype = None
         L.orc_score.argtypes = [vp, vp, vp, vp]
         L.orc_score.restype = ctypes.c_float
         L.orc_order_key.argtypes = [ctypes.c_float]
@@ -121,6 +127,40 @@ def score(qc, qs, kc, ks) -> float:
 
 def order_key(f: float) -> int:
     return int(lib().orc_order_key(float(f)))
+
+
+# ---------------- cache write ----------------
+def merge(x, w, ratio):
+    """fp32 ratio-m merge of token rows x [n*ratio, D] with weights w [n*ratio]
+    (None: weight 1) -> [n, D] float32."""
+    x = _c(x, np.float32)
+    T, D = x.shape
+    assert T % ratio == 0
+    w = None if w is None else _c(w, np.float32)
+    out = np.empty((T // ratio, D), np.float32)
+    assert lib().orc_merge_f32(_p(x), _p(w), T // ratio, ratio, D, _p(out)) == 0
+    return out
+
+
+def cache_write_mxfp4(x, w, ratio):
+    """Merged entries of x [n*ratio, D] stored as MXFP4: (codes [n, D/2], scales [n, D/32])."""
+    x = _c(x, np.float32)
+    T, D = x.shape
+    assert T % ratio == 0
+    n = T // ratio
+    w = None if w is None else _c(w, np.float32)
+    codes = np.empty((n, D // 2), np.uint8)
+    scales = np.empty((n, D // 32), np.uint8)
+    assert lib().orc_cache_write_mxfp4(_p(x), _p(w), n, ratio, D, _p(codes), _p(scales)) == 0
+    return codes, scales
+
+
+def cache_write_e4m3(x):
+    """FP8 E4M3 code of every element of x (float32), same shape, uint8."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_cache_write_e4m3(_p(x), x.size, _p(out))
+    return out
 
 
 # ---------------- the step ----------------

@@ -24,6 +24,11 @@
  *   - attention: one softmax over the selected latent rows and the window rows,
  *     value = key, scale sm_scale, computed in double, stored as float.
  *   - scores compare by their IEEE-754 total order (-0 below +0).
+ *   - cache write: an entry at ratio m is the weighted sum of its m token rows
+ *     with the caller's per-token weights, in fp32, tokens in order, each
+ *     product rounded before its addition; the sum is then stored with the
+ *     MXFP4 encoder below (NaN elements do not count towards amax, an infinite
+ *     amax takes E = 127).
  *
  * Pins: every function here is checked in tests/ against brute force, closed
  * forms, library routines or published format tables (see the test docstrings).
@@ -450,4 +455,56 @@ int orc_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_sca
     attn_ctx c = {q, c_codes, c_scales, idx, k, win, win_start, win_len, M, H, Tw, N_max, sm_scale, out};
     parallel_rows(attn_row, &c, (int64_t)B * M, threads);
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O13: cache write (CSA2 ratio-m compression, quantize-on-write)      */
+/* ------------------------------------------------------------------ */
+/* [P2] every m consecutive tokens are stored as one entry, a merge weighted by
+   the layer's compression weights, entries do not overlap; entry e of row
+   length D is sum_j w[m e + j] x[m e + j], j = 0..m-1, in fp32 in that order
+   (this file is compiled without contraction, so the product and the sum are
+   two roundings).  w == NULL means every weight is 1. */
+int orc_merge_f32(const float* x, const float* w, int64_t n_entries, int ratio, int D, float* out) {
+    if (n_entries < 0 || ratio < 1 || D < 1) return -1;
+    for (int64_t e = 0; e < n_entries; ++e) {
+        for (int d = 0; d < D; ++d) {
+            float s = 0.0f;
+            for (int j = 0; j < ratio; ++j) {
+                int64_t tok = e * ratio + j;
+                float wj = w ? w[tok] : 1.0f;
+                float p = x[tok * (int64_t)D + d] * wj;
+                s = (j == 0) ? p : s + p;
+            }
+            out[e * (int64_t)D + d] = s;
+        }
+    }
+    return 0;
+}
+
+/* [P2] the main KV and indexer keys are stored in MXFP4: the merged entries
+   through O3, 32 elements at a time (a float is exact as a double). */
+int orc_cache_write_mxfp4(const float* x, const float* w, int64_t n_entries, int ratio, int D, uint8_t* codes,
+                          uint8_t* scales) {
+    if (D < 32 || D % 32 != 0) return -1;
+    float* m = (float*)malloc(sizeof(float) * (size_t)D);
+    if (!m) return -2;
+    double blk[32];
+    for (int64_t e = 0; e < n_entries; ++e) {
+        if (orc_merge_f32(x + e * (int64_t)ratio * D, w ? w + e * ratio : NULL, 1, ratio, D, m) != 0) {
+            free(m);
+            return -1;
+        }
+        for (int b = 0; b < D / 32; ++b) {
+            for (int i = 0; i < 32; ++i) blk[i] = (double)m[32 * b + i];
+            orc_mxfp4_encode_block(blk, codes + e * (int64_t)(D / 2) + 16 * b, scales + e * (int64_t)(D / 32) + b);
+        }
+    }
+    free(m);
+    return 0;
+}
+
+/* [P2] the sliding-window KV is stored in FP8: every value through O4. */
+void orc_cache_write_e4m3(const float* x, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode((double)x[i]);
 }

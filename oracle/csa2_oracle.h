@@ -24,6 +24,10 @@ double orc_e8m0_scale(unsigned byte);
 double orc_e4m3_value(unsigned code);
 void orc_mxfp4_encode_block(const double* x, uint8_t* codes16, uint8_t* scale);
 uint8_t orc_e4m3_encode(double x);
+int orc_merge_f32(const float* x, const float* w, int64_t n_entries, int ratio, int D, float* out);
+int orc_cache_write_mxfp4(const float* x, const float* w, int64_t n_entries, int ratio, int D, uint8_t* codes,
+                          uint8_t* scales);
+void orc_cache_write_e4m3(const float* x, int64_t n, uint8_t* out);
 float orc_score(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks);
 uint32_t orc_order_key(float f);
 

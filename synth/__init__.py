@@ -31,6 +31,10 @@ BASE_SEED = 20260919
 T_INDEX_KEYS = 1
 T_LATENT = 2
 T_MERGE_LOGITS = 3
+# fp32 token rows before the cache write (latent, indexer key, window)
+T_TOKEN_LATENT = 7
+T_TOKEN_INDEX = 8
+T_TOKEN_WINDOW = 9
 
 
 def t_index_query(layer: int) -> int:
@@ -64,6 +68,8 @@ def lib():
         L.synth_f32.argtypes = [u64, u32, u64, u64, i32, vp, i32]
         L.synth_normals.argtypes = [u64, u32, u64, u64, i32, vp]
         L.synth_merge_weights.argtypes = [u64, u32, u64, vp]
+        L.synth_merge_weights_f32.argtypes = [u64, u32, u64, u64, vp]
+        L.synth_merge_weights_f32.restype = None
         L.synth_mxfp4_encode_block.argtypes = [vp, vp, vp]
         L.synth_e4m3_encode.argtypes = [ctypes.c_double]
         L.synth_e4m3_encode.restype = ctypes.c_uint8
@@ -117,6 +123,14 @@ def merge_weights(seed, logit_tensor, row):
     w = np.empty(2, np.float64)
     lib().synth_merge_weights(seed, logit_tensor, row, _p(w))
     return w
+
+
+def merge_weights_f32(seed, logit_tensor, row0, nrows):
+    """Merge weights of entries [row0, row0+nrows) as float32, flattened per token
+    ([2*nrows]: token 2r and 2r+1 of entry row0 + r)."""
+    out = np.empty(2 * nrows, np.float32)
+    lib().synth_merge_weights_f32(seed, logit_tensor, row0, nrows, _p(out))
+    return out
 
 
 def philox(ctr, key):
@@ -235,3 +249,53 @@ def gen_layer(w: Workload, layer: int = 0, threads=None, need_index_query=True):
     d["win_start"] = w.win_start()
     d["win_len"] = w.win_len_arr()
     return d
+
+
+# ----------------------------------------------------------------------------
+# cache-write workloads
+# ----------------------------------------------------------------------------
+@dataclass
+class CacheWriteWorkload:
+    """The cache write of whole contexts: B sequences of T fp32 tokens each are
+    merged at ratio m into T/m cached entries of the 512-d latent and of the
+    128-d indexer keys (MXFP4), and each sequence's newest win_len tokens are
+    written to its FP8 window.  Tokens are iid N(0,1) rows; the ratio-2 merge
+    weights are the generator's (softmax over each pair of N(0,1) logits)."""
+    name: str
+    seed: int
+    B: int
+    T: int
+    ratio: int = 2
+    win_len: int = 128
+    notes: str = ""
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+    @property
+    def entries(self) -> int:
+        return self.tokens // self.ratio
+
+    def latent_rows(self, row0, nrows, threads=None):
+        return f32(self.seed, T_TOKEN_LATENT, row0, nrows, 512, threads)
+
+    def index_rows(self, row0, nrows, threads=None):
+        return f32(self.seed, T_TOKEN_INDEX, row0, nrows, 128, threads)
+
+    def window_rows(self, threads=None):
+        return f32(self.seed, T_TOKEN_WINDOW, 0, self.B * self.win_len, 512, threads)
+
+    def weights(self, tok0, ntok):
+        """fp32 merge weights of tokens [tok0, tok0+ntok) (whole entries)."""
+        assert self.ratio == 2 and tok0 % 2 == 0 and ntok % 2 == 0
+        return merge_weights_f32(self.seed, T_MERGE_LOGITS, tok0 // 2, ntok // 2)
+
+
+CACHE_WRITES = {
+    # the cached state of c3 (4 sequences x 1,048,576 tokens at ratio 2) written
+    # from its fp32 tokens
+    "w3": CacheWriteWorkload("w3_cache_write_b4_1m_ratio2", BASE_SEED + 2, B=4, T=1048576, ratio=2,
+                             notes="cache write of 4 x 1,048,576 tokens at ratio 2: 2,097,152 latent (512-d) and "
+                                   "indexer-key (128-d) MXFP4 entries + 4 x 128 FP8 window rows"),
+}

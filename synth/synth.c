@@ -271,3 +271,14 @@ void synth_merge_weights(uint64_t seed, uint32_t logit_tensor, uint64_t row, dou
     w[0] = e0 / (e0 + e1);
     w[1] = e1 / (e0 + e1);
 }
+
+/* merge weights of entries [row0, row0 + nrows) as float32 pairs:
+   out[2r], out[2r+1] = (float)w0, (float)w1 of entry row0 + r */
+void synth_merge_weights_f32(uint64_t seed, uint32_t logit_tensor, uint64_t row0, uint64_t nrows, float* out) {
+    double w[2];
+    for (uint64_t r = 0; r < nrows; ++r) {
+        synth_merge_weights(seed, logit_tensor, row0 + r, w);
+        out[2 * r] = (float)w[0];
+        out[2 * r + 1] = (float)w[1];
+    }
+}
