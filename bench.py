@@ -43,6 +43,12 @@ COUNTERS = os.path.join(ROOT, "profiles", "index_scan_kernel_c3_hbm_counters.txt
 SCAN_SOURCES = ("hierarchical_sparse_attention_csa2_amd/csrc/scan.hip",
                 "hierarchical_sparse_attention_csa2_amd/csrc/score_core.h",
                 "hierarchical_sparse_attention_csa2_amd/csrc/device_common.h")
+WRITE_KERNEL = "write_mxfp4_kernel<2>"   # ratio-2 merge + MXFP4 quantize of the 512-d latent
+WRITE_COUNTERS = os.path.join(ROOT, "profiles", "write_mxfp4_kernel_w3_hbm_counters.txt")
+WRITE_SOURCES = ("hierarchical_sparse_attention_csa2_amd/csrc/cache_write.hip",
+                 "hierarchical_sparse_attention_csa2_amd/csrc/device_common.h")
+# per workload: the committed counter summary, the sources it was taken on, the kernel it covers
+TRAFFIC = {"c3": (COUNTERS, SCAN_SOURCES, SCAN_KERNEL), "w3": (WRITE_COUNTERS, WRITE_SOURCES, WRITE_KERNEL)}
 
 
 def log(*a):
@@ -106,23 +112,27 @@ def cpu_baseline(w, cache, lays, seconds):
 
 
 def measured_traffic(workload):
-    """HBM bytes per scan launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary (copy-calibrated), or None when that summary does not cover this
-    workload or the scan's source has changed since the counters were taken."""
+    """HBM bytes per launch of the workload's dominant kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary (copy-calibrated), or None when no
+    summary covers this workload or the kernel's source has changed since the
+    counters were taken."""
     import hashlib
 
-    if workload != "c3" or not os.path.exists(COUNTERS):
+    if workload not in TRAFFIC:
         return None
-    text = open(COUNTERS).read()
+    path, sources, kernel = TRAFFIC[workload]
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
     h = hashlib.sha256()
-    for f in SCAN_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     fields = dict(line.split(": ", 1) for line in text.splitlines()
                   if line.startswith(("source-sha256", "traffic_bytes_per_launch", "kernel")))
     if not any(v.strip() == h.hexdigest() for k, v in fields.items() if k.startswith("source-sha256")):
         return None
-    if fields.get("kernel", "").strip() != SCAN_KERNEL:
+    if fields.get("kernel", "").strip() != kernel:
         return None
     return float(fields["traffic_bytes_per_launch"])
 
@@ -150,12 +160,126 @@ def capture(fn, torch):
     return g
 
 
+def cache_write_cpu_baseline(cw, seconds):
+    """The oracle's cache write as it stands, on this host, over the first tokens
+    of the same workload (latent and indexer-key rows), repeated until `seconds`."""
+    import oracle
+
+    n = 8192
+    x_lat, x_idx, wts = cw.latent_rows(0, n), cw.index_rows(0, n), cw.weights(0, n)
+    reps = 0
+    t0 = time.time()
+    while True:
+        oracle.cache_write_mxfp4(x_lat, wts, cw.ratio)
+        oracle.cache_write_mxfp4(x_idx, wts, cw.ratio)
+        reps += 1
+        el = time.time() - t0
+        if el >= seconds:
+            break
+    return {"value": n * reps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} pass(es) over the first {n} tokens of the workload (512-d latent and 128-d "
+                      f"indexer-key rows merged at ratio {cw.ratio} and quantized; the window rows, 0.01% of the "
+                      f"bytes, left out), {el:.1f} s on 1 host thread"}
+
+
+def bench_cache_write(args, torch):
+    """The cache write of whole contexts: one step merges and quantizes every
+    token of the B sequences (latent and indexer keys) and writes each
+    sequence's newest window rows, with the fp32 tokens resident in HBM."""
+    import hierarchical_sparse_attention_csa2_amd as csa2
+    import synth
+
+    cw = synth.CACHE_WRITES[args.workload]
+    T, E = cw.tokens, cw.entries
+    t0 = time.time()
+    x_lat = torch.empty((T, 512), dtype=torch.float32, device="cuda")
+    x_idx = torch.empty((T, 128), dtype=torch.float32, device="cuda")
+    wts = torch.empty(T, dtype=torch.float32, device="cuda")
+    chunk = 1 << 18
+    for r0 in range(0, T, chunk):
+        n = min(chunk, T - r0)
+        x_lat[r0:r0 + n].copy_(torch.from_numpy(cw.latent_rows(r0, n)))
+        x_idx[r0:r0 + n].copy_(torch.from_numpy(cw.index_rows(r0, n)))
+        wts[r0:r0 + n].copy_(torch.from_numpy(cw.weights(r0, n)))
+    x_win = torch.from_numpy(cw.window_rows()).cuda()
+    c_codes = torch.empty((E, 256), dtype=torch.uint8, device="cuda")
+    c_scales = torch.empty((E, 16), dtype=torch.uint8, device="cuda")
+    k_codes = torch.empty((E, 64), dtype=torch.uint8, device="cuda")
+    k_scales = torch.empty((E, 4), dtype=torch.uint8, device="cuda")
+    win = torch.empty((cw.B * cw.win_len, 512), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"workload {cw.name}: {cw.notes}; inputs generated and uploaded in {time.time() - t0:.1f} s")
+
+    write_latent = lambda i=0: csa2.csa2_cache_write_mxfp4(x_lat, wts, cw.ratio, c_codes, c_scales)
+    write_index = lambda i=0: csa2.csa2_cache_write_mxfp4(x_idx, wts, cw.ratio, k_codes, k_scales)
+    write_window = lambda i=0: csa2.csa2_cache_write_e4m3(x_win, win)
+
+    def step(i=0):
+        write_latent()
+        write_index()
+        write_window()
+
+    for i in range(args.warmup):
+        step(i)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    lat_ms = time_back_to_back(write_latent, args.steps, torch)
+    idx_ms = time_back_to_back(write_index, args.steps, torch)
+    # algorithmic bytes: every fp32 token row and weight read once, every entry written once
+    lat_bytes = T * (512 * 4 + 4) + E * (256 + 16)
+    idx_bytes = T * (128 * 4 + 4) + E * (64 + 4)
+    win_bytes = cw.B * cw.win_len * 512 * 5
+    step_bytes = lat_bytes + idx_bytes + win_bytes
+    roof = {"kernel": WRITE_KERNEL, "bound": "hbm", "achieved": lat_bytes / (lat_ms / 1e3) / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": measured_traffic(args.workload),
+            "traffic_unit": "bytes/launch", "algorithmic_bytes_per_launch": lat_bytes,
+            "avg_launch_us": lat_ms * 1e3}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    log(f"step {ms_per_step * 1e3:.1f} us ({step_bytes / (ms_per_step / 1e3) / 1e9:.0f} GB/s over the step), "
+        f"latent write {lat_ms * 1e3:.1f} us -> {roof['achieved']:.0f} GB/s, index-key write {idx_ms * 1e3:.1f} us "
+        f"-> {idx_bytes / (idx_ms / 1e3) / 1e9:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cache_write_cpu_baseline(cw, args.cpu_seconds)
+        log(f"cpu oracle {cpu['value']:.0f} tokens/s ({cpu['sample']})")
+    out = {
+        "metric": "cache-write tokens/s (ratio-2 merge + MXFP4 / FP8 quantize-on-write); HBM GB/s vs peak",
+        "value": T / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) fp32 tokens, softmax-of-N(0,1) merge weights)",
+        "config": {"workload": cw.name, "batch": cw.B, "tokens_per_sequence": cw.T, "compression_ratio": cw.ratio,
+                   "entries": E, "latent_dim": 512, "index_dim": 128, "window_rows": cw.B * cw.win_len,
+                   "step_bytes": step_bytes},
+        "roofline": roof,
+        "index_key_write": {"kernel": WRITE_KERNEL, "avg_launch_us": idx_ms * 1e3,
+                            "algorithmic_bytes": idx_bytes, "gbs": idx_bytes / (idx_ms / 1e3) / 1e9},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "v3"])
+    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "v3", "w3"],
+                    help="c1..c5, v3: attention-layer steps; w3: the cache write of c3's context")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 512 MiB of index keys in rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -192,6 +316,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    if args.workload in synth.CACHE_WRITES:
+        bench_cache_write(args, torch)
         return
 
     w = synth.WORKLOADS[args.workload]

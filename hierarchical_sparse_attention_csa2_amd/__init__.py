@@ -35,7 +35,8 @@ CSA2_OP_SPARSE_ATTN = 2
 
 EXPORTED = (
     "csa2_index_scan", "csa2_select_blocks", "csa2_index_pool", "csa2_topk", "csa2_index_full",
-    "csa2_sparse_attn", "csa2_workspace_bytes", "csa2_status_string",
+    "csa2_sparse_attn", "csa2_cache_write_mxfp4", "csa2_cache_write_e4m3", "csa2_workspace_bytes",
+    "csa2_status_string",
 )
 
 _lib = None
@@ -64,12 +65,14 @@ def load_library(path: str = LIB_PATH):
     L.csa2_index_full.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.csa2_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i64, i32, i32, f32, vp, vp, sz,
                                    vp]
+    L.csa2_cache_write_mxfp4.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
+    L.csa2_cache_write_e4m3.argtypes = [vp, i64, vp, vp]
     L.csa2_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32]
     L.csa2_workspace_bytes.restype = sz
     L.csa2_status_string.argtypes = [i32]
     L.csa2_status_string.restype = ctypes.c_char_p
     for f in ("csa2_index_scan", "csa2_select_blocks", "csa2_index_pool", "csa2_topk", "csa2_index_full",
-              "csa2_sparse_attn"):
+              "csa2_sparse_attn", "csa2_cache_write_mxfp4", "csa2_cache_write_e4m3"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -223,3 +226,28 @@ def csa2_sparse_attn(q, c_codes, c_scales, idx, win, win_start, win_len, win_max
         _dev(workspace, "workspace", U8, optional=True) if workspace is not None else None,
         workspace.numel() if workspace is not None else 0, _stream(stream))
     _check("csa2_sparse_attn", st)
+
+
+def csa2_cache_write_mxfp4(x, w, ratio, codes, scales, stream=None):
+    """Merge every `ratio` consecutive token rows of x [n*ratio, D] with weights
+    w [n*ratio] (None only for ratio 1) and write the MXFP4 entries into codes
+    [n, D/2] and scales [n, D/32] (contiguous views into a cache are fine)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, D]")
+    T, D = x.shape
+    if ratio < 1 or T % ratio:
+        raise ValueError(f"{T} token rows do not split into groups of {ratio}")
+    n = T // ratio
+    st = load_library().csa2_cache_write_mxfp4(
+        _dev(x, "x", F32), _dev(w, "w", F32, (T,), optional=ratio == 1), n, int(ratio), D,
+        _dev(codes, "codes", U8, numel=n * (D // 2)), _dev(scales, "scales", U8, numel=n * (D // 32)),
+        _stream(stream))
+    _check("csa2_cache_write_mxfp4", st)
+
+
+def csa2_cache_write_e4m3(x, out, stream=None):
+    """FP8 E4M3 codes of every element of x (e.g. window rows [rows, 512]) into
+    out (uint8, same number of elements)."""
+    n = x.numel()
+    st = load_library().csa2_cache_write_e4m3(_dev(x, "x", F32), n, _dev(out, "out", U8, numel=n), _stream(stream))
+    _check("csa2_cache_write_e4m3", st)

@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcsa2.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["scan.hip", "prefill_scan.hip", "select.hip", "attn.hip", "csa2_abi.hip"]
+SOURCES = ["scan.hip", "prefill_scan.hip", "select.hip", "attn.hip", "cache_write.hip", "csa2_abi.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

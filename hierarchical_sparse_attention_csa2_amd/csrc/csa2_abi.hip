@@ -47,6 +47,9 @@ inline bool any_misaligned(const P*... p) {
 constexpr int64_t kMaxRows = 1 << 24;
 constexpr int64_t kMaxN = (int64_t)1 << 30;   // ids are int32; 8*blocks must fit
 constexpr int kMaxPool = 1 << 20;
+constexpr int kMaxRatio = 64;                          // tokens merged into one cached entry
+constexpr int kMaxWriteDim = 1 << 14;                  // elements per cached row
+constexpr int64_t kMaxWriteElems = (int64_t)1 << 40;   // fp32 input elements of one write call
 
 }  // namespace
 
@@ -212,6 +215,30 @@ int csa2_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_sc
   L.workspace = workspace;
   L.workspace_bytes = workspace_bytes;
   return hip_status(csa2::launch_sparse_attn(L, as_stream(stream)));
+}
+
+int csa2_cache_write_mxfp4(const float* x, const float* w, int64_t n_entries, int ratio, int D, uint8_t* codes,
+                           uint8_t* scales, void* stream) {
+  if (n_entries < 0 || ratio < 1 || ratio > kMaxRatio || D < 32 || D > kMaxWriteDim || (D & (D - 1)) != 0)
+    return CSA2_ERR_INVALID;
+  if (n_entries == 0) return CSA2_OK;   // nothing to write: pointers unused
+  if (!x || !codes || !scales) return CSA2_ERR_INVALID;
+  // entries are appended at any offset of a cache, so only what the kernel
+  // moves in vectors is held to 16 bytes: the fp32 rows (codes go out as
+  // 2-byte words, weights as floats, scales as bytes)
+  if (misaligned(x) || (reinterpret_cast<uintptr_t>(w) & 3u) != 0 || (reinterpret_cast<uintptr_t>(codes) & 1u) != 0)
+    return CSA2_ERR_INVALID;
+  if (ratio > 1 && !w) return CSA2_ERR_INVALID;
+  if (n_entries > kMaxWriteElems / ((int64_t)ratio * D)) return CSA2_ERR_INVALID;
+  return hip_status(csa2::launch_write_mxfp4(x, w, n_entries, ratio, D, codes, scales, as_stream(stream)));
+}
+
+int csa2_cache_write_e4m3(const float* x, int64_t n, uint8_t* out, void* stream) {
+  if (n < 0 || n % 4 != 0 || n > kMaxWriteElems) return CSA2_ERR_INVALID;
+  if (n == 0) return CSA2_OK;
+  if (!x || !out) return CSA2_ERR_INVALID;
+  if (misaligned(x) || (reinterpret_cast<uintptr_t>(out) & 3u) != 0) return CSA2_ERR_INVALID;
+  return hip_status(csa2::launch_write_e4m3(x, n, out, as_stream(stream)));
 }
 
 size_t csa2_workspace_bytes(int op, int B, int M, int64_t N_max, int H, int k) {

@@ -46,6 +46,13 @@ hipError_t launch_select_topk(const float* bmax, int64_t stride, const float* su
                               const int32_t* n_visible, int R, int n_pool, int32_t* pool_out, int kb,
                               const float* scores, int64_t n_max, int k, int32_t* idx, hipStream_t stream);
 
+// Cache write: ratio-m weighted merge of fp32 token rows (D a power of two,
+// >= 32) quantized to MXFP4 codes and E8M0 scales; and fp32 -> FP8 E4M3 of n
+// elements (n % 4 == 0).
+hipError_t launch_write_mxfp4(const float* x, const float* w, int64_t n_entries, int ratio, int D, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream);
+hipError_t launch_write_e4m3(const float* x, int64_t n, uint8_t* out, hipStream_t stream);
+
 struct AttnLaunch {
   const float* q;
   const uint8_t* c_codes;

@@ -189,6 +189,50 @@ int csa2_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_sc
                      float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * csa2_cache_write_mxfp4 - the cache write of a CSA2 layer at compression
+ * ratio m (fupanwang.com article, section "三个方向一起压小缓存": every m
+ * consecutive tokens become one cached entry, entries do not overlap, the merge
+ * is weighted by the layer's compression weights; the main KV and the indexer
+ * keys are stored in OCP MXFP4):
+ *     entry e = sum_{j=0..m-1} w[m*e + j] * x[m*e + j]
+ * in fp32, j ascending, each product rounded and then added (no fused
+ * multiply-add), then each 32-element block quantized: E = floor(log2 amax) - 2
+ * clamped to [-127, 127], scale byte E + 127, elements x / 2^E rounded to the
+ * nearest E2M1 value (ties to the even code, saturating at 6, a negative value
+ * that rounds to zero stored as +0).  An all-zero block stores scale byte 0 and
+ * zero codes; NaN elements are ignored by amax and stored as +0; an infinite
+ * amax takes E = 127 (infinite elements store +-6).
+ *   x       f32[n_entries*m][D] token rows (D a power of two, 32 <= D <= 16384:
+ *           128 for indexer keys, 512 for the latent)
+ *   w       f32[n_entries*m] per-token compression weights (the caller's, e.g.
+ *           a softmax over each group of m logits); may be NULL only for m = 1
+ *           (weight 1: the row is quantized as is)
+ *   codes   u8[n_entries][D/2], scales u8[n_entries][D/32] (the cached layout
+ *           of the entries: pass k_codes + e0*64 etc. to write entries from e0)
+ *   ratio   m, 1..64
+ * Alignment (the exception to the 16-byte rule, so that entries can be written
+ * at any offset of a cache): x 16 bytes, w 4 bytes, codes 2 bytes, scales any.
+ * Returns CSA2_OK, CSA2_ERR_INVALID (NULL pointer, misaligned pointer, D not a
+ * power of two in range, ratio out of range, w NULL with m > 1,
+ * n_entries < 0), CSA2_ERR_HIP.  n_entries = 0 returns CSA2_OK without
+ * launching or looking at the pointers.
+ */
+int csa2_cache_write_mxfp4(const float* x, const float* w, int64_t n_entries, int ratio, int D,
+                           uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * csa2_cache_write_e4m3 - quantize-on-write of sliding-window rows to FP8
+ * (same section: the sliding-window KV stays FP8): each of the n fp32 values
+ * to OCP E4M3FN, nearest value with ties to the even code, saturating at +-448
+ * (infinities too), NaN to 0x7F.
+ *   x  f32[n] (16-byte aligned), out u8[n] (4-byte aligned; e.g. window rows:
+ *      n = rows * 512), n % 4 == 0.
+ * Returns CSA2_OK, CSA2_ERR_INVALID (NULL or misaligned pointer, n < 0,
+ * n % 4 != 0), CSA2_ERR_HIP.  n = 0 returns CSA2_OK without launching.
+ */
+int csa2_cache_write_e4m3(const float* x, int64_t n, uint8_t* out, void* stream);
+
+/*
  * csa2_workspace_bytes - device workspace needed by an entry point.
  *   CSA2_OP_INDEX_FULL:  (B, M, N_max, k) as passed to csa2_index_full (H unused)
  *   CSA2_OP_SPARSE_ATTN: (B, M, -, H, k + win_max)

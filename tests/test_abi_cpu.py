@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "csa2.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -91,6 +91,35 @@ def test_validation_rejects_misaligned_pointers():
     assert L.csa2_index_full(P, P, P, P, P, 1, 1, 64, 4, 8, NULL, NULL, P, P, Q, 1 << 20, NULL) == -1
     assert L.csa2_sparse_attn(Q, P, P, P, 8, P, P, P, 4, 1, 1, 64, 64, 8, f, P, P, 1 << 20, NULL) == -1
     assert L.csa2_sparse_attn(P, P, P, P, 8, P, P, P, 4, 1, 1, 64, 64, 8, f, Q, P, 1 << 20, NULL) == -1
+
+
+def test_cache_write_validation():
+    """The cache-write entry points check sizes, NULLs and alignment before any launch."""
+    L = csa2.load_library()
+    Q = ctypes.c_void_p(0x1004)
+    # D must be a power of two in [32, 16384]; ratio in [1, 64]; weights needed for ratio > 1
+    assert L.csa2_cache_write_mxfp4(P, P, 4, 2, 96, P, P, NULL) == -1
+    assert L.csa2_cache_write_mxfp4(P, P, 4, 2, 16, P, P, NULL) == -1
+    assert L.csa2_cache_write_mxfp4(P, P, 4, 2, 32768, P, P, NULL) == -1
+    assert L.csa2_cache_write_mxfp4(P, P, 4, 0, 128, P, P, NULL) == -1
+    assert L.csa2_cache_write_mxfp4(P, P, 4, 65, 128, P, P, NULL) == -1
+    assert L.csa2_cache_write_mxfp4(P, NULL, 4, 2, 128, P, P, NULL) == -1
+    assert L.csa2_cache_write_mxfp4(P, P, -1, 2, 128, P, P, NULL) == -1
+    assert L.csa2_cache_write_mxfp4(NULL, P, 4, 2, 128, P, P, NULL) == -1
+    assert L.csa2_cache_write_mxfp4(P, P, 4, 2, 128, NULL, P, NULL) == -1
+    assert L.csa2_cache_write_mxfp4(Q, P, 4, 2, 128, P, P, NULL) == -1                    # x: 16 bytes
+    assert L.csa2_cache_write_mxfp4(P, ctypes.c_void_p(0x1002), 4, 2, 128, P, P, NULL) == -1   # w: 4 bytes
+    assert L.csa2_cache_write_mxfp4(P, P, 4, 2, 128, ctypes.c_void_p(0x1001), P, NULL) == -1   # codes: 2 bytes
+    # nothing to write: no launch, success (ratio 1 may omit the weights)
+    assert L.csa2_cache_write_mxfp4(P, NULL, 0, 1, 128, P, P, NULL) == 0
+    assert L.csa2_cache_write_e4m3(P, 6, P, NULL) == -1
+    assert L.csa2_cache_write_e4m3(P, -4, P, NULL) == -1
+    assert L.csa2_cache_write_e4m3(NULL, 8, P, NULL) == -1
+    assert L.csa2_cache_write_e4m3(Q, 8, P, NULL) == -1
+    assert L.csa2_cache_write_e4m3(P, 8, ctypes.c_void_p(0x1002), NULL) == -1
+    assert L.csa2_cache_write_e4m3(P, 0, P, NULL) == 0
+    assert L.csa2_cache_write_e4m3(NULL, 0, NULL, NULL) == 0
+    assert L.csa2_cache_write_mxfp4(NULL, NULL, 0, 2, 128, NULL, NULL, NULL) == 0
 
 
 def test_workspace_bytes():
