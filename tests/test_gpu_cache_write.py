@@ -2,8 +2,11 @@
 window quantize-on-write) through the C ABI against the oracle: codes and
 scale bytes must be bit-exact.
 
-Cases span several workgroups with ragged tails (the kernel's tile is 1,024
-four-element quads), every ratio code path (1, 2 and 4 compiled, others
+Cases span several workgroups with ragged tails (a workgroup takes 256
+four-element quads; tiles are handed out in groups of 512 so that each XCD
+streams 64 consecutive tiles, and a last partial group keeps launch order, so
+the larger cases cover full and partial groups), every ratio code path (1, 2
+and 4 compiled, others
 generic), both row widths the cached state uses (128 index-key elements, 512
 latent elements) and edge values: E2M1 midpoints and their neighbours, zero,
 subnormal, huge, infinite and NaN blocks, exponent clamps at both ends.
@@ -66,7 +69,7 @@ def _check(x, w, ratio):
 
 @pytest.mark.parametrize("n,ratio,D", [
     (1, 1, 32), (3, 2, 128), (37, 2, 512), (1000, 1, 128), (517, 3, 64), (64, 4, 512), (5, 8, 256),
-    (2049, 2, 128), (300, 1, 512), (8, 64, 32)])
+    (2049, 2, 128), (300, 1, 512), (8, 64, 32), (1100, 2, 512), (9000, 1, 128), (1025, 3, 512)])
 def test_cache_write_mxfp4_random(n, ratio, D):
     say(f"cache write n={n} ratio={ratio} D={D}")
     x = synth.f32(100 + n, synth.T_TOKEN_LATENT, 0, n * ratio, D)
@@ -182,7 +185,7 @@ def test_cache_write_e4m3_all_decision_points():
     assert bad.size == 0, f"{bad.size} mismatches, first x={x[bad[0]]!r} got {got[bad[0]]:#x} want {want[bad[0]]:#x}"
 
 
-@pytest.mark.parametrize("rows", [1, 3, 128, 1001])
+@pytest.mark.parametrize("rows", [1, 3, 128, 1001, 1100])
 def test_cache_write_e4m3_window_rows(rows):
     x = synth.f32(7 + rows, synth.T_TOKEN_WINDOW, 0, rows, 512)
     out = torch.empty((rows, 512), dtype=torch.uint8, device="cuda")
