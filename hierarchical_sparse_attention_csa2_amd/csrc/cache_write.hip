@@ -32,17 +32,7 @@ namespace csa2 {
 
 constexpr int kWriteThreads = 256;                 // one quad per lane
 constexpr int64_t kWriteTile = kWriteThreads;       // quads per workgroup
-constexpr int64_t kXcdRun = 64;                     // consecutive tiles per XCD turn
-
-// Tile of workgroup `bid`: workgroup bid runs on XCD bid % 8, so within each
-// group of 8 * kXcdRun tiles XCD k takes the k-th run of kXcdRun consecutive
-// tiles; a last partial group keeps launch order.  A bijection on [0, grid).
-__device__ __forceinline__ int64_t write_tile(int64_t bid, int64_t grid) {
-  const int64_t g = bid / (8 * kXcdRun);
-  if ((g + 1) * 8 * kXcdRun > grid) return bid;
-  const int64_t r = bid - g * 8 * kXcdRun;
-  return g * 8 * kXcdRun + (r % 8) * kXcdRun + r / 8;
-}
+constexpr int kXcdRun = 64;                         // consecutive tiles per XCD turn
 
 // max over lanes 8g..8g+7 (DPP: swap neighbours, swap pairs, mirror halves of
 // each group of 8)
@@ -123,7 +113,7 @@ __global__ __launch_bounds__(kWriteThreads) void write_mxfp4_kernel(const float*
                                                                     uint8_t* __restrict__ codes,
                                                                     uint8_t* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
-  const int64_t q = write_tile(blockIdx.x, gridDim.x) * kWriteTile + threadIdx.x;
+  const int64_t q = xcd_run_tile<kXcdRun>(blockIdx.x, gridDim.x) * kWriteTile + threadIdx.x;
   // the last tile is ragged: lanes past the end read quad 0 and store nothing
   const bool on = q < n_quads;
   const int64_t qq = on ? q : 0;
@@ -167,7 +157,7 @@ __global__ __launch_bounds__(kWriteThreads) void write_mxfp4_kernel(const float*
 
 __global__ __launch_bounds__(kWriteThreads) void write_e4m3_kernel(const float* __restrict__ x, int64_t n_quads,
                                                                    uint8_t* __restrict__ out) {
-  const int64_t q = write_tile(blockIdx.x, gridDim.x) * kWriteTile + threadIdx.x;
+  const int64_t q = xcd_run_tile<kXcdRun>(blockIdx.x, gridDim.x) * kWriteTile + threadIdx.x;
   if (q >= n_quads) return;
   const f32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(x + 4 * q));
   *reinterpret_cast<uint32_t*>(out + 4 * q) =

@@ -139,4 +139,18 @@ __device__ __forceinline__ void load_query_block(const uint8_t* codes16, half2_t
   }
 }
 
+// Workgroups of a launch are dealt to the 8 XCDs in turn (workgroup i runs on
+// XCD i % 8 when the grid's x extent is a multiple of 8).  For streaming
+// kernels, xcd_run_tile<kRun>(blockIdx.x, gridDim.x) gives the tile workgroup
+// bid should take so that each XCD streams runs of kRun consecutive tiles:
+// within each full group of 8 * kRun tiles, XCD k takes the k-th run; a last
+// partial group keeps launch order.  A bijection on [0, grid).
+template <int kRun>
+__device__ __forceinline__ int64_t xcd_run_tile(int64_t bid, int64_t grid) {
+  const int64_t g = bid / (8 * kRun);
+  if ((g + 1) * 8 * kRun > grid) return bid;
+  const int64_t r = bid - g * 8 * kRun;
+  return g * 8 * kRun + (r % 8) * kRun + r / 8;
+}
+
 }  // namespace csa2

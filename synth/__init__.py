@@ -211,11 +211,12 @@ WORKLOADS = {
     "c5": Workload("c5_prefill_4096_on_262144", BASE_SEED + 4, B=1, N=266240, M=4096,
                    prefill_base=262144,
                    notes="prefill chunk of 4,096 causal queries at positions 262,144..266,239"),
-    # multi-token decode (a verify step of 4 draft tokens) on the 1M-token cache
-    # of c3: the 4 queries of a sequence see entries up to their own positions
-    "v3": Workload("v3_verify_b4_m4_1m_ratio2", BASE_SEED + 2, B=4, N=524288, M=4, ratio=2,
-                   prefill_base=524288 - 4,
-                   notes="Full layer, 4 sequences x 4 causal decode queries (a verify step), 1,048,576 tokens "
+    # multi-token decode (a verify step over the drafter's 5 positions) on the
+    # 1M-token cache of c3: the 5 queries of a sequence see entries up to their
+    # own positions
+    "v3": Workload("v3_verify_b4_m5_1m_ratio2", BASE_SEED + 2, B=4, N=524288, M=5, ratio=2,
+                   prefill_base=524288 - 5,
+                   notes="Full layer, 4 sequences x 5 causal decode queries (a verify step), 1,048,576 tokens "
                          "at ratio 2 = 524,288 entries"),
 }
 

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 ATOL = 1e-3
 
 SAMPLES = {"c1": None, "c2": None, "c3": None, "c4": [0, 1, 31, 62, 63], "c5": [0, 1, 1000, 2047, 4094, 4095],
-           "v3": [0, 3, 5, 10, 15]}
+           "v3": [0, 4, 7, 13, 19]}
 
 
 @pytest.fixture(autouse=True)
