@@ -305,6 +305,36 @@ def test_chain_full_reindex_reindex_reuse():
     assert torch.equal(again, outs[3])
 
 
+@pytest.mark.parametrize("M", [5, 40])
+def test_chain_many_queries_per_sequence(M):
+    """Full -> Reindex -> Reuse with M causal query rows per sequence: M = 5 is a
+    verify step (multi-token decode scan), M = 40 a prefill chunk (the many-query
+    scan); the Reindex layer rescores the Full pool of each row with its own
+    query, the Reuse layer takes the Reindex indices."""
+    N = 20000
+    w = Workload("chainM", 97 + M, B=2, N=N, M=M, prefill_base=N - M, layers=("full", "reindex", "reuse"))
+    cache, lays = host_inputs(w, layers=3)
+    c = dev(cache)
+    ls = [dev(d) for d in lays]
+    say(f"chain M={M}")
+    st = pipeline.Step(w.layers, w.B, w.M, w.N, win_max=w.win_len)
+    pool, idxs, outs = st.run(pipeline.cache_from(c), [pipeline.layer_from(d) for d in ls])
+    torch.cuda.synchronize()
+    ref_full = oracle_full(w, cache, lays[0])
+    assert np.array_equal(pool.cpu().numpy(), ref_full["pool_blocks"])
+    ps = oracle.index_pool(lays[1]["q_codes"], lays[1]["q_scales"], cache["k_codes"], cache["k_scales"],
+                           ref_full["pool_blocks"], lays[1]["n_visible"], w.B, w.M, w.N)
+    ref_idx = [ref_full["idx"], oracle.topk_pool(ps, ref_full["pool_blocks"], lays[1]["n_visible"], w.k)]
+    ref_idx.append(ref_idx[1])
+    for L in range(2):
+        assert np.array_equal(idxs[L].cpu().numpy(), ref_idx[L]), L
+    for L in range(3):
+        ref = oracle_attn(w, cache, lays[L], ref_idx[L])
+        err = np.max(np.abs(outs[L].cpu().numpy() - ref))
+        say(f"chain M={M} layer {L} max abs err {err:.3e}")
+        assert err <= ATOL
+
+
 def test_deterministic_reruns():
     w = Workload("det", 55, B=4, N=60000)
     cache, (lay,) = host_inputs(w, kind="ties")
