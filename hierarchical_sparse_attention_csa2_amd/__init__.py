@@ -111,12 +111,61 @@ def _dev(t, name, dtype, shape=None, numel=None, optional=False):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if numel is not None and t.numel() != numel:
         raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if _recording is not None:
+        _recording_keep.append(t)   # a recorded call's tensors live as long as its replay
     return ctypes.c_void_p(t.data_ptr())
 
 
 def _check(fn, status):
     if status != CSA2_OK:
         raise Csa2Error(fn, status)
+
+
+_recording = None
+_recording_keep = None
+
+
+def _call(name, *args):
+    """Call C entry point `name` with marshalled arguments, or, inside
+    recording(), append the call for a later replay instead."""
+    fn = getattr(load_library(), name)
+    if _recording is not None:
+        _recording.append((name, fn, args))
+        return
+    _check(name, fn(*args))
+
+
+class recording:
+    """Context manager: the entry points called inside it are validated and
+    marshalled as usual but not run; `launches` then issues them again, in
+    order, with the same raw arguments (device pointers and the stream that was
+    current when they were recorded), so the tensors they name must stay alive
+    and in place.  For tight launch loops where the per-call checks cost more
+    host time than the kernels take."""
+
+    def __enter__(self):
+        global _recording, _recording_keep
+        if _recording is not None:
+            raise RuntimeError("recording() does not nest")
+        _recording = self.calls = []
+        _recording_keep = self.keep = []
+        return self
+
+    def __exit__(self, *exc):
+        global _recording, _recording_keep
+        _recording = _recording_keep = None
+        return False
+
+    def launches(self):
+        calls, keep = list(self.calls), list(self.keep)
+
+        def issue():
+            for name, fn, args in calls:
+                st = fn(*args)
+                if st != CSA2_OK:
+                    raise Csa2Error(name, st)
+        issue.tensors = keep   # the recorded tensors (workspaces included) live as long as `issue`
+        return issue
 
 
 U8, I32, F32 = torch.uint8, torch.int32, torch.float32
@@ -134,36 +183,33 @@ def csa2_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max
     R = B * M
     nblk = (N_max + 7) // 8
     nsup = (N_max + 63) // 64
-    st = load_library().csa2_index_scan(
+    _call("csa2_index_scan", 
         _dev(q_codes, "q_codes", U8, (R, 64)), _dev(q_scales, "q_scales", U8, (R, 4)),
         _dev(k_codes, "k_codes", U8, numel=B * N_max * 64), _dev(k_scales, "k_scales", U8, numel=B * N_max * 4),
         _dev(n_visible, "n_visible", I32, (R,)), B, M, N_max,
         _dev(scores, "scores", F32, (R, N_max), optional=True), _dev(block_max, "block_max", F32, (R, nblk)),
         _dev(super_max, "super_max", F32, (R, nsup), optional=True), _stream(stream))
-    _check("csa2_index_scan", st)
 
 
 def csa2_select_blocks(block_max, n_visible, n_pool, pool_blocks, k_blocks=0, topk_blocks=None, super_max=None,
                        stream=None):
     R, stride = block_max.shape
-    st = load_library().csa2_select_blocks(
+    _call("csa2_select_blocks", 
         _dev(block_max, "block_max", F32), _dev(super_max, "super_max", F32, (R, (stride + 7) // 8), optional=True),
         stride, _dev(n_visible, "n_visible", I32, (R,)), R, n_pool,
         _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), k_blocks,
         _dev(topk_blocks, "topk_blocks", I32, (R, k_blocks), optional=k_blocks == 0), _stream(stream))
-    _check("csa2_select_blocks", st)
 
 
 def csa2_index_pool(q_codes, q_scales, k_codes, k_scales, pool_blocks, n_visible, B, M, N_max, pool_scores,
                     stream=None):
     R = B * M
     n_pool = pool_blocks.shape[1]
-    st = load_library().csa2_index_pool(
+    _call("csa2_index_pool", 
         _dev(q_codes, "q_codes", U8, (R, 64)), _dev(q_scales, "q_scales", U8, (R, 4)),
         _dev(k_codes, "k_codes", U8, numel=B * N_max * 64), _dev(k_scales, "k_scales", U8, numel=B * N_max * 4),
         _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), n_pool, _dev(n_visible, "n_visible", I32, (R,)),
         B, M, N_max, _dev(pool_scores, "pool_scores", F32, (R, 8 * n_pool)), _stream(stream))
-    _check("csa2_index_pool", st)
 
 
 def csa2_topk(scores, n_visible, k, idx, pool_blocks=None, stream=None):
@@ -176,9 +222,8 @@ def csa2_topk(scores, n_visible, k, idx, pool_blocks=None, stream=None):
         n_pool = scores.shape[1]
         sc = _dev(scores, "scores", F32, (R, n_pool))
         pb = None
-    st = load_library().csa2_topk(sc, pb, n_pool, _dev(n_visible, "n_visible", I32, (R,)), R, k,
+    _call("csa2_topk", sc, pb, n_pool, _dev(n_visible, "n_visible", I32, (R,)), R, k,
                                   _dev(idx, "idx", I32, (R, k)), _stream(stream))
-    _check("csa2_topk", st)
 
 
 def csa2_index_full(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool, k, pool_blocks,
@@ -190,7 +235,7 @@ def csa2_index_full(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max
         workspace = torch.empty(need, dtype=U8, device=q_codes.device)
     if workspace.numel() < need:
         raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
-    st = load_library().csa2_index_full(
+    _call("csa2_index_full", 
         _dev(q_codes, "q_codes", U8, (R, 64)), _dev(q_scales, "q_scales", U8, (R, 4)),
         _dev(k_codes, "k_codes", U8, numel=B * N_max * 64), _dev(k_scales, "k_scales", U8, numel=B * N_max * 4),
         _dev(n_visible, "n_visible", I32, (R,)), B, M, N_max, n_pool, k,
@@ -198,7 +243,6 @@ def csa2_index_full(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max
         _dev(block_max, "block_max", F32, (R, nblk), optional=True),
         _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), _dev(idx, "idx", I32, (R, k), optional=k == 0),
         _dev(workspace, "workspace", U8), workspace.numel(), _stream(stream))
-    _check("csa2_index_full", st)
 
 
 def csa2_sparse_attn(q, c_codes, c_scales, idx, win, win_start, win_len, win_max, B, M, N_max, sm_scale, out,
@@ -215,7 +259,7 @@ def csa2_sparse_attn(q, c_codes, c_scales, idx, win, win_start, win_len, win_max
         workspace = torch.empty(need, dtype=U8, device=q.device)
     if need > 0 and workspace.numel() < need:
         raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
-    st = load_library().csa2_sparse_attn(
+    _call("csa2_sparse_attn", 
         _dev(q, "q", F32, (R, H, 512)),
         _dev(c_codes, "c_codes", U8, numel=B * N_max * 256, optional=k == 0),
         _dev(c_scales, "c_scales", U8, numel=B * N_max * 16, optional=k == 0),
@@ -225,7 +269,6 @@ def csa2_sparse_attn(q, c_codes, c_scales, idx, win, win_start, win_len, win_max
         _dev(out, "out", F32, (R, H, 512)),
         _dev(workspace, "workspace", U8, optional=True) if workspace is not None else None,
         workspace.numel() if workspace is not None else 0, _stream(stream))
-    _check("csa2_sparse_attn", st)
 
 
 def csa2_cache_write_mxfp4(x, w, ratio, codes, scales, stream=None):
@@ -238,16 +281,14 @@ def csa2_cache_write_mxfp4(x, w, ratio, codes, scales, stream=None):
     if ratio < 1 or T % ratio:
         raise ValueError(f"{T} token rows do not split into groups of {ratio}")
     n = T // ratio
-    st = load_library().csa2_cache_write_mxfp4(
+    _call("csa2_cache_write_mxfp4", 
         _dev(x, "x", F32), _dev(w, "w", F32, (T,), optional=ratio == 1), n, int(ratio), D,
         _dev(codes, "codes", U8, numel=n * (D // 2)), _dev(scales, "scales", U8, numel=n * (D // 32)),
         _stream(stream))
-    _check("csa2_cache_write_mxfp4", st)
 
 
 def csa2_cache_write_e4m3(x, out, stream=None):
     """FP8 E4M3 codes of every element of x (e.g. window rows [rows, 512]) into
     out (uint8, same number of elements)."""
     n = x.numel()
-    st = load_library().csa2_cache_write_e4m3(_dev(x, "x", F32), n, _dev(out, "out", U8, numel=n), _stream(stream))
-    _check("csa2_cache_write_e4m3", st)
+    _call("csa2_cache_write_e4m3", _dev(x, "x", F32), n, _dev(out, "out", U8, numel=n), _stream(stream))

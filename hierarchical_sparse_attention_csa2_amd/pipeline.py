@@ -19,7 +19,7 @@ from dataclasses import dataclass
 import torch
 
 from . import (CSA2_OP_INDEX_FULL, CSA2_OP_SPARSE_ATTN, csa2_index_full, csa2_index_pool, csa2_index_scan,
-               csa2_select_blocks, csa2_sparse_attn, csa2_topk, csa2_workspace_bytes)
+               csa2_select_blocks, csa2_sparse_attn, csa2_topk, csa2_workspace_bytes, recording)
 
 
 @dataclass
@@ -120,6 +120,15 @@ class Step:
     def attend(self, cache: Cache, li: LayerInputs, idx: torch.Tensor, out: torch.Tensor):
         csa2_sparse_attn(li.q, cache.c_codes, cache.c_scales, idx, li.win, li.win_start, li.win_len, self.win_max,
                          self.B, self.M, self.N, self.sm_scale, out, self.ws_attn)
+
+    def bind(self, cache: Cache, layers):
+        """The launches run(cache, layers) makes, checked and marshalled once:
+        returns a function that issues them again on the stream current now,
+        with no per-call argument checks.  It holds raw device pointers, so the
+        cache, the layer inputs and this Step must stay alive and in place."""
+        with recording() as rec:
+            self.run(cache, layers)
+        return rec.launches()
 
     def run(self, cache: Cache, layers):
         """layers: one LayerInputs per mode.  Returns (pool, [idx per layer], [out per layer])."""

@@ -54,3 +54,47 @@ def test_graph_replays_match_eager(modes):
         for a, b in zip(got, ref):
             assert torch.equal(a, b), f"replay {rep} differs from the eager step"
         assert any(not torch.equal(a, b) for a, b in zip(other, ref)), "the eager work did not change the outputs"
+
+
+@pytest.mark.parametrize("modes", [("full",), ("full", "reindex", "reuse")])
+def test_bound_step_matches_run(modes):
+    """Step.bind(): the recorded launches give run()'s outputs bit for bit, and
+    follow new inputs copied into the same tensors."""
+    w = Workload("bound", 1357, B=3, N=20000, layers=modes)
+    w_other = Workload("bound_other", 2468, B=3, N=20000, layers=modes)
+    cache_a, lays_a = host_inputs(w, layers=len(modes))
+    cache_b, lays_b = host_inputs(w_other, layers=len(modes), kind="mixed")
+    say(f"bound step modes={modes}")
+    ca, la = pipeline.cache_from(dev(cache_a)), [pipeline.layer_from(dev(l)) for l in lays_a]
+    st = pipeline.Step(modes, w.B, 1, w.N, n_pool=256, k=128, win_max=128)
+    # the buffers a step writes (a Reuse layer keeps the previous indices)
+    written = [st.pool] + [x for x, m in zip(st.idx, modes) if m != "reuse"] + st.out
+
+    def snapshot():
+        return [x.clone() for x in written]
+
+    st.run(ca, la)
+    torch.cuda.synchronize()
+    want_a = snapshot()
+    step = st.bind(ca, la)
+    for t in written:
+        t.fill_(-7)
+    step()
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(snapshot(), want_a))
+    # new inputs in place: the bound launches read them
+    cb, lb = pipeline.cache_from(dev(cache_b)), [pipeline.layer_from(dev(l)) for l in lays_b]
+    st.run(cb, lb)
+    torch.cuda.synchronize()
+    want_b = snapshot()
+    for dst, src in zip((ca.k_codes, ca.k_scales, ca.c_codes, ca.c_scales), (cb.k_codes, cb.k_scales, cb.c_codes,
+                                                                             cb.c_scales)):
+        dst.copy_(src)
+    for x, y in zip(la, lb):
+        for name in ("q", "win", "win_start", "win_len", "n_visible", "q_codes", "q_scales"):
+            if getattr(x, name) is not None:
+                getattr(x, name).copy_(getattr(y, name))
+    step()
+    step()
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(snapshot(), want_b))

@@ -61,3 +61,49 @@ def test_workload_parity(name):
         err = float(np.max(np.abs(got - ref)))
         say(f"  layer {L} ({mode}) idx ok, attention max abs err {err:.3e}")
         assert err <= ATOL
+
+
+def test_cache_write_full_size_sampled():
+    """The cache write of c3's context (w3: 4 x 1,048,576 fp32 tokens at ratio 2,
+    latent and indexer keys, plus the window rows) in bench.py's launch
+    configuration; codes and scale bytes bit-exact on sampled entries (the first
+    and last, entries around the kernels' tile-group boundaries and random ones)
+    and on every window row."""
+    cw = synth.CACHE_WRITES["w3"]
+    T, E = cw.tokens, cw.entries
+    say(f"cache write {cw.name}: {T} tokens -> {E} entries")
+    x_lat = torch.empty((T, 512), dtype=torch.float32, device="cuda")
+    x_idx = torch.empty((T, 128), dtype=torch.float32, device="cuda")
+    wts = torch.empty(T, dtype=torch.float32, device="cuda")
+    chunk = 1 << 18
+    for r0 in range(0, T, chunk):
+        n = min(chunk, T - r0)
+        x_lat[r0:r0 + n].copy_(torch.from_numpy(cw.latent_rows(r0, n)))
+        x_idx[r0:r0 + n].copy_(torch.from_numpy(cw.index_rows(r0, n)))
+        wts[r0:r0 + n].copy_(torch.from_numpy(cw.weights(r0, n)))
+    xw = cw.window_rows()
+    c_codes = torch.empty((E, 256), dtype=torch.uint8, device="cuda")
+    c_scales = torch.empty((E, 16), dtype=torch.uint8, device="cuda")
+    k_codes = torch.empty((E, 64), dtype=torch.uint8, device="cuda")
+    k_scales = torch.empty((E, 4), dtype=torch.uint8, device="cuda")
+    win = torch.empty(xw.shape, dtype=torch.uint8, device="cuda")
+    csa2.csa2_cache_write_mxfp4(x_lat, wts, cw.ratio, c_codes, c_scales)
+    csa2.csa2_cache_write_mxfp4(x_idx, wts, cw.ratio, k_codes, k_scales)
+    csa2.csa2_cache_write_e4m3(torch.from_numpy(xw).cuda(), win)
+    torch.cuda.synchronize()
+    del x_lat, x_idx, wts
+    # a workgroup takes 256 quads: 2 latent entries or 8 key entries; tiles are
+    # permuted in groups of 512
+    rng = np.random.default_rng(3)
+    edges = [0, 1, 2, 3, 7, 8, 1023, 1024, 1025, 4095, 4096, 4097, E // 2, E - 2, E - 1]
+    sample = np.unique(np.concatenate([edges, rng.integers(0, E, 48)]))
+    cc, cs = c_codes.cpu().numpy(), c_scales.cpu().numpy()
+    kc, ks = k_codes.cpu().numpy(), k_scales.cpu().numpy()
+    say(f"  GPU done; oracle on {sample.size} entries")
+    for e in sample.tolist():
+        w2 = cw.weights(2 * e, 2)
+        rc, rs = oracle.cache_write_mxfp4(cw.latent_rows(2 * e, 2), w2, 2)
+        assert np.array_equal(cc[e], rc[0]) and np.array_equal(cs[e], rs[0]), ("latent", e)
+        rc, rs = oracle.cache_write_mxfp4(cw.index_rows(2 * e, 2), w2, 2)
+        assert np.array_equal(kc[e], rc[0]) and np.array_equal(ks[e], rs[0]), ("index key", e)
+    assert np.array_equal(win.cpu().numpy(), oracle.cache_write_e4m3(xw))
