@@ -51,6 +51,15 @@ WRITE_SOURCES = ("hierarchical_sparse_attention_csa2_amd/csrc/cache_write.hip",
 TRAFFIC = {"c3": (COUNTERS, SCAN_SOURCES, SCAN_KERNEL), "w3": (WRITE_COUNTERS, WRITE_SOURCES, WRITE_KERNEL)}
 
 
+# The pages' own figures for the method (DeepSeek-V4.1-Flash write-ups): whole-
+# model HBM-resident global KV per token, entries read per layer, the candidate
+# pool, the window and the context length.  They give no hardware, kernel or
+# throughput figures for any of them, so nothing here is compared against them.
+PAGES_FIGURES = {"global_kv_bytes_per_token": 890, "entries_read_per_layer": 512,
+                 "candidate_pool": "2048 blocks x 8 positions = 16,384", "window_tokens": 128,
+                 "context_tokens": 1048576, "throughput_given_by_pages": False}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -279,6 +288,7 @@ def bench_cache_write(args, torch):
         "index_key_write": {"kernel": WRITE_KERNEL, "avg_launch_us": idx_ms * 1e3,
                             "algorithmic_bytes": idx_bytes, "gbs": idx_bytes / (idx_ms / 1e3) / 1e9},
         "cpu_baseline": cpu,
+        "pages_figures": PAGES_FIGURES,
     }
     print(json.dumps(out))
 
@@ -447,6 +457,7 @@ def main():
         "roofline": scan_roof,
         "attention": attn,
         "cpu_baseline": cpu,
+        "pages_figures": PAGES_FIGURES,
     }
     print(json.dumps(out))
 

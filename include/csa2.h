@@ -63,7 +63,7 @@ extern "C" {
 enum {
     CSA2_OK = 0,
     CSA2_ERR_INVALID = -1,      /* bad pointer, size or range */
-    CSA2_ERR_UNSUPPORTED = -2,  /* valid but not supported by this build */
+    CSA2_ERR_UNSUPPORTED = -2,  /* valid but not supported by this library */
     CSA2_ERR_WORKSPACE = -3,    /* workspace missing or too small */
     CSA2_ERR_HIP = -4           /* a HIP launch failed */
 };
