@@ -89,35 +89,49 @@ def replicate(cache, layers, n, torch):
 
 
 def cpu_baseline(w, cache, lays, seconds):
-    """The oracle as it stands, on this host: whole layer steps for all B queries."""
+    """The oracle as it stands, on this host: whole layer steps over a bounded
+    sample of the workload's query rows (every row of a decode workload; the
+    first rows of each sequence of a prefill chunk), on as many host threads as
+    it can use (it threads over rows), then on one thread."""
     import oracle
 
-    R = w.R
-    threads = max(1, min(os.cpu_count() or 1, R))
+    m_s = min(w.M, max(8, os.cpu_count() or 1))   # query rows per sequence in the sample
+    rows = np.concatenate([b * w.M + np.arange(m_s) for b in range(w.B)])
+    per_row = ("q", "q_codes", "q_scales", "n_visible", "win_start", "win_len")
+    sl = [{k: (v[rows] if k in per_row else v) for k, v in d.items()} for d in lays]
+    R = w.B * m_s
     sm = np.float32(1.0 / math.sqrt(512.0))
-    reps = 0
-    t0 = time.time()
-    while True:
-        prev = None
-        for L, mode in enumerate(w.layers):
-            d = lays[L]
-            if mode == "full":
-                res = oracle.index_full(d["q_codes"], d["q_scales"], cache["k_codes"], cache["k_scales"],
-                                        d["n_visible"], w.B, w.M, w.N, n_pool=w.n_pool, k=w.k, threads=threads)
-                pool, prev = res["pool_blocks"], res["idx"]
-            elif mode == "reindex":
-                ps = oracle.index_pool(d["q_codes"], d["q_scales"], cache["k_codes"], cache["k_scales"], pool,
-                                       d["n_visible"], w.B, w.M, w.N, threads=threads)
-                prev = oracle.topk_pool(ps, pool, d["n_visible"], w.k, threads=threads)
-            oracle.sparse_attn(d["q"], cache["c_codes"], cache["c_scales"], prev, d["win"], d["win_start"],
-                               d["win_len"], w.B, w.M, w.N, sm, threads=threads)
-        reps += 1
-        el = time.time() - t0
-        if el >= seconds:
-            break
-    return {"value": R * len(w.layers) * reps / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full step(s) of the same workload ({w.B} sequences x {w.M} queries, "
-                      f"{len(w.layers)} layer(s)), {el:.1f} s on {threads} host thread(s)"}
+
+    def run(threads, budget):
+        reps = 0
+        t0 = time.time()
+        while True:
+            prev = None
+            for L, mode in enumerate(w.layers):
+                d = sl[L]
+                if mode == "full":
+                    res = oracle.index_full(d["q_codes"], d["q_scales"], cache["k_codes"], cache["k_scales"],
+                                            d["n_visible"], w.B, m_s, w.N, n_pool=w.n_pool, k=w.k, threads=threads)
+                    pool, prev = res["pool_blocks"], res["idx"]
+                elif mode == "reindex":
+                    ps = oracle.index_pool(d["q_codes"], d["q_scales"], cache["k_codes"], cache["k_scales"], pool,
+                                           d["n_visible"], w.B, m_s, w.N, threads=threads)
+                    prev = oracle.topk_pool(ps, pool, d["n_visible"], w.k, threads=threads)
+                oracle.sparse_attn(d["q"], cache["c_codes"], cache["c_scales"], prev, d["win"], d["win_start"],
+                                   d["win_len"], w.B, m_s, w.N, sm, threads=threads)
+            reps += 1
+            el = time.time() - t0
+            if el >= budget:
+                return R * len(w.layers) * reps / el, reps, el
+
+    threads = max(1, min(os.cpu_count() or 1, R))
+    value, reps, el = run(threads, seconds)
+    one, reps1, el1 = run(1, seconds / 2) if threads > 1 else (value, reps, el)
+    sample = (f"{reps} full step(s) over {R} of the workload's {w.R} query rows ({w.B} sequences x {m_s} "
+              f"queries, {len(w.layers)} layer(s)), {el:.1f} s on {threads} host thread(s); on 1 thread "
+              f"{reps1} step(s) in {el1:.1f} s")
+    return {"value": value, "unit": "queries/s", "cores": threads, "kind": "oracle", "sample": sample,
+            "value_1_thread": one, "host_cores": os.cpu_count()}
 
 
 def measured_traffic(workload):
