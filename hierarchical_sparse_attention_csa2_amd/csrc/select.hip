@@ -827,6 +827,12 @@ struct RegTopkShared {
   uint32_t floor;
 };
 
+// Grid 2R: workgroup r < R selects row r's first kb blocks and then its top-k
+// (what the attention waits for); workgroup R + r selects row r's pool beside
+// it, on another CU (the pool is read only by later layers).  The first kb
+// blocks of the ranking do not depend on the pool size, and ranking for kb
+// alone keeps fewer super-blocks and survivors than ranking for the pool.
+//
 // Block rows of at most 1024*J blocks (register filter), kb <= 128*JT.
 template <int J, int JT>
 __global__ __launch_bounds__(kSelThreads) void select_reg_topk_kernel(
@@ -834,9 +840,16 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_topk_kernel(
     int32_t* __restrict__ pool_out, int kb, const float* __restrict__ scores, int64_t n_max, int k,
     int32_t* __restrict__ idx) {
   __shared__ RegTopkShared sh;
+  const int R = (int)(gridDim.x >> 1);
+  if ((int)blockIdx.x >= R) {
+    const int r = (int)blockIdx.x - R;
+    select_reg_row<J, kSelBlocks>(sh.rs, r, bmax, stride, nullptr, 0, n_visible, n_pool,
+                                  pool_out + (int64_t)r * n_pool, 0, nullptr, nullptr, nullptr);
+    return;
+  }
   const int r = blockIdx.x;
-  select_reg_row<J, kSelBlocks>(sh.rs, r, bmax, stride, nullptr, 0, n_visible, n_pool, pool_out + (int64_t)r * n_pool,
-                                kb, sh.blk, nullptr, &sh.floor);
+  select_reg_row<J, kSelBlocks>(sh.rs, r, bmax, stride, nullptr, 0, n_visible, 0, nullptr, kb, sh.blk, nullptr,
+                                &sh.floor);
   __syncthreads();
   int64_t nv = n_visible[r];
   nv = nv < 0 ? 0 : (nv < n_max ? nv : n_max);
@@ -853,9 +866,17 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks3_topk_kernel(
     const int32_t* __restrict__ n_visible, int n_pool, int32_t* __restrict__ pool_out, int kb,
     const float* __restrict__ scores, int64_t n_max, int k, int32_t* __restrict__ idx) {
   __shared__ Blocks3Shared sh;
+  // grid 2R, as select_reg_topk_kernel
+  const int R = (int)(gridDim.x >> 1);
+  if ((int)blockIdx.x >= R) {
+    const int r = (int)blockIdx.x - R;
+    select_blocks3_row<true, kVec>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, n_pool,
+                                   pool_out + (int64_t)r * n_pool, 0, nullptr, nullptr);
+    return;
+  }
   const int r = blockIdx.x;
-  select_blocks3_row<true, kVec>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, n_pool,
-                                 pool_out + (int64_t)r * n_pool, kb, sh.sbsel, &sh.floor);
+  select_blocks3_row<true, kVec>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, 0, nullptr, kb, sh.sbsel,
+                                 &sh.floor);
   __syncthreads();
   int64_t nv = n_visible[r];
   nv = nv < 0 ? 0 : (nv < n_max ? nv : n_max);
@@ -963,7 +984,7 @@ hipError_t launch_select_topk(const float* bmax, int64_t stride, const float* su
                               const float* scores, int64_t n_max, int k, int32_t* idx, hipStream_t stream) {
   if (kb < 1 || kb > kFusedMaxKb || k < 1 || n_pool < kb || n_pool > 2048 || !super_max)
     return hipErrorNotSupported;
-  const dim3 grid((unsigned)R), block(kSelThreads);
+  const dim3 grid(2u * (unsigned)R), block(kSelThreads);   // top-k workgroups, then pool workgroups
   const bool small_kb = kb <= 512;
 #define CSA2_REGT(J)                                                                                          \
   do {                                                                                                        \
