@@ -139,6 +139,46 @@ def test_index_full_bitexact(kind, N, n_pool, k, nv):
     assert np.array_equal(pool2.cpu().numpy(), ref["pool_blocks"])
 
 
+@pytest.mark.parametrize("kind", ["normal", "ties", "mixed"])
+@pytest.mark.parametrize("N,M,k,nv", [
+    (1, 1, 512, [1, 0, 1]),
+    (64, 1, 512, [64, 63, 1]),
+    (4096, 1, 512, [4096, 4095, 2049]),
+    (4097, 1, 512, [4097, 4096, 100]),        # 8 key groups per wave
+    (8192, 1, 1000, [8192, 0, 8191]),         # an empty row, k above half the blocks
+    (16384, 1, 512, [16384, 16383, 9000]),    # 16 key groups per wave; blocks = pool size
+    (9000, 5, 512, None),                     # 5 causal queries per sequence
+])
+def test_index_full_short_context(kind, N, M, k, nv):
+    """Decode over contexts whose blocks all fit in the 2048-block pool (the
+    pool is every visible block): the pool, the top-k and the optional score and
+    block-max outputs of csa2_index_full are bit-exact."""
+    w = Workload("small", 7 + N + M, B=3, N=N, M=M, k=k, prefill_base=(N - M) if M > 1 else -1)
+    cache, (lay,) = host_inputs(w, kind=kind)
+    if nv is not None:
+        lay["n_visible"] = np.array(nv, np.int32)
+    c, l = dev(cache), dev(lay)
+    say(f"index_full short context N={N} M={M} k={k} kind={kind}")
+    ref = oracle_full(w, cache, lay, want_scores=True, want_block_max=True)
+    nblk = (N + 7) // 8
+    pool = torch.empty((w.R, 2048), dtype=torch.int32, device="cuda")
+    idx = torch.empty((w.R, k), dtype=torch.int32, device="cuda")
+    scores = torch.full((w.R, N), float("nan"), device="cuda")
+    bmax = torch.full((w.R, nblk), float("nan"), device="cuda")
+    csa2.csa2_index_full(l["q_codes"], l["q_scales"], c["k_codes"], c["k_scales"], l["n_visible"], w.B, w.M, N,
+                         2048, k, pool, idx, scores=scores, block_max=bmax)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.cpu().numpy(), ref["pool_blocks"])
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    sc, bm = scores.cpu().numpy(), bmax.cpu().numpy()
+    for r in range(w.R):
+        n = int(lay["n_visible"][r])
+        assert np.array_equal(f32_bits(sc[r, :n]), f32_bits(ref["scores"][r, :n])), r
+        assert np.all(np.isnan(sc[r, n:])), r   # invisible entries are not written
+        nb = (n + 7) // 8
+        assert np.array_equal(f32_bits(bm[r, :nb]), f32_bits(ref["block_max"][r, :nb])), r
+
+
 def test_select_blocks_and_topk_full_layout():
     """csa2_select_blocks (pool + first k blocks) and csa2_topk over full score
     rows, against the oracle's sorts."""
