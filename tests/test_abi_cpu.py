@@ -141,3 +141,25 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         csa2.csa2_index_scan(x, x, x, x, torch.zeros(1, dtype=torch.int32), 1, 1, 1,
                              torch.zeros((1, 1), dtype=torch.float32))
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/csa2.h compiles as C99 (no C++ constructs), and a C program that
+    references every entry point links against libcsa2.so (nothing is run)."""
+    import shutil
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = _declared()
+    src = tmp_path / "use_csa2.c"
+    body = "\n".join(f"    (void)&{n};" for n in names)
+    src.write_text('#include "csa2.h"\n#include <stdio.h>\n'
+                   "int main(void) {\n" + body + "\n"
+                   '    printf("%s\\n", csa2_status_string(CSA2_OK));\n    return 0;\n}\n')
+    exe = tmp_path / "use_csa2"
+    libdir = os.path.dirname(csa2.LIB_PATH)
+    res = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                          str(src), "-o", str(exe), "-L", libdir, "-l:libcsa2.so", f"-Wl,-rpath,{libdir}"],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
