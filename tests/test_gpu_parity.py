@@ -179,6 +179,38 @@ def test_index_full_short_context(kind, N, M, k, nv):
         assert np.array_equal(f32_bits(bm[r, :nb]), f32_bits(ref["block_max"][r, :nb])), r
 
 
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+@pytest.mark.parametrize("N,nv", [(600000, [600000, 599993]), (4194304, [4194304, 3000001])])
+def test_index_full_rows_past_the_two_level_filter(kind, N, nv):
+    """Rows of more than 65,536 blocks (the block filter's in-memory path) up to
+    4,194,304 entries: pool and top-k bit-exact through csa2_index_full."""
+    import synth
+
+    B = len(nv)
+    w = Workload("long", 31 + N, B=B, N=N)
+    say(f"index_full long rows N={N} kind={kind}")
+    if kind == "ties":   # a 4-code key alphabet and 2-code queries: scores tie constantly
+        rng = np.random.default_rng(N)
+        kc = rng.choice(np.array([0x00, 0x11, 0x22, 0x21], np.uint8), size=(B * N, 64))
+        ks = np.full((B * N, 4), 127, np.uint8)
+        qc = rng.choice(np.array([0x11, 0x22], np.uint8), size=(B, 64))
+        qs = np.full((B, 4), 127, np.uint8)
+    else:
+        kc, ks = synth.mxfp4(w.seed, synth.T_INDEX_KEYS, 0, B * N, 128)
+        qc, qs = synth.mxfp4(w.seed, synth.t_index_query(0), 0, B, 128)
+    cache = {"k_codes": kc.reshape(B, N, 64), "k_scales": ks.reshape(B, N, 4)}
+    lay = {"q_codes": qc, "q_scales": qs, "n_visible": np.array(nv, np.int32)}
+    c, l = dev(cache), dev(lay)
+    pool = torch.empty((B, 2048), dtype=torch.int32, device="cuda")
+    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda")
+    csa2.csa2_index_full(l["q_codes"], l["q_scales"], c["k_codes"], c["k_scales"], l["n_visible"], B, 1, N, 2048,
+                         512, pool, idx)
+    torch.cuda.synchronize()
+    ref = oracle.index_full(qc, qs, kc, ks, lay["n_visible"], B, 1, N, n_pool=2048, k=512)
+    assert np.array_equal(pool.cpu().numpy(), ref["pool_blocks"])
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+
+
 def test_select_blocks_and_topk_full_layout():
     """csa2_select_blocks (pool + first k blocks) and csa2_topk over full score
     rows, against the oracle's sorts."""
