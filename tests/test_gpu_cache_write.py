@@ -192,3 +192,52 @@ def test_cache_write_e4m3_window_rows(rows):
     csa2.csa2_cache_write_e4m3(torch.from_numpy(x).cuda(), out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), oracle.cache_write_e4m3(x))
+
+
+def test_cache_write_then_full_layer():
+    """End to end: fp32 tokens -> the GPU cache write (ratio 2, latent, indexer
+    keys, window) -> a Full layer (pool, top-512, attention) on the written
+    cache, against the oracle doing the same from the same tokens."""
+    import math
+
+    from hierarchical_sparse_attention_csa2_amd import pipeline
+
+    B, N, ratio, Tw = 2, 3000, 2, 128
+    T = N * ratio
+    seed = 4711
+    xl = synth.f32(seed, synth.T_TOKEN_LATENT, 0, B * T, 512)
+    xi = synth.f32(seed, synth.T_TOKEN_INDEX, 0, B * T, 128)
+    wts = synth.merge_weights_f32(seed, synth.T_MERGE_LOGITS, 0, B * N)
+    xw = synth.f32(seed, synth.T_TOKEN_WINDOW, 0, B * Tw, 512)
+    say("cache write -> full layer")
+    cc = torch.empty((B, N, 256), dtype=torch.uint8, device="cuda")
+    cs = torch.empty((B, N, 16), dtype=torch.uint8, device="cuda")
+    kc = torch.empty((B, N, 64), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((B, N, 4), dtype=torch.uint8, device="cuda")
+    win = torch.empty((B, Tw, 512), dtype=torch.uint8, device="cuda")
+    wt = torch.from_numpy(wts).cuda()
+    csa2.csa2_cache_write_mxfp4(torch.from_numpy(xl).cuda(), wt, ratio, cc.view(B * N, 256), cs.view(B * N, 16))
+    csa2.csa2_cache_write_mxfp4(torch.from_numpy(xi).cuda(), wt, ratio, kc.view(B * N, 64), ks.view(B * N, 4))
+    csa2.csa2_cache_write_e4m3(torch.from_numpy(xw).cuda(), win.view(B * Tw, 512))
+    qc, qs = synth.mxfp4(seed, synth.t_index_query(0), 0, B, 128)
+    q = synth.f32(seed, synth.t_attn_query(0), 0, B * 64, 512).reshape(B, 64, 512)
+    nv = np.array([N, N - 777], np.int32)
+    ws0, wl = np.zeros(B, np.int32), np.full(B, Tw, np.int32)
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    st = pipeline.Step(("full",), B, 1, N)
+    pool, idxs, outs = st.run(pipeline.Cache(kc, ks, cc, cs),
+                              [pipeline.LayerInputs(q=dv(q), win=win, win_start=dv(ws0), win_len=dv(wl),
+                                                    n_visible=dv(nv), q_codes=dv(qc), q_scales=dv(qs))])
+    torch.cuda.synchronize()
+    # the oracle's own cache from the same tokens
+    rc_c, rc_s = oracle.cache_write_mxfp4(xl, wts, ratio)
+    rk_c, rk_s = oracle.cache_write_mxfp4(xi, wts, ratio)
+    r_win = oracle.cache_write_e4m3(xw).reshape(B, Tw, 512)
+    ref = oracle.index_full(qc, qs, rk_c, rk_s, nv, B, 1, N, n_pool=2048, k=512)
+    assert np.array_equal(pool.cpu().numpy(), ref["pool_blocks"])
+    assert np.array_equal(idxs[0].cpu().numpy(), ref["idx"])
+    o_ref = oracle.sparse_attn(q, rc_c.reshape(B, N, 256), rc_s.reshape(B, N, 16), ref["idx"], r_win, ws0, wl, B, 1,
+                               N, np.float32(1 / math.sqrt(512)))
+    err = float(np.max(np.abs(outs[0].cpu().numpy() - o_ref)))
+    say(f"  attention max abs err {err:.2e}")
+    assert err <= 1e-3
