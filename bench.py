@@ -118,7 +118,7 @@ def cpu_baseline(w, cache, lays, seconds):
                                            d["n_visible"], w.B, m_s, w.N, threads=threads)
                     prev = oracle.topk_pool(ps, pool, d["n_visible"], w.k, threads=threads)
                 oracle.sparse_attn(d["q"], cache["c_codes"], cache["c_scales"], prev, d["win"], d["win_start"],
-                                   d["win_len"], w.B, m_s, w.N, sm, threads=threads)
+                                   d["win_len"], w.B, m_s, w.N, sm, threads=threads, win_max=w.win_len)
             reps += 1
             el = time.time() - t0
             if el >= budget:

@@ -26,6 +26,13 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// A score that is not a number (two block values overflowing to opposite
+// infinities) is stored as the positive quiet NaN 0x7FC00000, whatever NaN the
+// adder produced, so that its rank in the total order is fixed.
+__device__ __forceinline__ float canonical_nan(float s) {
+  return s != s ? __uint_as_float(0x7FC00000u) : s;
+}
+
 // Two E2M1 codes (byte SEL of w, low nibble first) -> two exact f16 values.
 template <int SEL>
 __device__ __forceinline__ half2_t fp4x2_to_f16(uint32_t w) {

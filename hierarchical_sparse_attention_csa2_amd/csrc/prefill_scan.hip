@@ -89,7 +89,7 @@ __device__ __noinline__ float pair_score_valu(const uint8_t* qc, const uint8_t* 
     const float v = __builtin_amdgcn_ldexpf(block_dot(c, qh), (int)qs[b] + (int)ks[b] - 254);
     s = b == 0 ? v : s + v;
   }
-  return s;
+  return canonical_nan(s);
 }
 
 template <bool kScores, bool kSuper>

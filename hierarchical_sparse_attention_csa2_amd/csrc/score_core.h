@@ -27,7 +27,7 @@ __device__ __forceinline__ float score_key_valu(const uint8_t* qr, const uint8_t
     const float v = __builtin_amdgcn_ldexpf(block_dot(c, qh), (int)qs[b] + (int)ksr[b] - 254);
     s = b == 0 ? v : s + v;
   }
-  return s;
+  return canonical_nan(s);
 }
 
 // The four block values of 16 keys on the matrix cores.  kb[u], ek[u]: lane
@@ -64,10 +64,12 @@ __device__ __forceinline__ float score_groups_mfma(const u32x4_t qa, int eq, con
   return s + 0.0f;   // an exact zero sum is +0
 }
 
-// block exponent eq + ek - 254 outside [-124, 114]: the matrix-core value may
-// be inexact
+// Block exponent e = eq + ek - 254 outside [-124, 114]: the matrix-core value
+// may be inexact.  Inside it a block value is an integer of at most 13 bits
+// (|sum| <= 4608 quarter-units) times 2^(e - 2): every nonzero value is a normal
+// float (>= 2^-126) below 2^125, so the product is exact and cannot overflow.
 __device__ __forceinline__ bool exponent_out_of_range(int eq, uint32_t ek) {
-  return (uint32_t)(eq + (int)ek - 130) > 244u;
+  return (uint32_t)(eq + (int)ek - 130) > 238u;
 }
 
 }  // namespace csa2

@@ -45,6 +45,10 @@
  *     blocks rank by (score descending, position ascending): ties go to the
  *     lowest position.  Selected positions/blocks are written in ascending order
  *     and the rest of each output row is padded with -1.
+ *   - A block value past the fp32 range is +-inf (ldexp semantics); a score
+ *     adding opposite infinities is not a number and is stored as the positive
+ *     quiet NaN 0x7FC00000, which ranks above +inf.  (Only scale bytes far from
+ *     those of real data, eq + ek > 371, can overflow.)
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -72,6 +76,9 @@ enum { CSA2_OP_INDEX_FULL = 1, CSA2_OP_SPARSE_ATTN = 2 };
 
 /*
  * csa2_index_scan - the Full layer's indexer scan (first step of the indexer).
+ * Defined by: fupanwang.com article, section "三个方向一起压小缓存" - the FP4
+ * indexer query and key score every visible cached position, and each block of
+ * 8 positions is represented by its highest score.
  * For every row r and visible position j computes the score
  *     s = ((v0 + v1) + v2) + v3,   v_b = sum_{i in block b} q_i k_i   (b = 0..3)
  * where each 32-element block sum is exact and the four adds are fp32
@@ -95,6 +102,9 @@ int csa2_index_scan(const uint8_t* q_codes, const uint8_t* q_scales,
 
 /*
  * csa2_select_blocks - the coarse filter: rank the visible blocks of each row by
+ * (defined by: fupanwang.com article, section "三个方向一起压小缓存" and its
+ * figure caption on the hierarchical sparse indexer - at most 2048 blocks of 8
+ * positions, 16,384 candidates, are kept as the pool shared by later layers)
  * (block max descending, block id ascending) and keep the first
  * min(n_pool, nblk) as the candidate pool, nblk = ceil(n_visible[r]/8).
  *   block_max    f32[R][nblk_stride] (as written by csa2_index_scan)
@@ -114,6 +124,9 @@ int csa2_select_blocks(const float* block_max, const float* super_max, int64_t n
 
 /*
  * csa2_index_pool - score only inside a pool (Reindex layers, and the Full
+ * layer's own top-k; defined by: fupanwang.com article, section
+ * "三个方向一起压小缓存" - later layers score only inside the first Full layer's
+ * candidate pool; dreamax.pages.dev notes, CSA2 paragraph - the Reindex mode)
  * layer's own top-k): for row r, pool block i and t = 0..7 the score of position
  * j = 8*pool_blocks[r][i] + t against the row's own index query, written to
  * pool_scores[r][8i+t]; slots with pool_blocks < 0 or j >= n_visible[r] are
@@ -130,6 +143,8 @@ int csa2_index_pool(const uint8_t* q_codes, const uint8_t* q_scales,
 /*
  * csa2_topk - keep the first min(k, #valid) slots of each row by (score desc,
  * position asc) and write their positions ascending, -1 padded, to idx i32[R][k].
+ * Defined by: fupanwang.com article, section "三个方向一起压小缓存" and its figure
+ * caption - every layer selects its 512 entries inside the pool.
  *   pool layout (pool_blocks != NULL): scores f32[R][8*n_pool]; slot s is position
  *     8*pool_blocks[r][s/8] + s%8, valid when the block id is >= 0 and the
  *     position < n_visible[r].  pool_blocks rows must be ascending (as produced by
@@ -142,7 +157,10 @@ int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, c
               int R, int k, int32_t* idx, void* stream);
 
 /*
- * csa2_index_full - the whole Full-layer indexer: csa2_index_scan, then
+ * csa2_index_full - the whole Full-layer indexer (defined by: fupanwang.com
+ * article, section "三个方向一起压小缓存" and its figure caption - the first Full
+ * layer scores the whole visible context, builds the pool from the block maxima
+ * and picks its own top-512): csa2_index_scan, then
  * csa2_select_blocks (the pool and its first kb = min(k, n_pool) blocks), then
  * csa2_index_pool over those kb blocks and csa2_topk.  The row's top-k over the
  * pool equals its top-k over the pool's kb best blocks (every block ranked ahead
@@ -179,6 +197,9 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales,
  *   win, win_start and win_len may then be NULL).
  *   Window rows outside [0, Tw) are skipped like entries outside [0, N_max).
  *   workspace: csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, M, 0, H, k + win_max)
+ * Defined by: fupanwang.com article, section "三个方向一起压小缓存" - a layer reads
+ * its 512 selected entries of the MXFP4 main KV - and section
+ * "后 20 层干脆共用一份 KV" - beside them, a 128-token sliding window kept in FP8.
  * Returns CSA2_OK, CSA2_ERR_INVALID, CSA2_ERR_UNSUPPORTED (H), CSA2_ERR_WORKSPACE,
  * CSA2_ERR_HIP.
  */

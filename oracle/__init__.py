@@ -58,7 +58,7 @@ def lib():
         L.orc_index_pool.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i64, vp, i32]
         L.orc_topk_pool.argtypes = [vp, vp, i32, vp, i64, i32, vp, i32]
         L.orc_topk_full.argtypes = [vp, vp, i64, i64, i32, vp, i32]
-        L.orc_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i64, i32, i32, f32, vp, i32]
+        L.orc_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i64, i32, i32, f32, vp, i32]
         for f in ("orc_index_full", "orc_index_pool", "orc_topk_pool", "orc_topk_full", "orc_sparse_attn"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -226,7 +226,9 @@ def topk_full(scores, n_visible, k, threads=None):
     return idx
 
 
-def sparse_attn(q, c_codes, c_scales, idx, win, win_start, win_len, B, M, N_max, sm_scale, threads=None):
+def sparse_attn(q, c_codes, c_scales, idx, win, win_start, win_len, B, M, N_max, sm_scale, threads=None,
+                win_max=None):
+    """win_max: rows per window at most (None: the window store's length Tw)."""
     q = _c(q, np.float32)
     R, H, D = q.shape
     assert D == 512 and R == B * M
@@ -235,10 +237,11 @@ def sparse_attn(q, c_codes, c_scales, idx, win, win_start, win_len, B, M, N_max,
     k = idx.shape[1]
     win = _c(win, np.uint8)
     Tw = win.shape[1] if win.size else 0
+    win_max = Tw if win_max is None else int(win_max)
     win_start, win_len = _c(win_start, np.int32), _c(win_len, np.int32)
     out = np.empty((R, H, 512), np.float32)
     rc = lib().orc_sparse_attn(_p(q), _p(c_codes), _p(c_scales), _p(idx), k, _p(win), _p(win_start),
-                               _p(win_len), B, M, N_max, H, Tw, float(sm_scale), _p(out),
+                               _p(win_len), win_max, B, M, N_max, H, Tw, float(sm_scale), _p(out),
                                threads or threads_default())
     assert rc == 0
     return out

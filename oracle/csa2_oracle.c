@@ -140,7 +140,15 @@ float orc_score(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const u
     volatile float s = v[0] + v[1];
     s = s + v[2];
     s = s + v[3];
-    return s;
+    float out = s;
+    /* A score that is not a number (two block values overflowing to opposite
+       infinities) is the positive quiet NaN 0x7FC00000, whatever NaN the host's
+       adder produced, so that its place in the total order is fixed. */
+    if (isnan(out)) {
+        uint32_t u = 0x7FC00000u;
+        memcpy(&out, &u, 4);
+    }
+    return out;
 }
 
 /* ------------------------------------------------------------------ */
@@ -388,7 +396,7 @@ int orc_topk_full(const float* scores, const int32_t* n_visible, int64_t R, int6
 /* ------------------------------------------------------------------ */
 typedef struct {
     const float* q; const uint8_t *cc, *cs; const int32_t* idx; int k;
-    const uint8_t* win; const int32_t *win_start, *win_len;
+    const uint8_t* win; const int32_t *win_start, *win_len; int win_max;
     int M, H, Tw; int64_t N_max; float sm_scale; float* out;
 } attn_ctx;
 
@@ -402,22 +410,30 @@ static void decode_latent_row(const uint8_t* codes, const uint8_t* scales, doubl
 static void attn_row(void* vctx, int64_t r) {
     attn_ctx* c = (attn_ctx*)vctx;
     int64_t seq = r / c->M;
-    int nw = c->win_len[r];
-    int ne_max = c->k + (nw > 0 ? nw : 0);
+    /* the row's window: rows win_start .. win_start + n - 1 of its sequence's
+       window store, n = min(win_len, win_max) (a negative length is empty) */
+    int nw = c->win_max > 0 ? c->win_len[r] : 0;
+    if (nw < 0) nw = 0;
+    if (nw > c->win_max) nw = c->win_max;
+    int ne_max = c->k + nw;
     double* vals = (double*)malloc(sizeof(double) * 512 * (size_t)(ne_max > 0 ? ne_max : 1));
     int ne = 0;
-    /* the selected latent rows (value = key) */
+    /* the selected latent rows (value = key); an index outside the cache
+       [0, N_max) names no entry and is left out */
     for (int j = 0; j < c->k; ++j) {
         int64_t p = c->idx[r * c->k + j];
-        if (p < 0) continue;
+        if (p < 0 || p >= c->N_max) continue;
         const uint8_t* codes = c->cc + (seq * c->N_max + p) * 256;
         const uint8_t* scales = c->cs + (seq * c->N_max + p) * 16;
         decode_latent_row(codes, scales, vals + 512 * (size_t)ne);
         ++ne;
     }
-    /* the sliding-window rows (FP8, value = key) */
+    /* the sliding-window rows (FP8, value = key); a row outside the window
+       store [0, Tw) names no entry and is left out */
     for (int t = 0; t < nw; ++t) {
-        const uint8_t* row = c->win + (seq * (int64_t)c->Tw + c->win_start[r] + t) * 512;
+        int64_t wr = (int64_t)c->win_start[r] + t;
+        if (wr < 0 || wr >= c->Tw) continue;
+        const uint8_t* row = c->win + (seq * (int64_t)c->Tw + wr) * 512;
         for (int i = 0; i < 512; ++i) vals[512 * (size_t)ne + i] = orc_e4m3_value(row[i]);
         ++ne;
     }
@@ -449,10 +465,10 @@ static void attn_row(void* vctx, int64_t r) {
 }
 
 int orc_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_scales, const int32_t* idx,
-                    int k, const uint8_t* win, const int32_t* win_start, const int32_t* win_len, int B, int M,
-                    int64_t N_max, int H, int Tw, float sm_scale, float* out, int threads) {
-    if (B < 0 || M < 0 || H <= 0 || k < 0 || Tw < 0) return -1;
-    attn_ctx c = {q, c_codes, c_scales, idx, k, win, win_start, win_len, M, H, Tw, N_max, sm_scale, out};
+                    int k, const uint8_t* win, const int32_t* win_start, const int32_t* win_len, int win_max,
+                    int B, int M, int64_t N_max, int H, int Tw, float sm_scale, float* out, int threads) {
+    if (B < 0 || M < 0 || H <= 0 || k < 0 || Tw < 0 || win_max < 0) return -1;
+    attn_ctx c = {q, c_codes, c_scales, idx, k, win, win_start, win_len, win_max, M, H, Tw, N_max, sm_scale, out};
     parallel_rows(attn_row, &c, (int64_t)B * M, threads);
     return 0;
 }

@@ -7,7 +7,8 @@
  *   index query  codes u8[R][64]  scales u8[R][4]        (R = B*M query rows)
  *   index keys   codes u8[B][N_max][64] scales u8[B][N_max][4]
  *   latent       codes u8[B][N_max][256] scales u8[B][N_max][16]
- *   window       u8[B][Tw][512] (FP8 E4M3), rows win_start[r] .. +win_len[r]
+ *   window       u8[B][Tw][512] (FP8 E4M3), rows win_start[r] .. + min(win_len[r], win_max)
+ *                (rows outside [0, Tw) and indices outside [0, N_max) are left out)
  *   q, out       f32[R][H][512]
  * Query row r belongs to sequence r / M.  All functions return 0 or -1.
  */
@@ -43,8 +44,8 @@ int orc_topk_pool(const float* pool_scores, const int32_t* pool_blocks, int n_po
 int orc_topk_full(const float* scores, const int32_t* n_visible, int64_t R, int64_t N_max, int k,
                   int32_t* idx, int threads);
 int orc_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_scales, const int32_t* idx,
-                    int k, const uint8_t* win, const int32_t* win_start, const int32_t* win_len, int B, int M,
-                    int64_t N_max, int H, int Tw, float sm_scale, float* out, int threads);
+                    int k, const uint8_t* win, const int32_t* win_start, const int32_t* win_len, int win_max,
+                    int B, int M, int64_t N_max, int H, int Tw, float sm_scale, float* out, int threads);
 
 #ifdef __cplusplus
 }

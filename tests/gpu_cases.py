@@ -33,6 +33,14 @@ def host_inputs(w: Workload, layers=1, kind="normal", seed_offset=0):
                       in {1..4, 250..253} (block exponents outside the range
                       where a matrix-core block sum is exact), so the
                       matrix-core and vector paths meet in one row
+          "overflow" - query scale bytes 243 + U[0, 4], so that eq + ek lands
+                      on both sides of 368 (the top of the matrix cores' exact
+                      range) up to 376; half of the query rows hold +6 in every
+                      element of blocks 0 and 1, and 20% of the cached
+                      positions hold +-6 in every element of each block (sign
+                      per block) with scale bytes 126 + U[-2, 3]: block sums of
+                      up to 4608 quarter-units that overflow to +-inf, and NaN
+                      scores where two blocks overflow with opposite signs
     """
     cache = synth.gen_cache(w)
     lays = [synth.gen_layer(w, layer=L) for L in range(layers)]
@@ -55,6 +63,18 @@ def host_inputs(w: Workload, layers=1, kind="normal", seed_offset=0):
         extreme = np.array([1, 2, 3, 4, 250, 251, 252, 253], np.uint8)
         for pos in ext:
             ks[tuple(pos) + (int(rng.integers(0, ks.shape[-1])),)] = extreme[int(rng.integers(0, len(extreme)))]
+    elif kind == "overflow":
+        kc, ks = cache["k_codes"], cache["k_scales"]
+        lead = kc.shape[:-1]
+        hit = rng.random(lead) < 0.2
+        signs = rng.integers(0, 2, size=lead + (4,)).astype(np.uint8)    # per block: +6 or -6
+        big = np.repeat(np.where(signs == 1, 0xFF, 0x77).astype(np.uint8), 16, axis=-1)
+        kc[hit] = big[hit]
+        ks[hit] = (126 + rng.integers(-2, 4, size=(int(hit.sum()), 4))).astype(np.uint8)
+        for d in lays:
+            R = d["q_scales"].shape[0]
+            d["q_scales"] = (243 + rng.integers(0, 5, size=(R, 4))).astype(np.uint8)
+            d["q_codes"][::2, :32] = 0x77
     elif kind != "normal":
         raise ValueError(kind)
     return cache, lays
@@ -99,7 +119,7 @@ def oracle_attn(w: Workload, cache, lay, idx_rows, rows=None):
         rs = [r for _, r in members]
         o = oracle.sparse_attn(lay["q"][rs], cache["c_codes"][seq:seq + 1], cache["c_scales"][seq:seq + 1],
                                np.asarray(idx_rows)[js], lay["win"][seq:seq + 1], lay["win_start"][rs],
-                               lay["win_len"][rs], 1, len(rs), w.N, SM_SCALE)
+                               lay["win_len"][rs], 1, len(rs), w.N, SM_SCALE, win_max=w.win_len)
         out[js] = o
     return out
 

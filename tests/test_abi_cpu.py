@@ -144,8 +144,10 @@ def test_binding_rejects_cpu_tensors():
 
 
 def test_header_is_plain_c_and_links(tmp_path):
-    """include/csa2.h compiles as C99 (no C++ constructs), and a C program that
-    references every entry point links against libcsa2.so (nothing is run)."""
+    """include/csa2.h compiles as C99 (no C++ constructs), a C program that
+    references every entry point links against libcsa2.so, and it runs: the
+    host-side answers (status strings, workspace sizes, argument errors
+    returned before any launch) reach a C caller unchanged."""
     import shutil
 
     cc = shutil.which("gcc") or shutil.which("cc")
@@ -154,12 +156,25 @@ def test_header_is_plain_c_and_links(tmp_path):
     names = _declared()
     src = tmp_path / "use_csa2.c"
     body = "\n".join(f"    (void)&{n};" for n in names)
-    src.write_text('#include "csa2.h"\n#include <stdio.h>\n'
-                   "int main(void) {\n" + body + "\n"
-                   '    printf("%s\\n", csa2_status_string(CSA2_OK));\n    return 0;\n}\n')
+    checks = r"""
+    if (csa2_workspace_bytes(CSA2_OP_INDEX_FULL, 4, 1, 524288, 0, 512) == 0) return 2;
+    if (csa2_workspace_bytes(99, 1, 1, 1, 0, 1) != 0) return 3;
+    if (csa2_index_scan(NULL, NULL, NULL, NULL, NULL, 1, 1, 1, NULL, NULL, NULL, NULL) != CSA2_ERR_INVALID)
+        return 4;
+    if (csa2_sparse_attn(NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, 0, 1, 1, 1, 64, 0, 1.0f, NULL, NULL, 0,
+                         NULL) != CSA2_ERR_INVALID)
+        return 5;
+    if (csa2_cache_write_e4m3(NULL, 0, NULL, NULL) != CSA2_OK) return 6;
+    printf("%s|%s\n", csa2_status_string(CSA2_OK), csa2_status_string(CSA2_ERR_WORKSPACE));
+"""
+    src.write_text('#include "csa2.h"\n#include <stdio.h>\n#include <stddef.h>\n'
+                   "int main(void) {\n" + body + "\n" + checks + "    return 0;\n}\n")
     exe = tmp_path / "use_csa2"
     libdir = os.path.dirname(csa2.LIB_PATH)
     res = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
                           str(src), "-o", str(exe), "-L", libdir, "-l:libcsa2.so", f"-Wl,-rpath,{libdir}"],
                          capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, (run.returncode, run.stderr)
+    assert run.stdout.strip() == "ok|workspace missing or too small"

@@ -45,7 +45,7 @@ def _run_scan(w, c, l, want_super=False):
     return scores.cpu().numpy(), bmax.cpu().numpy()
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed", "overflow"])
 @pytest.mark.parametrize("N,nv", [(3000, [3000, 2995, 1]), (4099, [4099, 2048, 2049]), (40, [0, 40, 17])])
 def test_index_scan_bitexact(kind, N, nv):
     w = Workload("scan", 1234 + N, B=3, N=N)
@@ -66,14 +66,11 @@ def test_index_scan_bitexact(kind, N, nv):
 
 
 def _same_f32(a, b):
-    """Bitwise equality, except that any NaN matches any NaN."""
-    a = np.asarray(a, np.float32)
-    b = np.asarray(b, np.float32)
-    both_nan = np.isnan(a) & np.isnan(b)
-    return bool(np.all(both_nan | (f32_bits(a) == f32_bits(b))))
+    """Bitwise equality (a NaN score is one fixed bit pattern on both sides)."""
+    return bool(np.array_equal(f32_bits(a), f32_bits(b)))
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed", "overflow"])
 @pytest.mark.parametrize("B,M,N", [(1, 40, 3000), (2, 33, 2100), (1, 130, 5000), (3, 5, 2500), (2, 15, 700),
                                    (2, 16, 1900)])
 def test_prefill_scan_bitexact(kind, B, M, N):
@@ -101,7 +98,7 @@ def test_prefill_scan_bitexact(kind, B, M, N):
         assert _same_f32(smax[r, :ns], np.array(want, np.float32)), r
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed", "overflow"])
 @pytest.mark.parametrize("N,n_pool,k,nv", [
     (4096, 2048, 512, [4096, 4000, 3333]),      # pool covers all blocks
     (20000, 2048, 512, [20000, 19999, 8191]),   # pool smaller than the block count
@@ -139,7 +136,7 @@ def test_index_full_bitexact(kind, N, n_pool, k, nv):
     assert np.array_equal(pool2.cpu().numpy(), ref["pool_blocks"])
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "mixed"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "mixed", "overflow"])
 @pytest.mark.parametrize("N,M,k,nv", [
     (1, 1, 512, [1, 0, 1]),
     (64, 1, 512, [64, 63, 1]),
@@ -238,7 +235,7 @@ def test_select_blocks_and_topk_full_layout():
         assert np.array_equal(idx.cpu().numpy(), want), k
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed", "overflow"])
 def test_reindex_pool_scores_and_topk(kind):
     """A Reindex layer: its own index query scored only inside the Full pool."""
     w = Workload("reidx", 777, B=3, N=50000, n_pool=2048, k=512)
@@ -314,6 +311,41 @@ def test_sparse_attn_many_rows_long_rows(B, M, k, H):
     say(f"  max abs err {err:.3e}")
     assert np.isfinite(got).all()
     assert err <= ATOL
+
+
+@pytest.mark.parametrize("H", [32, 64])
+def test_sparse_attn_out_of_range_names(H):
+    """Indices outside [0, N_max), window rows outside [0, Tw), window lengths
+    above win_max or below zero: the kernels leave out what the oracle leaves
+    out (the interface's rule), in every chunk position."""
+    B, M, N = 2, 4, 900
+    w = Workload("attnX", 4000 + H, B=B, M=M, N=N, H=H, k=100, prefill_base=N - M)
+    cache, (lay,) = host_inputs(w)
+    Tw = lay["win"].shape[1]
+    rng = np.random.default_rng(H)
+    idx = np.sort(rng.integers(0, N, size=(w.R, 100)), axis=1).astype(np.int32)
+    idx[0, 10:20] = N                  # just past the cache
+    idx[1, ::3] = N + 12345
+    idx[2, :] = -5
+    idx[3, 50:] = 1 << 30
+    idx[4, :] = N + 1                  # with its window before row 0: nothing to attend to
+    idx[5, 31:33] = -1                 # chunk edges
+    idx[6, 60:] = N
+    lay["win_start"] = np.array([0, -40, Tw - 60, Tw + 3, -200, 5, Tw - 1, 2], np.int32)
+    lay["win_len"] = np.array([128, 100, 128, 50, 128, 500, 7, -3], np.int32)
+    win_max = 96
+    say(f"attn out-of-range names H={H} Tw={Tw} win_max={win_max}")
+    got = _attn_case(w, cache, lay, idx, win_max)
+    seqs = np.arange(w.R) // M
+    ref = np.stack([oracle.sparse_attn(lay["q"][r:r + 1], cache["c_codes"][s:s + 1], cache["c_scales"][s:s + 1],
+                                       idx[r:r + 1], lay["win"][s:s + 1], lay["win_start"][r:r + 1],
+                                       lay["win_len"][r:r + 1], 1, 1, N, SM_SCALE, win_max=win_max)[0]
+                    for r, s in enumerate(seqs)])
+    err = np.max(np.abs(got - ref))
+    say(f"  max abs err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= ATOL
+    assert (got[4] == 0).all() and (ref[4] == 0).all()
 
 
 def test_sparse_attn_no_window_and_empty():

@@ -120,3 +120,73 @@ def test_convexity_and_duplicates():
     lo, hi = rows.min(axis=0), rows.max(axis=0)
     assert (out[0] >= lo - 1e-6).all() and (out[0] <= hi + 1e-6).all()
     assert np.max(np.abs(out[0] - _torch_attn(q[0], rows, scale))) < 1e-6
+
+
+def _ref_row(q, cc, cs, idx_row, win, ws, wl, win_max, N, Tw, scale):
+    """Brute-force attention of one row: the entries it names, written out by
+    hand (indices in [0, N), window rows ws + t in [0, Tw) for
+    t < min(max(wl, 0), win_max)), torch float64 softmax; zeros if empty."""
+    sel = [int(p) for p in idx_row if 0 <= p < N]
+    n = min(max(int(wl), 0), win_max)
+    wrows = [int(ws) + t for t in range(n) if 0 <= int(ws) + t < Tw]
+    parts = []
+    if sel:
+        parts.append(_decode_latent(cc[sel], cs[sel]))
+    if wrows:
+        parts.append(_decode_e4m3(win[wrows]))
+    if not parts:
+        return np.zeros_like(q, dtype=np.float64)
+    return _torch_attn(q, np.concatenate(parts), scale)
+
+
+def test_many_queries_per_sequence():
+    """M > 1 query rows per sequence: row r reads its sequence's (r // M) latent
+    and window store, with its own indices, window start and length."""
+    B, M, N, H, Tw = 2, 3, 60, 4, 20
+    cc, cs, _, win = _case(36, B, N, H, Tw)
+    q = synth.f32(36, 5, 0, B * M * H, 512).reshape(B * M, H, 512)
+    rng = np.random.default_rng(36)
+    idx = rng.integers(0, N, size=(B * M, 9)).astype(np.int32)
+    idx[2, 4:] = -1
+    ws = np.array([0, 3, 7, 0, 11, 19], np.int32)
+    wl = np.array([5, 8, 13, 0, 9, 1], np.int32)
+    scale = np.float32(1 / np.sqrt(512))
+    out = oracle.sparse_attn(q, cc, cs, idx, win, ws, wl, B, M, N, scale, win_max=Tw)
+    for r in range(B * M):
+        seq = r // M
+        ref = _ref_row(q[r], cc[seq], cs[seq], idx[r], win[seq], ws[r], wl[r], Tw, N, Tw, scale)
+        assert np.max(np.abs(out[r] - ref)) < 1e-6, r
+
+
+def test_out_of_range_entries_and_window_rows_are_left_out():
+    """The interface's rules for names that point nowhere: indices outside
+    [0, N_max) and window rows outside [0, Tw) are not part of the set, and a
+    row's window has min(win_len, win_max) rows (none for a negative length)."""
+    B, N, H, Tw = 1, 30, 3, 16
+    cc, cs, _, win = _case(37, B, N, H, Tw)
+    rows = 7
+    q = synth.f32(37, 5, 0, rows * H, 512).reshape(rows, H, 512)
+    cc7, cs7 = np.repeat(cc, rows, 0), np.repeat(cs, rows, 0)
+    win7 = np.repeat(win, rows, 0)
+    idx = np.array([[0, 29, 30, 31, -1],          # 30 and 31 past the cache
+                    [5, 1 << 30, -7, 2, 2],        # huge and negative indices
+                    [-1, -1, -1, -1, -1],
+                    [3, 4, 5, 6, 7],
+                    [30, 30, 30, 30, 30],          # nothing valid
+                    [1, 2, 3, 4, 5],
+                    [29, 0, 15, 40, 16]], np.int32)
+    ws = np.array([12, -3, 14, 0, -10, 0, 15], np.int32)
+    wl = np.array([8, 6, 2, 40, 5, -4, 1], np.int32)   # past Tw, before 0, > win_max, empty
+    win_max = 12
+    scale = np.float32(1 / np.sqrt(512))
+    out = oracle.sparse_attn(q, cc7, cs7, idx, win7, ws, wl, rows, 1, N, scale, win_max=win_max)
+    for r in range(rows):
+        ref = _ref_row(q[r], cc[0], cs[0], idx[r], win[0], ws[r], wl[r], win_max, N, Tw, scale)
+        assert np.max(np.abs(out[r] - ref)) < 1e-6, r
+    # row 4 names no entry at all: zeros
+    assert (out[4] == 0).all()
+    # row 3's window is clamped to 12 rows: the same as asking for exactly 12
+    wl12 = wl.copy()
+    wl12[3] = 12
+    out12 = oracle.sparse_attn(q, cc7, cs7, idx, win7, ws, wl12, rows, 1, N, scale, win_max=win_max)
+    assert np.array_equal(out[3], out12[3])

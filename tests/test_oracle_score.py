@@ -95,3 +95,48 @@ def test_score_subnormal_rounding():
     got = oracle.score(qc, qs, kc, ks)
     assert got == float(np.float32(3 * 2.0 ** -150))
     assert got == 2.0 ** -148
+
+
+def _block_codes(sign_per_block, code=7):
+    """128 nibbles: every element of block b is +-6 (E2M1 code 7) with the given sign."""
+    n = np.zeros(128, np.uint8)
+    for b, neg in enumerate(sign_per_block):
+        n[32 * b:32 * b + 32] = code | (8 if neg else 0)
+    return _pack(n)
+
+
+def test_score_overflow_to_infinity_and_canonical_nan():
+    """Block sums of 4608 quarter-units (32 products of 6 x 6) at block exponents
+    e = eq + ek - 256 past 2^128 / 4608 overflow: ldexp gives +-inf, and a sum of
+    opposite infinities is NaN, stored as the positive quiet NaN 0x7FC00000 (a
+    fixed bit pattern, so it ranks above +inf in the total order on every host)."""
+    q = _block_codes([False] * 4)
+    # key blocks 0 and 1 of opposite signs, blocks 2 and 3 zero
+    k = _block_codes([False, True, False, False])
+    kz = np.frombuffer(k, np.uint8).copy()
+    kz[32:] = 0
+    qs = np.array([250, 250, 127, 127], np.uint8)
+    ks = np.array([124, 124, 127, 127], np.uint8)     # e = 118: 4608 * 2^118 > 2^130 -> inf
+    s = oracle.score(q, qs, kz, ks)
+    assert np.isnan(s)
+    assert np.float32(s).view(np.uint32) == 0x7FC00000
+    assert oracle.order_key(s) == 0xFFC00000 > oracle.order_key(np.inf)
+    # one block overflowing, the other finite: +inf, and -inf with the signs swapped
+    ks2 = np.array([124, 100, 127, 127], np.uint8)
+    assert oracle.score(q, qs, kz, ks2) == np.inf
+    kneg = _block_codes([True, False, False, False])
+    kn = np.frombuffer(kneg, np.uint8).copy()
+    kn[32:] = 0
+    assert oracle.score(q, qs, kn, ks2) == -np.inf
+    # the largest block exponent whose block values stay finite for any codes:
+    # 4608 * 2^e < 2^128 for e <= 115 (e = eq + ek - 256), exact there
+    for e, want_inf in ((115, False), (116, True)):
+        qs3 = np.array([127 + 64, 127, 127, 127], np.uint8)
+        ks3 = np.array([256 + e - (127 + 64), 127, 127, 127], np.uint8)
+        kk = np.frombuffer(_block_codes([False] * 4), np.uint8).copy()
+        kk[16:] = 0
+        s = oracle.score(q, qs3, kk, ks3)
+        if want_inf:
+            assert s == np.inf
+        else:
+            assert Fraction(s) == Fraction(4608) * Fraction(2) ** e

@@ -161,3 +161,96 @@ def test_topk_full_against_brute_force():
         for r in range(R):
             cand = [(oracle.order_key(scores[r, j]), j) for j in range(nv[r])]
             assert np.array_equal(idx[r], _pad(_brute_first_k(cand, k), k))
+
+
+@pytest.mark.parametrize("few", [False, True])
+def test_index_full_many_queries_per_sequence_brute_force(few):
+    """M > 1 query rows per sequence: row r belongs to sequence r // M and sees
+    its own first n_visible[r] entries of that sequence's cache.  Each sequence
+    has its own keys, so a row scored against the wrong cache, or with another
+    row's visible count, fails the brute-force sort."""
+    rng = np.random.default_rng(41 + few)
+    B, M, N = 3, 4, 90
+    qc, qs, kc, ks = _random_case(rng, B, N, M=M, few_values=few)
+    nv = rng.integers(0, N + 1, size=B * M).astype(np.int32)
+    nv[0], nv[5], nv[B * M - 1] = N, 1, 0
+    n_pool, k = 5, 13
+    out = oracle.index_full(qc, qs, kc, ks, nv, B, M, N, n_pool=n_pool, k=k, want_scores=True,
+                            want_block_max=True)
+    for r in range(B * M):
+        seq = r // M
+        s = [oracle.score(qc[r], qs[r], kc[seq, j], ks[seq, j]) for j in range(nv[r])]
+        assert np.array_equal(np.array(s, np.float32), out["scores"][r, : nv[r]]), r
+        bm = _brute_blocks(s, nv[r])
+        assert np.array_equal(np.array(bm, np.float32), out["block_max"][r, : len(bm)]), r
+        pool = _brute_first_k([(oracle.order_key(v), b) for b, v in enumerate(bm)], n_pool)
+        assert np.array_equal(out["pool_blocks"][r], _pad(pool, n_pool)), r
+        cand = [(oracle.order_key(s[j]), j) for b in pool for j in range(8 * b, min(8 * b + 8, nv[r]))]
+        assert np.array_equal(out["idx"][r], _pad(_brute_first_k(cand, k), k)), r
+
+
+def test_index_pool_many_queries_per_sequence_brute_force():
+    """Reindex over M > 1 rows per sequence: row r's own query against its
+    sequence's (r // M) keys, only inside its own pool row, -inf for slots past
+    its own visible count or with no block."""
+    rng = np.random.default_rng(43)
+    B, M, N = 2, 3, 120
+    qc, qs, kc, ks = _random_case(rng, B, N, M=M, few_values=True)
+    nv = np.array([120, 77, 9, 64, 0, 119], np.int32)
+    pool = np.array([[0, 3, 14, -1], [2, 9, 10, -1], [0, 1, -1, -1],
+                     [4, 5, 6, 7], [0, -1, -1, -1], [1, 13, 14, -1]], np.int32)
+    ps = oracle.index_pool(qc, qs, kc, ks, pool, nv, B, M, N)
+    for r in range(B * M):
+        seq = r // M
+        for i, b in enumerate(pool[r]):
+            for t in range(8):
+                j = 8 * b + t
+                v = ps[r, 8 * i + t]
+                if b < 0 or j >= nv[r]:
+                    assert v == -np.inf
+                else:
+                    assert v == oracle.score(qc[r], qs[r], kc[seq, j], ks[seq, j]), (r, i, t)
+    for k in (1, 5, 40):
+        idx = oracle.topk_pool(ps, pool, nv, k)
+        for r in range(B * M):
+            cand = [(oracle.order_key(ps[r, 8 * i + t]), 8 * b + t)
+                    for i, b in enumerate(pool[r]) if b >= 0 for t in range(8) if 8 * b + t < nv[r]]
+            assert np.array_equal(idx[r], _pad(_brute_first_k(cand, k), k)), (r, k)
+
+
+def test_nan_scores_rank_first():
+    """A NaN score (opposite infinite block values) is the positive quiet NaN and
+    ranks ahead of +inf and of every number, in the block max, the pool and the
+    top-k; ties among the NaN positions go to the lowest position."""
+    B, N = 1, 40
+    nib = lambda vals: (np.asarray(vals[0::2], np.uint8) | (np.asarray(vals[1::2], np.uint8) << 4))
+    qn = np.full(128, 7, np.uint8)                     # +6 everywhere
+    qc = nib(qn)[None, :]
+    qs = np.array([[250, 250, 127, 127]], np.uint8)
+    kc = np.zeros((B, N, 64), np.uint8)
+    ks = np.full((B, N, 4), 127, np.uint8)
+    # positions 3 and 17: blocks 0 / 1 at +6 / -6 with overflowing exponents -> NaN
+    # position 30: block 0 overflowing alone -> +inf; the rest small finite values
+    for p in (3, 17):
+        kn = np.zeros(128, np.uint8)
+        kn[0:32] = 7
+        kn[32:64] = 15
+        kc[0, p] = nib(kn)
+        ks[0, p] = [124, 124, 127, 127]
+    kn = np.zeros(128, np.uint8)
+    kn[0:32] = 7
+    kc[0, 30] = nib(kn)
+    ks[0, 30] = [124, 124, 127, 127]
+    for p in (1, 9, 25):
+        kn = np.zeros(128, np.uint8)
+        kn[100] = 2
+        kc[0, p] = nib(kn)
+    nv = np.array([N], np.int32)
+    out = oracle.index_full(qc, qs, kc, ks, nv, B, 1, N, n_pool=3, k=4, want_scores=True, want_block_max=True)
+    s = out["scores"][0]
+    assert np.isnan(s[3]) and np.isnan(s[17]) and s[30] == np.inf
+    assert s.view(np.uint32)[3] == 0x7FC00000
+    assert np.array_equal(out["pool_blocks"][0], [0, 2, 3])     # NaN blocks 0, 2, then +inf block 3
+    # NaN, NaN and +inf, then the best finite score inside the pool: positions
+    # 1 and 25 tie (9 is in block 1, outside the pool), the lower one wins
+    assert np.array_equal(out["idx"][0], [1, 3, 17, 30])
