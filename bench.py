@@ -38,6 +38,7 @@ LATENT_ROW_BYTES = 256 + 16      # MXFP4 latent row: 256 B of E2M1 codes + 16 E8
 WINDOW_ROW_BYTES = 512           # FP8 E4M3 window row
 INDEX_KEY_BYTES = 68          # 64 B of E2M1 codes + 4 E8M0 scale bytes per cached entry
 SCORE_BYTES = 4               # the decode scan stores each visible entry's fp32 score
+MEASURE_LIB = os.path.join(ROOT, "hierarchical_sparse_attention_csa2_amd", "libcsa2_measure.so")
 SCAN_KERNEL = "index_scan_kernel<true, true>"   # decode scan storing scores and super-block maxima
 COUNTERS = os.path.join(ROOT, "profiles", "index_scan_kernel_c3_hbm_counters.txt")
 SCAN_SOURCES = ("hierarchical_sparse_attention_csa2_amd/csrc/scan.hip",
@@ -88,11 +89,21 @@ def replicate(cache, layers, n, torch):
     return reps
 
 
+def host_threads():
+    """Host threads for the CPU baseline: the CPUs this process may run on,
+    at most OMP_NUM_THREADS when that is set (the share a GPU machine gives a job)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
 def cpu_baseline(w, cache, lays, seconds):
     """The oracle as it stands, on this host: whole layer steps over a bounded
     sample of the workload's query rows (every row of a decode workload; the
-    first rows of each sequence of a prefill chunk), on as many host threads as
-    it can use (it threads over rows), then on one thread."""
+    first rows of each sequence of a prefill chunk), on every host thread, then
+    on one thread."""
     import oracle
 
     m_s = min(w.M, max(8, os.cpu_count() or 1))   # query rows per sequence in the sample
@@ -124,7 +135,9 @@ def cpu_baseline(w, cache, lays, seconds):
             if el >= budget:
                 return R * len(w.layers) * reps / el, reps, el
 
-    threads = max(1, min(os.cpu_count() or 1, R))
+    # every host thread this process may use (the oracle splits rows over
+    # position ranges and heads when there are fewer rows than threads)
+    threads = host_threads()
     value, reps, el = run(threads, seconds)
     one, reps1, el1 = run(1, seconds / 2) if threads > 1 else (value, reps, el)
     sample = (f"{reps} full step(s) over {R} of the workload's {w.R} query rows ({w.B} sequences x {m_s} "
@@ -158,6 +171,64 @@ def measured_traffic(workload):
     if fields.get("kernel", "").strip() != kernel:
         return None
     return float(fields["traffic_bytes_per_launch"])
+
+
+def measure_lib():
+    """The measurement kernels (read-only probe, scan variants), built beside libcsa2.so."""
+    import ctypes
+
+    if not os.path.exists(MEASURE_LIB):
+        raise RuntimeError(f"{MEASURE_LIB} is missing: build it with hierarchical_sparse_attention_csa2_amd/build.py")
+    L = ctypes.CDLL(MEASURE_LIB)
+    vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32
+    L.csa2m_read_probe.argtypes = [vp, vp, i32, i64, u32, vp, vp]
+    L.csa2m_read_probe.restype = i32
+    L.csa2m_index_scan_valu.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp]
+    L.csa2m_index_scan_valu.restype = i32
+    return L
+
+
+def probe_and_variants(w, reps, st, steps, torch, variants):
+    """The read-only probe over each replica's index keys (the decode scan's
+    loads, nothing computed), timed like the scan; with `variants`, also the
+    decode scan with vector-ALU block values on the same inputs and outputs."""
+    import ctypes
+
+    L = measure_lib()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def probe(i):
+        c = reps[i % len(reps)][0]
+        rc = L.csa2m_read_probe(ptr(c.k_codes), ptr(c.k_scales), w.B, w.N, 0x5EEDF00D, ptr(sink), stream())
+        if rc != 0:
+            raise RuntimeError(f"csa2m_read_probe failed ({rc})")
+
+    for i in range(len(reps)):
+        probe(i)
+    probe_ms = time_back_to_back(probe, steps, torch)
+    read_bytes = INDEX_KEY_BYTES * w.B * w.N
+    out = {"kernel": "read_probe_kernel", "avg_launch_us": probe_ms * 1e3, "bytes_per_launch": read_bytes,
+           "gbs": read_bytes / (probe_ms / 1e3) / 1e9}
+    if variants and w.M == 1:
+        scores = torch.empty((w.R, w.N), dtype=torch.float32, device="cuda")
+
+        def valu(i):
+            c, ls = reps[i % len(reps)]
+            li = ls[0]
+            rc = L.csa2m_index_scan_valu(ptr(li.q_codes), ptr(li.q_scales), ptr(c.k_codes), ptr(c.k_scales),
+                                         ptr(li.n_visible), w.B, w.N, ptr(scores), ptr(st.block_max),
+                                         ptr(st.super_max), stream())
+            if rc != 0:
+                raise RuntimeError(f"csa2m_index_scan_valu failed ({rc})")
+
+        for i in range(len(reps)):
+            valu(i)
+        valu_ms = time_back_to_back(valu, steps, torch)
+        out["valu_scan_variant"] = {"kernel": "index_scan_valu_kernel", "avg_launch_us": valu_ms * 1e3,
+                                    "gbs": read_bytes / (valu_ms / 1e3) / 1e9}
+    return out
 
 
 def time_back_to_back(fn, n, torch):
@@ -323,6 +394,8 @@ def main():
                     help="replay one captured HIP graph per input set instead of launching each step from Python")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for HBM counter scaling)")
+    ap.add_argument("--scan-variants", action="store_true",
+                    help="also time the decode scan with vector-ALU block values (measurement library)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -365,10 +438,14 @@ def main():
                        staged=args.staged)
     nv_rows = lays_np[0]["n_visible"].astype(np.int64)
     visible = int(np.sum(nv_rows))
-    # decode reads each sequence's keys once for all its query rows and stores
-    # one score per (row, visible entry); prefill counts products
+    # algorithmic bytes of the decode scan: 68 B of index key per cached entry
+    # read (each sequence's keys once for all its query rows); the stores it
+    # makes besides (one score per (row, visible entry), block and super-block
+    # maxima) are reported apart as write overhead.  Prefill counts products.
     keys_read = int(np.sum(nv_rows.reshape(w.B, w.M).max(axis=1)))
-    scan_bytes = INDEX_KEY_BYTES * keys_read + (SCORE_BYTES * visible if w.M < 16 else 0)
+    scan_bytes = INDEX_KEY_BYTES * keys_read
+    write_overhead = int(np.sum((SCORE_BYTES if w.M < 16 else 0) * nv_rows + 4 * ((nv_rows + 7) // 8)
+                                + 4 * ((nv_rows + 63) // 64)))
     scan_flops = 2.0 * 128 * visible
     log(f"workload {w.name}: {w.notes}; {n_rep} replica(s); scan bytes/launch {scan_bytes / 1e6:.1f} MB")
 
@@ -423,9 +500,13 @@ def main():
     value = queries_per_step / (ms_per_step / 1e3)
     if w.M < 16:
         # decode: the scan streams every visible entry's 68 index-key bytes once
-        scan_roof = {"kernel": SCAN_KERNEL, "bound": "hbm", "achieved": scan_bytes / (scan_ms / 1e3) / 1e9,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": measured_traffic(args.workload),
-                     "traffic_unit": "bytes/launch", "algorithmic_bytes_per_launch": scan_bytes}
+        traffic = measured_traffic(args.workload)
+        kname = SCAN_KERNEL if w.M == 1 else "index_scan_multi_kernel<true, true>"
+        scan_roof = {"kernel": kname, "bound": "hbm", "achieved": scan_bytes / (scan_ms / 1e3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": traffic,
+                     "traffic_unit": "bytes/launch", "algorithmic_bytes_per_launch": scan_bytes,
+                     "write_overhead_bytes_per_launch": write_overhead,
+                     "traffic_over_algorithmic": traffic / scan_bytes if traffic else None}
     else:
         # prefill: 2 x 128 FP4 products per (query, visible entry) pair on the matrix cores
         scan_roof = {"kernel": "prefill_scan_kernel", "bound": "mfma",
@@ -433,6 +514,15 @@ def main():
                      "unit": "TFLOP/s", "traffic": None, "algorithmic_flops_per_launch": scan_flops}
     scan_roof["frac"] = scan_roof["achieved"] / scan_roof["peak"]
     scan_roof["avg_launch_us"] = scan_ms * 1e3
+    if w.M < 16:
+        # the same fraction against what this access pattern reaches when
+        # nothing is computed (the read-only probe, timed the same way)
+        probe = probe_and_variants(w, reps, st, args.steps, torch, args.scan_variants)
+        scan_roof["probe"] = probe
+        scan_roof["probe_frac"] = scan_roof["achieved"] / probe["gbs"]
+        log(f"read-only probe {probe['avg_launch_us']:.1f} us -> {probe['gbs']:.0f} GB/s; scan at "
+            f"{scan_roof['probe_frac']:.3f} of it" + (f"; vector-ALU scan variant "
+            f"{probe['valu_scan_variant']['avg_launch_us']:.1f} us" if "valu_scan_variant" in probe else ""))
     attn_rows = w.k + w.win_len
     attn_flops = 4.0 * w.R * w.H * attn_rows * LATENT_DIM
     attn_bytes = w.R * (w.k * LATENT_ROW_BYTES + w.win_len * WINDOW_ROW_BYTES + 2 * w.H * LATENT_DIM * 4)

@@ -12,6 +12,9 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcsa2.so")
+# measurement-only kernels (read-only probe, scan variants): loaded by the benchmark alone
+MEASURE_LIB = os.path.join(HERE, "libcsa2_measure.so")
+MEASURE_SOURCES = ["measure.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["scan.hip", "prefill_scan.hip", "select.hip", "attn.hip", "cache_write.hip", "csa2_abi.hip"]
@@ -53,18 +56,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + MEASURE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in MEASURE_SOURCES], MEASURE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {MEASURE_LIB}")
     return LIB
 
 

@@ -232,19 +232,34 @@ typedef struct {
     float* scores; float* block_max; int32_t* pool_blocks; int32_t* idx;
     int64_t nblk_max;
     int global_topk;
+    float** pre;              /* when set: each row's scores, computed beforehand */
+    int64_t parts;            /* position ranges per row when scoring beforehand */
 } full_ctx;
 
-static void full_row(void* vctx, int64_t r) {
-    full_ctx* c = (full_ctx*)vctx;
+/* O5 for row r over positions [j0, j1): s[j] for each of them. */
+static void score_range(const full_ctx* c, int64_t r, int64_t j0, int64_t j1, float* s) {
     int64_t seq = r / c->M;
-    int64_t nv = c->n_visible[r];
     const uint8_t* qc = c->qc + r * 64;
     const uint8_t* qs = c->qs + r * 4;
     const uint8_t* kc = c->kc + seq * c->N_max * 64;
     const uint8_t* ks = c->ks + seq * c->N_max * 4;
+    for (int64_t j = j0; j < j1; ++j) s[j] = orc_score(qc, qs, kc + j * 64, ks + j * 4);
+}
+
+/* Task t of the scoring beforehand: part t % parts of row t / parts. */
+static void score_part(void* vctx, int64_t t) {
+    full_ctx* c = (full_ctx*)vctx;
+    int64_t r = t / c->parts, part = t % c->parts;
+    int64_t nv = c->n_visible[r];
+    score_range(c, r, nv * part / c->parts, nv * (part + 1) / c->parts, c->pre[r]);
+}
+
+static void full_row(void* vctx, int64_t r) {
+    full_ctx* c = (full_ctx*)vctx;
+    int64_t nv = c->n_visible[r];
     /* O5: every visible position */
-    float* s = (float*)malloc(sizeof(float) * (size_t)(nv > 0 ? nv : 1));
-    for (int64_t j = 0; j < nv; ++j) s[j] = orc_score(qc, qs, kc + j * 64, ks + j * 4);
+    float* s = c->pre ? c->pre[r] : (float*)malloc(sizeof(float) * (size_t)(nv > 0 ? nv : 1));
+    if (!c->pre) score_range(c, r, 0, nv, s);
     if (c->scores)
         for (int64_t j = 0; j < nv; ++j) c->scores[r * c->N_max + j] = s[j];
     /* O6: block b = positions [8b, 8b+8) that are visible; max by total order */
@@ -285,7 +300,7 @@ static void full_row(void* vctx, int64_t r) {
         free(cand);
     }
     free(blocks);
-    free(s);
+    if (!c->pre) free(s);
 }
 
 int orc_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
@@ -296,8 +311,22 @@ int orc_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
     for (int64_t r = 0; r < (int64_t)B * M; ++r)
         if (n_visible[r] < 0 || n_visible[r] > N_max) return -1;
     full_ctx c = {q_codes, q_scales, k_codes, k_scales, n_visible, M, N_max, n_pool, k,
-                  scores, block_max, pool_blocks, idx, (N_max + 7) / 8, global_topk};
-    parallel_rows(full_row, &c, (int64_t)B * M, threads);
+                  scores, block_max, pool_blocks, idx, (N_max + 7) / 8, global_topk, NULL, 1};
+    int64_t R = (int64_t)B * M;
+    if (threads > R && R > 0) {
+        /* fewer rows than threads: score each row's position ranges on all of
+           them first, then run the rest of each row (O6-O8) as usual */
+        c.parts = (4 * (int64_t)threads + R - 1) / R;
+        c.pre = (float**)malloc(sizeof(float*) * (size_t)R);
+        for (int64_t r = 0; r < R; ++r)
+            c.pre[r] = (float*)malloc(sizeof(float) * (size_t)(n_visible[r] > 0 ? n_visible[r] : 1));
+        parallel_rows(score_part, &c, R * c.parts, threads);
+        parallel_rows(full_row, &c, R, threads);
+        for (int64_t r = 0; r < R; ++r) free(c.pre[r]);
+        free(c.pre);
+        return 0;
+    }
+    parallel_rows(full_row, &c, R, threads);
     return 0;
 }
 
@@ -407,16 +436,16 @@ static void decode_latent_row(const uint8_t* codes, const uint8_t* scales, doubl
     }
 }
 
-static void attn_row(void* vctx, int64_t r) {
-    attn_ctx* c = (attn_ctx*)vctx;
+/* The row's attention set: the decoded values of its entries in order, the
+   selected latent rows then the window rows; returns how many (vals holds room
+   for k + win_max rows). */
+static int row_values(const attn_ctx* c, int64_t r, double* vals) {
     int64_t seq = r / c->M;
     /* the row's window: rows win_start .. win_start + n - 1 of its sequence's
        window store, n = min(win_len, win_max) (a negative length is empty) */
     int nw = c->win_max > 0 ? c->win_len[r] : 0;
     if (nw < 0) nw = 0;
     if (nw > c->win_max) nw = c->win_max;
-    int ne_max = c->k + nw;
-    double* vals = (double*)malloc(sizeof(double) * 512 * (size_t)(ne_max > 0 ? ne_max : 1));
     int ne = 0;
     /* the selected latent rows (value = key); an index outside the cache
        [0, N_max) names no entry and is left out */
@@ -437,31 +466,64 @@ static void attn_row(void* vctx, int64_t r) {
         for (int i = 0; i < 512; ++i) vals[512 * (size_t)ne + i] = orc_e4m3_value(row[i]);
         ++ne;
     }
-    double* z = (double*)malloc(sizeof(double) * (size_t)(ne > 0 ? ne : 1));
-    for (int h = 0; h < c->H; ++h) {
-        const float* qh = c->q + (r * c->H + h) * 512;
-        float* oh = c->out + (r * c->H + h) * 512;
-        if (ne == 0) {
-            for (int d = 0; d < 512; ++d) oh[d] = 0.f;
-            continue;
-        }
-        double m = -INFINITY;
-        for (int i = 0; i < ne; ++i) {
-            double dot = 0.0;
-            for (int d = 0; d < 512; ++d) dot += (double)qh[d] * vals[512 * (size_t)i + d];
-            z[i] = dot * (double)c->sm_scale;
-            if (z[i] > m) m = z[i];
-        }
-        double l = 0.0;
-        for (int i = 0; i < ne; ++i) { z[i] = exp(z[i] - m); l += z[i]; }
-        for (int d = 0; d < 512; ++d) {
-            double o = 0.0;
-            for (int i = 0; i < ne; ++i) o += z[i] * vals[512 * (size_t)i + d];
-            oh[d] = (float)(o / l);
-        }
+    return ne;
+}
+
+/* O11 for head h of row r over the row's ne values; z: room for ne doubles. */
+static void attn_head(const attn_ctx* c, int64_t r, int h, const double* vals, int ne, double* z) {
+    const float* qh = c->q + (r * c->H + h) * 512;
+    float* oh = c->out + (r * c->H + h) * 512;
+    if (ne == 0) {
+        for (int d = 0; d < 512; ++d) oh[d] = 0.f;
+        return;
     }
+    double m = -INFINITY;
+    for (int i = 0; i < ne; ++i) {
+        double dot = 0.0;
+        for (int d = 0; d < 512; ++d) dot += (double)qh[d] * vals[512 * (size_t)i + d];
+        z[i] = dot * (double)c->sm_scale;
+        if (z[i] > m) m = z[i];
+    }
+    double l = 0.0;
+    for (int i = 0; i < ne; ++i) { z[i] = exp(z[i] - m); l += z[i]; }
+    for (int d = 0; d < 512; ++d) {
+        double o = 0.0;
+        for (int i = 0; i < ne; ++i) o += z[i] * vals[512 * (size_t)i + d];
+        oh[d] = (float)(o / l);
+    }
+}
+
+static size_t row_capacity(const attn_ctx* c) {
+    int cap = c->k + (c->win_max > 0 ? c->win_max : 0);
+    return (size_t)(cap > 0 ? cap : 1);
+}
+
+static void attn_row(void* vctx, int64_t r) {
+    attn_ctx* c = (attn_ctx*)vctx;
+    double* vals = (double*)malloc(sizeof(double) * 512 * row_capacity(c));
+    double* z = (double*)malloc(sizeof(double) * row_capacity(c));
+    int ne = row_values(c, r, vals);
+    for (int h = 0; h < c->H; ++h) attn_head(c, r, h, vals, ne, z);
     free(z);
     free(vals);
+}
+
+/* Fewer rows than threads: each row's values decoded first (task = row), then
+   one task per (row, head). */
+typedef struct { attn_ctx* c; double** vals; int* ne; } attn_split_ctx;
+
+static void attn_decode_task(void* vctx, int64_t r) {
+    attn_split_ctx* a = (attn_split_ctx*)vctx;
+    a->ne[r] = row_values(a->c, r, a->vals[r]);
+}
+
+static void attn_head_task(void* vctx, int64_t t) {
+    attn_split_ctx* a = (attn_split_ctx*)vctx;
+    int64_t r = t / a->c->H;
+    int h = (int)(t % a->c->H);
+    double* z = (double*)malloc(sizeof(double) * row_capacity(a->c));
+    attn_head(a->c, r, h, a->vals[r], a->ne[r], z);
+    free(z);
 }
 
 int orc_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_scales, const int32_t* idx,
@@ -469,7 +531,18 @@ int orc_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_sca
                     int B, int M, int64_t N_max, int H, int Tw, float sm_scale, float* out, int threads) {
     if (B < 0 || M < 0 || H <= 0 || k < 0 || Tw < 0 || win_max < 0) return -1;
     attn_ctx c = {q, c_codes, c_scales, idx, k, win, win_start, win_len, win_max, M, H, Tw, N_max, sm_scale, out};
-    parallel_rows(attn_row, &c, (int64_t)B * M, threads);
+    int64_t R = (int64_t)B * M;
+    if (threads > R && R > 0) {
+        attn_split_ctx a = {&c, (double**)malloc(sizeof(double*) * (size_t)R), (int*)malloc(sizeof(int) * (size_t)R)};
+        for (int64_t r = 0; r < R; ++r) a.vals[r] = (double*)malloc(sizeof(double) * 512 * row_capacity(&c));
+        parallel_rows(attn_decode_task, &a, R, threads);
+        parallel_rows(attn_head_task, &a, R * H, threads);
+        for (int64_t r = 0; r < R; ++r) free(a.vals[r]);
+        free(a.vals);
+        free(a.ne);
+        return 0;
+    }
+    parallel_rows(attn_row, &c, R, threads);
     return 0;
 }
 

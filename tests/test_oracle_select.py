@@ -254,3 +254,26 @@ def test_nan_scores_rank_first():
     # NaN, NaN and +inf, then the best finite score inside the pool: positions
     # 1 and 25 tie (9 is in block 1, outside the pool), the lower one wins
     assert np.array_equal(out["idx"][0], [1, 3, 17, 30])
+
+
+def test_threading_does_not_change_results():
+    """Fewer rows than threads splits each row's scoring over position ranges
+    (and attention over heads); the results equal a one-thread run bit for bit."""
+    rng = np.random.default_rng(44)
+    B, M, N = 1, 3, 5000
+    qc, qs, kc, ks = _random_case(rng, B, N, M=M)
+    nv = np.array([5000, 4321, 17], np.int32)
+    one = oracle.index_full(qc, qs, kc, ks, nv, B, M, N, n_pool=64, k=100, want_scores=True, want_block_max=True,
+                            threads=1)
+    many = oracle.index_full(qc, qs, kc, ks, nv, B, M, N, n_pool=64, k=100, want_scores=True,
+                             want_block_max=True, threads=16)
+    for key in one:
+        assert np.array_equal(np.asarray(one[key]).view(np.uint32), np.asarray(many[key]).view(np.uint32)), key
+    cc, cs = synth.mxfp4(44, 2, 0, N, 512)
+    q = synth.f32(44, 5, 0, M * 8, 512).reshape(M, 8, 512)
+    win = synth.e4m3(44, 6, 0, 16, 512).reshape(1, 16, 512)
+    ws, wl = np.zeros(M, np.int32), np.array([16, 3, 0], np.int32)
+    args = (q, cc.reshape(1, N, 256), cs.reshape(1, N, 16), one["idx"], win, ws, wl, B, M, N, np.float32(0.04))
+    a1 = oracle.sparse_attn(*args, threads=1)
+    a16 = oracle.sparse_attn(*args, threads=16)
+    assert np.array_equal(a1.view(np.uint32), a16.view(np.uint32))
