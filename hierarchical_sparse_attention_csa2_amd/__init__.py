@@ -30,13 +30,15 @@ CSA2_ERR_INVALID = -1
 CSA2_ERR_UNSUPPORTED = -2
 CSA2_ERR_WORKSPACE = -3
 CSA2_ERR_HIP = -4
+CSA2_ERR_TOO_LARGE = -5
+CSA2_STATIC_SCRATCH_BYTES = 64 << 20
 CSA2_OP_INDEX_FULL = 1
 CSA2_OP_SPARSE_ATTN = 2
 
 EXPORTED = (
     "csa2_index_scan", "csa2_select_blocks", "csa2_index_pool", "csa2_topk", "csa2_index_full",
-    "csa2_sparse_attn", "csa2_cache_write_mxfp4", "csa2_cache_write_e4m3", "csa2_workspace_bytes",
-    "csa2_status_string",
+    "csa2_index_full_static", "csa2_sparse_attn", "csa2_cache_write_mxfp4", "csa2_cache_write_e4m3",
+    "csa2_workspace_bytes", "csa2_status_string",
 )
 
 _lib = None
@@ -63,6 +65,7 @@ def load_library(path: str = LIB_PATH):
     L.csa2_index_pool.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i64, vp, vp]
     L.csa2_topk.argtypes = [vp, vp, i64, vp, i32, i32, vp, vp]
     L.csa2_index_full.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.csa2_index_full_static.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp]
     L.csa2_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i64, i32, i32, f32, vp, vp, sz,
                                    vp]
     L.csa2_cache_write_mxfp4.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
@@ -72,7 +75,7 @@ def load_library(path: str = LIB_PATH):
     L.csa2_status_string.argtypes = [i32]
     L.csa2_status_string.restype = ctypes.c_char_p
     for f in ("csa2_index_scan", "csa2_select_blocks", "csa2_index_pool", "csa2_topk", "csa2_index_full",
-              "csa2_sparse_attn", "csa2_cache_write_mxfp4", "csa2_cache_write_e4m3"):
+              "csa2_index_full_static", "csa2_sparse_attn", "csa2_cache_write_mxfp4", "csa2_cache_write_e4m3"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -243,6 +246,25 @@ def csa2_index_full(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max
         _dev(block_max, "block_max", F32, (R, nblk), optional=True),
         _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), _dev(idx, "idx", I32, (R, k), optional=k == 0),
         _dev(workspace, "workspace", U8), workspace.numel(), _stream(stream))
+
+
+def csa2_index_full_static(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool, k, pool_blocks,
+                           idx=None, scores=None, block_max=None, stream=None):
+    """csa2_index_full on the library's static per-device scratch: allocates
+    nothing (no workspace tensor either).  Raises Csa2Error with
+    CSA2_ERR_TOO_LARGE when the problem needs more than
+    CSA2_STATIC_SCRATCH_BYTES of scratch.  Calls that overlap on one device
+    race on that scratch; calls ordered on one stream do not."""
+    R = B * M
+    nblk = (N_max + 7) // 8
+    _call("csa2_index_full_static",
+        _dev(q_codes, "q_codes", U8, (R, 64)), _dev(q_scales, "q_scales", U8, (R, 4)),
+        _dev(k_codes, "k_codes", U8, numel=B * N_max * 64), _dev(k_scales, "k_scales", U8, numel=B * N_max * 4),
+        _dev(n_visible, "n_visible", I32, (R,)), B, M, N_max, n_pool, k,
+        _dev(scores, "scores", F32, (R, N_max), optional=True),
+        _dev(block_max, "block_max", F32, (R, nblk), optional=True),
+        _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), _dev(idx, "idx", I32, (R, k), optional=k == 0),
+        _stream(stream))
 
 
 def csa2_sparse_attn(q, c_codes, c_scales, idx, win, win_start, win_len, win_max, B, M, N_max, sm_scale, out,

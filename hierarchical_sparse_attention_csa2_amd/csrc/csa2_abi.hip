@@ -4,6 +4,8 @@
 #include "../../include/csa2.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace {
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -62,6 +64,7 @@ const char* csa2_status_string(int status) {
     case CSA2_ERR_UNSUPPORTED: return "unsupported configuration";
     case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA2_ERR_HIP: return "HIP launch failed";
+    case CSA2_ERR_TOO_LARGE: return "needs more than the static scratch (CSA2_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -118,29 +121,38 @@ int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, c
                                         n_visible, R, k, idx, 0, nullptr, nullptr, 0, as_stream(stream)));
 }
 
-int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+}  // extern "C"
+
+namespace {
+
+// Argument checks of csa2_index_full, apart from the workspace.
+int index_full_args(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                     const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max, int n_pool,
-                    int k, float* scores, float* block_max, int32_t* pool_blocks, int32_t* idx, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    int k, const float* scores, const float* block_max, const int32_t* pool_blocks,
+                    const int32_t* idx) {
   if (!q_codes || !q_scales || !k_codes || !k_scales || !n_visible || !pool_blocks) return CSA2_ERR_INVALID;
-  if (any_misaligned(q_codes, q_scales, k_codes, k_scales, n_visible, scores, block_max, pool_blocks, idx,
-                     static_cast<const char*>(workspace)))
+  if (any_misaligned(q_codes, q_scales, k_codes, k_scales, n_visible, scores, block_max, pool_blocks, idx))
     return CSA2_ERR_INVALID;
   if (B < 1 || M < 1 || N_max < 1 || N_max > kMaxN || (int64_t)B * M > kMaxRows || n_pool < 1 ||
       n_pool > kMaxPool || k < 0 || k > kMaxPool)
     return CSA2_ERR_INVALID;
   if (k > 0 && !idx) return CSA2_ERR_INVALID;
+  return CSA2_OK;
+}
+
+// The Full-layer indexer's launches, with the arguments checked and `ws`
+// holding at least full_ws(...).total bytes.
+int index_full_run(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes, const uint8_t* k_scales,
+                   const int32_t* n_visible, int B, int M, int64_t N_max, int n_pool, int k, float* scores,
+                   float* block_max, int32_t* pool_blocks, int32_t* idx, char* ws, hipStream_t s) {
   const int64_t R = (int64_t)B * M;
   const int64_t nblk = (N_max + 7) / 8;
   const FullWs w = full_ws(R, M, N_max, k);
-  if (!workspace || workspace_bytes < w.total) return CSA2_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
   float* bmax = block_max ? block_max : reinterpret_cast<float*>(ws + w.block_max);
   int32_t* topk_blocks = reinterpret_cast<int32_t*>(ws + w.topk_blocks);
   float* topk_scores = reinterpret_cast<float*>(ws + w.topk_scores);
   float* smax = reinterpret_cast<float*>(ws + w.super_max);
   const int64_t nsup = (N_max + 63) / 64;
-  hipStream_t s = as_stream(stream);
   // the pool's top-k lies in the pool's first min(k, n_pool) blocks
   const int kb = k < n_pool ? k : n_pool;
   if (M < kStoreScoresBelowM && k > 0) {
@@ -176,6 +188,70 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
   e = csa2::launch_select(csa2::kSelPool, topk_scores, 8 * (int64_t)kb, topk_blocks, kb, n_visible, (int)R, k, idx,
                           0, nullptr, nullptr, 0, s, kb == k ? key_floor : nullptr, nullptr);
   return hip_status(e);
+}
+
+// The allocation-free entry point's scratch: one copy per device, in the code
+// object's device memory, kept until the process ends.  Host code never uses
+// the array's name as an address: the device address of each GPU's copy comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+__device__ __align__(256) uint8_t scratch[CSA2_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of the scratch array (the stream's device).
+int scratch_for(hipStream_t stream, char** out) {
+  int dev = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return CSA2_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return CSA2_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return CSA2_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return CSA2_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return CSA2_ERR_HIP;
+    if (e != hipSuccess || !p) return CSA2_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                    const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max, int n_pool,
+                    int k, float* scores, float* block_max, int32_t* pool_blocks, int32_t* idx, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const int st = index_full_args(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool, k, scores,
+                                 block_max, pool_blocks, idx);
+  if (st != CSA2_OK) return st;
+  if (misaligned(workspace)) return CSA2_ERR_INVALID;
+  const FullWs w = full_ws((int64_t)B * M, M, N_max, k);
+  if (!workspace || workspace_bytes < w.total) return CSA2_ERR_WORKSPACE;
+  return index_full_run(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool, k, scores, block_max,
+                        pool_blocks, idx, static_cast<char*>(workspace), as_stream(stream));
+}
+
+int csa2_index_full_static(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                           const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
+                           int n_pool, int k, float* scores, float* block_max, int32_t* pool_blocks, int32_t* idx,
+                           void* stream) {
+  const int st = index_full_args(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool, k, scores,
+                                 block_max, pool_blocks, idx);
+  if (st != CSA2_OK) return st;
+  if (full_ws((int64_t)B * M, M, N_max, k).total > (size_t)CSA2_STATIC_SCRATCH_BYTES) return CSA2_ERR_TOO_LARGE;
+  hipStream_t s = as_stream(stream);
+  char* ws = nullptr;
+  const int got = scratch_for(s, &ws);
+  if (got != CSA2_OK) return got;
+  return index_full_run(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool, k, scores, block_max,
+                        pool_blocks, idx, ws, s);
 }
 
 int csa2_sparse_attn(const float* q, const uint8_t* c_codes, const uint8_t* c_scales, const int32_t* idx, int k,

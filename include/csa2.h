@@ -69,8 +69,12 @@ enum {
     CSA2_ERR_INVALID = -1,      /* bad pointer, size or range */
     CSA2_ERR_UNSUPPORTED = -2,  /* valid but not supported by this library */
     CSA2_ERR_WORKSPACE = -3,    /* workspace missing or too small */
-    CSA2_ERR_HIP = -4           /* a HIP launch failed */
+    CSA2_ERR_HIP = -4,          /* a HIP launch failed */
+    CSA2_ERR_TOO_LARGE = -5     /* needs more than CSA2_STATIC_SCRATCH_BYTES (static-scratch calls) */
 };
+
+/* Size of the per-device scratch array behind csa2_index_full_static. */
+#define CSA2_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 
 enum { CSA2_OP_INDEX_FULL = 1, CSA2_OP_SPARSE_ATTN = 2 };
 
@@ -182,6 +186,32 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales,
                     int n_pool, int k, float* scores, float* block_max,
                     int32_t* pool_blocks, int32_t* idx,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * csa2_index_full_static - csa2_index_full for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments and results without the
+ * workspace.  Its scratch is a static device array of CSA2_STATIC_SCRATCH_BYTES
+ * (64 MiB) per device, held from the first such call on a device until the
+ * process ends; the call allocates nothing.
+ *   - Problems whose csa2_workspace_bytes(CSA2_OP_INDEX_FULL, ...) exceeds
+ *     CSA2_STATIC_SCRATCH_BYTES return CSA2_ERR_TOO_LARGE and launch nothing
+ *     (every decode shape up to 64 rows of 131,072 entries, or 4 rows of
+ *     524,288, fits; a 4,096-query prefill chunk does not).
+ *   - All calls on one device share that device's array, and each call's
+ *     kernels overwrite it: calls that overlap on one device (on different
+ *     streams, or from different threads without ordering) race.  Calls
+ *     ordered on one stream are safe.
+ *   - The scratch of the stream's device is used (the current device for the
+ *     NULL stream); its address is looked up once per device.
+ * Returns as csa2_index_full, with CSA2_ERR_TOO_LARGE in place of
+ * CSA2_ERR_WORKSPACE.
+ */
+int csa2_index_full_static(const uint8_t* q_codes, const uint8_t* q_scales,
+                           const uint8_t* k_codes, const uint8_t* k_scales,
+                           const int32_t* n_visible, int B, int M, int64_t N_max,
+                           int n_pool, int k, float* scores, float* block_max,
+                           int32_t* pool_blocks, int32_t* idx, void* stream);
 
 /*
  * csa2_sparse_attn - one softmax attention per row and head over the row's k
