@@ -183,15 +183,15 @@ def measure_lib():
     vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32
     L.csa2m_read_probe.argtypes = [vp, vp, i32, i64, u32, vp, vp]
     L.csa2m_read_probe.restype = i32
-    L.csa2m_index_scan_valu.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp]
-    L.csa2m_index_scan_valu.restype = i32
+    L.csa2m_index_scan_mfma.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp]
+    L.csa2m_index_scan_mfma.restype = i32
     return L
 
 
 def probe_and_variants(w, reps, st, steps, torch, variants):
     """The read-only probe over each replica's index keys (the decode scan's
     loads, nothing computed), timed like the scan; with `variants`, also the
-    decode scan with vector-ALU block values on the same inputs and outputs."""
+    decode scan with FP4 matrix-core block values on the same inputs and outputs."""
     import ctypes
 
     L = measure_lib()
@@ -214,20 +214,20 @@ def probe_and_variants(w, reps, st, steps, torch, variants):
     if variants and w.M == 1:
         scores = torch.empty((w.R, w.N), dtype=torch.float32, device="cuda")
 
-        def valu(i):
+        def mfma(i):
             c, ls = reps[i % len(reps)]
             li = ls[0]
-            rc = L.csa2m_index_scan_valu(ptr(li.q_codes), ptr(li.q_scales), ptr(c.k_codes), ptr(c.k_scales),
+            rc = L.csa2m_index_scan_mfma(ptr(li.q_codes), ptr(li.q_scales), ptr(c.k_codes), ptr(c.k_scales),
                                          ptr(li.n_visible), w.B, w.N, ptr(scores), ptr(st.block_max),
                                          ptr(st.super_max), stream())
             if rc != 0:
-                raise RuntimeError(f"csa2m_index_scan_valu failed ({rc})")
+                raise RuntimeError(f"csa2m_index_scan_mfma failed ({rc})")
 
         for i in range(len(reps)):
-            valu(i)
-        valu_ms = time_back_to_back(valu, steps, torch)
-        out["valu_scan_variant"] = {"kernel": "index_scan_valu_kernel", "avg_launch_us": valu_ms * 1e3,
-                                    "gbs": read_bytes / (valu_ms / 1e3) / 1e9}
+            mfma(i)
+        mfma_ms = time_back_to_back(mfma, steps, torch)
+        out["mfma_scan_variant"] = {"kernel": "index_scan_mfma_kernel", "avg_launch_us": mfma_ms * 1e3,
+                                    "gbs": read_bytes / (mfma_ms / 1e3) / 1e9}
     return out
 
 
@@ -395,7 +395,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for HBM counter scaling)")
     ap.add_argument("--scan-variants", action="store_true",
-                    help="also time the decode scan with vector-ALU block values (measurement library)")
+                    help="also time the decode scan with FP4 matrix-core block values (measurement library)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -521,8 +521,8 @@ def main():
         scan_roof["probe"] = probe
         scan_roof["probe_frac"] = scan_roof["achieved"] / probe["gbs"]
         log(f"read-only probe {probe['avg_launch_us']:.1f} us -> {probe['gbs']:.0f} GB/s; scan at "
-            f"{scan_roof['probe_frac']:.3f} of it" + (f"; vector-ALU scan variant "
-            f"{probe['valu_scan_variant']['avg_launch_us']:.1f} us" if "valu_scan_variant" in probe else ""))
+            f"{scan_roof['probe_frac']:.3f} of it" + (f"; matrix-core scan variant "
+            f"{probe['mfma_scan_variant']['avg_launch_us']:.1f} us" if "mfma_scan_variant" in probe else ""))
     attn_rows = w.k + w.win_len
     attn_flops = 4.0 * w.R * w.H * attn_rows * LATENT_DIM
     attn_bytes = w.R * (w.k * LATENT_ROW_BYTES + w.win_len * WINDOW_ROW_BYTES + 2 * w.H * LATENT_DIM * 4)

@@ -1,12 +1,13 @@
 // Measurement kernels for the indexer scan's roofline (not part of the C ABI;
-// built into libcsa2_measure.so, which only the benchmark loads):
+// built into libcsa2_measure.so, which only the benchmark and its tests load):
 //   - a read-only probe that fetches exactly the bytes the decode scan reads,
 //     in the same grid, wave layout and load instructions, and computes nothing
 //     from them: the bandwidth this access pattern can reach on the part;
-//   - the decode scan with its block values taken on the vector ALUs instead of
-//     the FP4 matrix cores (E2M1 decoded in registers, exact dot2 block sums,
-//     ldexp, the same fixed-order fp32 sum), same loads and same outputs, so
-//     the two ways of forming the block values can be timed against each other.
+//   - the decode scan with its block values taken on the FP4 matrix cores
+//     instead of the vector ALUs (block-diagonal query operand, keys as the B
+//     operand; waves with a block exponent outside [-124, 114] fall back to the
+//     vector ALUs), same loads and same outputs, so the two ways of forming the
+//     block values can be timed against each other.
 #include "device_common.h"
 #include "score_core.h"
 
@@ -56,11 +57,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
   if (x == magic) sink[0] = x;
 }
 
-// The decode scan (one query row per sequence) with vector-ALU block values.
-// Same grid, loads and outputs as the library's decode scan storing scores and
-// super-block maxima; lane 16g + c forms block g of key 16u + c, the four
-// blocks of a key meet through lane shuffles and are added in block order.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void index_scan_valu_kernel(
+// The decode scan (one query row per sequence) with FP4 matrix-core block
+// values.  Same grid, loads and outputs as the library's decode scan storing
+// scores and super-block maxima.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void index_scan_mfma_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     const int32_t* __restrict__ n_visible, int64_t N_max, int64_t nblk_stride, int64_t nsup_stride,
@@ -84,22 +84,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
     kb[u] = load_codes16(kc + p * 64 + 16 * g);
     ek[u] = ks[p * 4 + g];
   }
-  half2_t qh[16];
-  load_query_block(q_codes + r * 64 + 16 * g, qh);
+  // A operand: lane 16g + i (row i, K group g) holds query block g when i % 4 == g
+  const uint8_t* qr = q_codes + r * 64;
   const int eq = q_scales[r * 4 + g];
-  float sc[4];
+  u32x4_t qa = {0u, 0u, 0u, 0u};
+  if ((lane & 3) == g) qa = *reinterpret_cast<const u32x4_t*>(qr + 16 * g);
+  bool bad = false;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const float v = __builtin_amdgcn_ldexpf(block_dot(kb[u], qh), eq + (int)ek[u] - 254);
-    const float v0 = __shfl(v, c, 64), v1 = __shfl(v, 16 + c, 64), v2 = __shfl(v, 32 + c, 64),
-                v3 = __shfl(v, 48 + c, 64);
-    float s = v0 + v1;
-    s = s + v2;
-    s = s + v3;
-    sc[u] = canonical_nan(s);
+  for (int u = 0; u < 4; ++u) bad |= p0 + 16 * u + c < nv && exponent_out_of_range(eq, ek[u]);
+  float s;
+  if (__ballot(bad) == 0ull) {
+    s = score_groups_mfma(qa, eq, kb, ek);
+  } else {
+    int64_t p = p0 + lane;
+    p = p < nv ? p : nv - 1;
+    s = score_key_valu(qr, q_scales + r * 4, kc + p * 64, ks + p * 4);
   }
-  // lane 16g + c keeps the score of key 16g + c
-  const float s = g == 0 ? sc[0] : (g == 1 ? sc[1] : (g == 2 ? sc[2] : sc[3]));
   const int64_t key = p0 + lane;
   const bool vis = key < nv;
   if (vis) __builtin_nontemporal_store(s, &scores[r * N_max + key]);
@@ -125,16 +125,17 @@ int csa2m_read_probe(const uint8_t* k_codes, const uint8_t* k_scales, int B, int
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-// The decode scan with vector-ALU block values: one query row per sequence
-// (M = 1), arguments and outputs as csa2_index_scan with scores and super_max.
-int csa2m_index_scan_valu(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+// The decode scan with FP4 matrix-core block values: one query row per
+// sequence (M = 1), arguments and outputs as csa2_index_scan with scores and
+// super_max.
+int csa2m_index_scan_mfma(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                           const uint8_t* k_scales, const int32_t* n_visible, int B, int64_t N_max, float* scores,
                           float* block_max, float* super_max, void* stream) {
   if (!q_codes || !q_scales || !k_codes || !k_scales || !n_visible || !scores || !block_max || !super_max)
     return -1;
   if (B < 1 || B > 65535 || N_max < 1 || N_max > ((int64_t)1 << 30)) return -1;
   const dim3 grid((unsigned)((N_max + csa2m::kChunk - 1) / csa2m::kChunk), 1u, (unsigned)B);
-  hipLaunchKernelGGL(csa2m::index_scan_valu_kernel, grid, dim3(csa2m::kThreads), 0,
+  hipLaunchKernelGGL(csa2m::index_scan_mfma_kernel, grid, dim3(csa2m::kThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), q_codes, q_scales, k_codes, k_scales, n_visible, N_max,
                      (N_max + 7) / 8, (N_max + 63) / 64, scores, block_max, super_max);
   return hipGetLastError() == hipSuccess ? 0 : -4;

@@ -8,19 +8,25 @@
 // summed exactly; block b contributes v_b = sum_b * 2^(eq_b + ek_b - 254); the
 // score is ((v0+v1)+v2)+v3 in fp32.
 //
-// Full-layer scan (few queries per sequence): the block values come from the FP4
-// matrix cores.  One v_mfma_scale_f32_16x16x128_f8f6f4 scores 16 keys: the keys
-// are the B operand (lane 16g + c holds block g of key c with its E8M0 scale, so
-// one load instruction still reads 1 KiB of contiguous codes), and the A operand
-// is block-diagonal in the query: row i holds query block i % 4 in K group
-// i % 4 and zeros elsewhere.  Output row i of column c is then the single block
-// value v_{i%4} of key c, a sum of 32 exact products at one scale: exact while
-// the block exponent eq_b + ek_b - 254 lies in [-124, 114] (the integer sum
-// needs 13 bits and every value stays a normal float).  Each lane receives
-// v_0..v_3 of one key and adds them in order itself, so after four products
-// lane l holds the score of the wave's key l.  A wave whose keys have a block
-// exponent outside that range is scored on the vector ALUs instead (E2M1 codes
-// decoded with v_cvt_scalef32_pk_f16_fp4, v_dot2 into fp32, ldexp), giving the
+// One query per sequence (decode) and the pool scan: a streaming pass over the
+// index keys.  Lane 16g + c of a wave loads block g of key c of each 16-key group
+// with one 16-byte load (so one load instruction reads 1 KiB of contiguous
+// codes) and its E8M0 byte, decodes the E2M1 codes in registers, forms the
+// block's exact value (v_dot2 into fp32, ldexp with the two scale exponents) and
+// meets the key's other three blocks through lane shuffles; the four are added
+// in block order, so lane l ends with the score of the wave's key l.  Exact for
+// any scale bytes.
+//
+// Several queries per sequence (a verify step over draft tokens): the keys are
+// loaded once and every row's block values come from the FP4 matrix cores.  One
+// v_mfma_scale_f32_16x16x128_f8f6f4 scores 16 keys: the keys are the B operand
+// (the same lane layout, with the E8M0 byte as the lane's scale), and the A
+// operand is block-diagonal in the query: row i holds query block i % 4 in K
+// group i % 4 and zeros elsewhere.  Output row i of column c is then the single
+// block value v_{i%4} of key c, a sum of 32 exact products at one scale: exact
+// while the block exponent eq_b + ek_b - 254 lies in [-124, 114] (the integer
+// sum needs 13 bits and every value stays a normal float).  Rows whose keys have
+// a block exponent outside that range are scored on the vector ALUs, giving the
 // same fixed-order result.
 #include "device_common.h"
 #include "kernels.h"
@@ -52,8 +58,9 @@ __device__ __forceinline__ uint32_t group8_max_u32(uint32_t x) {
 // Grid (ceil(N_max / 256), M, B): query row r = seq * M + blockIdx.y.  Each wave
 // scores 64 consecutive positions; all of its loads are issued before any
 // arithmetic.  Chunks go to the XCDs in runs of 64 (c3: scan 24.1 -> 23.6 us
-// against launch order; runs of 256 made the step slower).  Outputs: block maxima, optional super-block maxima (8 blocks) and
-// optional per-position scores.
+// against launch order; runs of 256 made the step slower).  Outputs: block
+// maxima, optional super-block maxima (8 blocks) and optional per-position
+// scores.
 template <bool kScores, bool kSuper>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void index_scan_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
@@ -64,8 +71,8 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8,
   const int r = (int)seq * M + (int)blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int c = lane & 15;   // key within a 16-position group (B column)
-  const int g = lane >> 4;   // block held by this lane (B K group)
+  const int c = lane & 15;   // key within a 16-position group
+  const int g = lane >> 4;   // block held by this lane
   int64_t nv = n_visible[r];
   nv = nv < 0 ? 0 : (nv > N_max ? N_max : nv);
   const int64_t p0 = xcd_run_tile<kScanXcdRun>(blockIdx.x, gridDim.x) * kScanChunk + (int64_t)wave * 64;
@@ -82,24 +89,11 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8,
     kb[u] = load_codes16(kc + p * 64 + 16 * g);
     ek[u] = ks[p * 4 + g];
   }
-  // A operand: lane 16g + i (row i, K group g) holds query block g when i % 4 == g
-  const uint8_t* qr = q_codes + (int64_t)r * 64;
+  // this lane's query block g, decoded once
+  half2_t qh[16];
+  load_query_block(q_codes + (int64_t)r * 64 + 16 * g, qh);
   const int eq = q_scales[(int64_t)r * 4 + g];
-  u32x4_t qa = {0u, 0u, 0u, 0u};
-  if ((lane & 3) == g) qa = *reinterpret_cast<const u32x4_t*>(qr + 16 * g);
-
-  // every visible block exponent in [-124, 114]
-  bool bad = false;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) bad |= p0 + 16 * u + c < nv && exponent_out_of_range(eq, ek[u]);
-  float s;
-  if (__ballot(bad) == 0ull) {
-    s = score_groups_mfma(qa, eq, kb, ek);
-  } else {
-    int64_t p = p0 + lane;
-    p = p < nv ? p : nv - 1;
-    s = score_key_valu(qr, q_scales + (int64_t)r * 4, kc + p * 64, ks + p * 4);
-  }
+  const float s = score_groups_valu(qh, eq, kb, ek);
   const int64_t key = p0 + lane;
   const bool vis = key < nv;
   if (kScores && vis) __builtin_nontemporal_store(s, &scores[(int64_t)r * N_max + key]);
@@ -205,11 +199,11 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(7,
   }
 }
 
-// Pool scan: one wave scores 8 pool blocks (64 positions) on the matrix cores,
-// with the operand layout of the Full-layer scan (group u = pool blocks 2u and
-// 2u + 1; lane 16g + c holds block g of position c & 7 of pool block
-// 2u + (c >> 3)); lane l's result is slot l of the wave's 64 output slots.
-// Grid (ceil(n_pool / 8), M, B), one wave per workgroup.
+// Pool scan: one wave scores 8 pool blocks (64 positions) with the decode scan's
+// lane layout (group u = pool blocks 2u and 2u + 1; lane 16g + c holds block g
+// of position c & 7 of pool block 2u + (c >> 3)); lane l's result is slot l of
+// the wave's 64 output slots.  Grid (ceil(n_pool / 8), M, B), one wave per
+// workgroup.
 constexpr int kPoolWaveBlocks = 8;
 
 __global__ __launch_bounds__(64) void pool_scan_kernel(
@@ -249,25 +243,12 @@ __global__ __launch_bounds__(64) void pool_scan_kernel(
     kb[u] = load_codes16(kc + p * 64 + 16 * g);
     ek[u] = ks[p * 4 + g];
   }
-  const uint8_t* qr = q_codes + (int64_t)r * 64;
+  half2_t qh[16];
+  load_query_block(q_codes + (int64_t)r * 64 + 16 * g, qh);
   const int eq = q_scales[(int64_t)r * 4 + g];
-  u32x4_t qa = {0u, 0u, 0u, 0u};
-  if ((lane & 3) == g) qa = *reinterpret_cast<const u32x4_t*>(qr + 16 * g);
-
-  bool bad = false;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) bad |= ok[u] && exponent_out_of_range(eq, ek[u]);
+  const float s = score_groups_valu(qh, eq, kb, ek);
   // this lane's output slot: group g, column c
   const bool mine_ok = (g & 2) ? ((g & 1) ? ok[3] : ok[2]) : ((g & 1) ? ok[1] : ok[0]);
-  float s;
-  if (__ballot(bad) == 0ull) {
-    s = score_groups_mfma(qa, eq, kb, ek);
-  } else {
-    const int32_t b = (g & 2) ? ((g & 1) ? blk[3] : blk[2]) : ((g & 1) ? blk[1] : blk[0]);
-    int64_t p = 8 * (int64_t)b + (c & 7);
-    p = mine_ok ? p : 0;
-    s = score_key_valu(qr, q_scales + (int64_t)r * 4, kc + p * 64, ks + p * 4);
-  }
   if (base + 2 * g + (c >> 3) < n_pool)
     pool_scores[((int64_t)r * n_pool + base) * 8 + lane] = mine_ok ? s : -__builtin_inff();
 }

@@ -1,6 +1,7 @@
 // MXFP4 indexer scores of single keys and of 16-key groups (the score as
 // defined in the indexer scans: exact block sums, ((v0+v1)+v2)+v3 in fp32),
-// shared by the Full-layer scan and the pool scan.
+// shared by the indexer scans: on the vector ALUs (any scales) or on the FP4
+// matrix cores (block exponents in the range where their sums are exact).
 #pragma once
 #include "device_common.h"
 
@@ -62,6 +63,30 @@ __device__ __forceinline__ float score_groups_mfma(const u32x4_t qa, int eq, con
   s = s + v[2];
   s = s + v[3];
   return s + 0.0f;   // an exact zero sum is +0
+}
+
+// The scores of 4 groups of 16 keys on the vector ALUs, for any scale bytes:
+// lane 16g + c holds block g of key c of group u (kb[u] codes, ek[u] scale byte,
+// as loaded for score_groups_mfma), qh its query block g as 16 f16 pairs and eq
+// that block's scale byte.  Each lane forms its block's exact value (E2M1
+// decoded in registers, v_dot2 into fp32, ldexp), the four blocks of a key meet
+// through lane shuffles and are added in block order.  Returns the score of the
+// wave's key 16g + c in lane 16g + c.
+__device__ __forceinline__ float score_groups_valu(const half2_t* qh, int eq, const u32x4_t* kb, const uint32_t* ek) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  float sc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float v = __builtin_amdgcn_ldexpf(block_dot(kb[u], qh), eq + (int)ek[u] - 254);
+    const float v0 = __shfl(v, c, 64), v1 = __shfl(v, 16 + c, 64), v2 = __shfl(v, 32 + c, 64),
+                v3 = __shfl(v, 48 + c, 64);
+    float s = v0 + v1;
+    s = s + v2;
+    s = s + v3;
+    sc[u] = canonical_nan(s);
+  }
+  return g == 0 ? sc[0] : (g == 1 ? sc[1] : (g == 2 ? sc[2] : sc[3]));
 }
 
 // Block exponent e = eq + ek - 254 outside [-124, 114]: the matrix-core value

@@ -1,5 +1,5 @@
 """The benchmark's measurement kernels (libcsa2_measure.so): the decode scan
-with vector-ALU block values must give the library scan's outputs bit for bit
+with FP4 matrix-core block values must give the library scan's outputs bit for bit
 (same scores, block maxima and super-block maxima as the oracle), so that its
 timing compares like with like; the read-only probe runs and stores nothing."""
 import ctypes
@@ -29,7 +29,7 @@ def _lib():
     L = ctypes.CDLL(LIB)
     vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32
     L.csa2m_read_probe.argtypes = [vp, vp, i32, i64, u32, vp, vp]
-    L.csa2m_index_scan_valu.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp]
+    L.csa2m_index_scan_mfma.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp]
     return L
 
 
@@ -38,17 +38,17 @@ S = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 @pytest.mark.parametrize("kind", ["normal", "spread", "mixed", "overflow"])
-def test_valu_scan_variant_bitexact(kind):
+def test_mfma_scan_variant_bitexact(kind):
     N = 5000
-    w = Workload("mvalu", 5150, B=3, N=N)
+    w = Workload("mmfma", 5150, B=3, N=N)
     cache, (lay,) = host_inputs(w, kind=kind)
     lay["n_visible"] = np.array([N, 4093, 1], np.int32)
     c, l = dev(cache), dev(lay)
-    say(f"vector-ALU scan variant kind={kind}")
+    say(f"matrix-core scan variant kind={kind}")
     sc = torch.full((w.R, N), float("nan"), device="cuda")
     bm = torch.full((w.R, (N + 7) // 8), float("nan"), device="cuda")
     sm = torch.full((w.R, (N + 63) // 64), float("nan"), device="cuda")
-    assert _lib().csa2m_index_scan_valu(P(l["q_codes"]), P(l["q_scales"]), P(c["k_codes"]), P(c["k_scales"]),
+    assert _lib().csa2m_index_scan_mfma(P(l["q_codes"]), P(l["q_scales"]), P(c["k_codes"]), P(c["k_scales"]),
                                         P(l["n_visible"]), w.B, N, P(sc), P(bm), P(sm), S()) == 0
     torch.cuda.synchronize()
     ref = oracle_full(w, cache, lay, want_scores=True, want_block_max=True)
