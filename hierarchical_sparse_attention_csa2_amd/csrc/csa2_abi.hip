@@ -162,6 +162,9 @@ int index_full_run(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
     hipError_t e = csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, sc, bmax,
                                            nblk, smax, nsup, s);
     if (e != hipSuccess) return CSA2_ERR_HIP;
+    // every block in the pool: the top-k straight from the score rows
+    e = csa2::launch_select_short(sc, N_max, n_visible, (int)R, n_pool, pool_blocks, k, idx, s);
+    if (e != hipErrorNotSupported) return hip_status(e);
     e = csa2::launch_select_topk(bmax, nblk, smax, nsup, n_visible, (int)R, n_pool, pool_blocks, kb, sc, N_max, k,
                                  idx, s);
     if (e != hipErrorNotSupported) return hip_status(e);

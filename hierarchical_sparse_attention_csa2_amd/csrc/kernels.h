@@ -46,6 +46,13 @@ hipError_t launch_select_topk(const float* bmax, int64_t stride, const float* su
                               const int32_t* n_visible, int R, int n_pool, int32_t* pool_out, int kb,
                               const float* scores, int64_t n_max, int k, int32_t* idx, hipStream_t stream);
 
+// Full layer, decode, every block of every row in the pool (ceil(n_max/8) <=
+// n_pool) and rows of at most 16,384 positions: the pool is every visible block
+// and the top-k is taken from the stored score rows (row stride n_max).
+// hipErrorNotSupported (nothing launched) outside those shapes.
+hipError_t launch_select_short(const float* scores, int64_t n_max, const int32_t* n_visible, int R, int n_pool,
+                               int32_t* pool_out, int k, int32_t* idx, hipStream_t stream);
+
 // Cache write: ratio-m weighted merge of fp32 token rows (D a power of two,
 // >= 32) quantized to MXFP4 codes and E8M0 scales; and fp32 -> FP8 E4M3 of n
 // elements (n % 4 == 0).

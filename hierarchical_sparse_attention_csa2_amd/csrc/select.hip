@@ -885,6 +885,34 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks3_topk_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Full layer, decode, rows whose every block fits in the pool: the pool is every
+// visible block, and (the pool keeping at least k blocks) the top-k over the
+// pool is the top-k over every visible position, taken straight from the
+// scan's stored score row.  Grid 2R: workgroup r < R ranks row r's scores,
+// workgroup R + r writes its pool.  Rows of at most 1024*J positions.
+// ---------------------------------------------------------------------------
+template <int J>
+__global__ __launch_bounds__(kSelThreads) void select_short_kernel(const float* __restrict__ scores, int64_t n_max,
+                                                                   const int32_t* __restrict__ n_visible, int n_pool,
+                                                                   int32_t* __restrict__ pool_out, int k,
+                                                                   int32_t* __restrict__ idx) {
+  __shared__ RegShared sh;
+  const int R = (int)(gridDim.x >> 1);
+  if ((int)blockIdx.x >= R) {
+    const int r = (int)blockIdx.x - R;
+    int64_t nv = n_visible[r];
+    nv = nv < 0 ? 0 : (nv < n_max ? nv : n_max);
+    const int nblk = (int)((nv + 7) >> 3);
+    int32_t* po = pool_out + (int64_t)r * n_pool;
+    for (int p = threadIdx.x; p < n_pool; p += kSelThreads) po[p] = p < nblk ? p : -1;
+    return;
+  }
+  const int r = blockIdx.x;
+  select_reg_row<J, kSelFull>(sh, r, scores, n_max, nullptr, 0, n_visible, k, idx + (int64_t)r * k, 0, nullptr,
+                              nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------------------
 // generic selection: the row stays in memory
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSelThreads) void select_mem_kernel(int layout, const float* __restrict__ scores,
@@ -1020,6 +1048,22 @@ hipError_t launch_select_topk(const float* bmax, int64_t stride, const float* su
     return hipErrorNotSupported;
   }
 #undef CSA2_REGT
+  return hipGetLastError();
+}
+
+hipError_t launch_select_short(const float* scores, int64_t n_max, const int32_t* n_visible, int R, int n_pool,
+                               int32_t* pool_out, int k, int32_t* idx, hipStream_t stream) {
+  if (k < 1 || n_max > 16384 || (n_max + 7) / 8 > n_pool) return hipErrorNotSupported;
+  const dim3 grid(2u * (unsigned)R), block(kSelThreads);
+  if (n_max <= 4096)
+    hipLaunchKernelGGL((select_short_kernel<4>), grid, block, 0, stream, scores, n_max, n_visible, n_pool, pool_out, k,
+                       idx);
+  else if (n_max <= 8192)
+    hipLaunchKernelGGL((select_short_kernel<8>), grid, block, 0, stream, scores, n_max, n_visible, n_pool, pool_out, k,
+                       idx);
+  else
+    hipLaunchKernelGGL((select_short_kernel<16>), grid, block, 0, stream, scores, n_max, n_visible, n_pool, pool_out,
+                       k, idx);
   return hipGetLastError();
 }
 
