@@ -235,7 +235,7 @@ def csa2_index_full(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max
     nblk = (N_max + 7) // 8
     need = csa2_workspace_bytes(CSA2_OP_INDEX_FULL, B, M, N_max, 0, k)
     if workspace is None:
-        workspace = torch.zeros(need, dtype=U8, device=q_codes.device)   # row counters start at zero
+        workspace = torch.empty(need, dtype=U8, device=q_codes.device)
     if workspace.numel() < need:
         raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
     _call("csa2_index_full", 

@@ -21,17 +21,14 @@ constexpr int kStoreScoresBelowM = 16;
 
 // index_full workspace carve-up
 struct FullWs {
-  size_t counters, block_max, super_max, topk_blocks, topk_scores, key_floor, scores, total;
+  size_t block_max, super_max, topk_blocks, topk_scores, key_floor, scores, total;
 };
 
-// The row counters of the one-launch short-row indexer sit at offset 0 with a
-// fixed size, so they stay zero between calls of any shape on one workspace.
 inline FullWs full_ws(int64_t R, int M, int64_t N_max, int k) {
   FullWs w;
   const int64_t nblk = (N_max + 7) / 8;
   const int64_t nsup = (N_max + 63) / 64;
-  w.counters = 0;
-  w.block_max = align_up((size_t)csa2::kShortCounterRows * sizeof(uint32_t));
+  w.block_max = 0;
   w.super_max = align_up(w.block_max + (size_t)R * nblk * sizeof(float));
   w.topk_blocks = align_up(w.super_max + (size_t)R * nsup * sizeof(float));
   w.topk_scores = align_up(w.topk_blocks + (size_t)R * (k > 0 ? k : 0) * sizeof(int32_t));
@@ -159,16 +156,10 @@ int index_full_run(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
   // the pool's top-k lies in the pool's first min(k, n_pool) blocks
   const int kb = k < n_pool ? k : n_pool;
   if (M < kStoreScoresBelowM && k > 0) {
-    float* sc = scores ? scores : reinterpret_cast<float*>(ws + w.scores);
-    // short rows, one query each, every block in the pool: scan, pool and top-k
-    // in one launch
-    hipError_t e = csa2::launch_index_full_short(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool,
-                                                 k, pool_blocks, idx, sc, block_max,
-                                                 reinterpret_cast<uint32_t*>(ws + w.counters), s);
-    if (e != hipErrorNotSupported) return hip_status(e);
     // decode: the scan stores every score; one workgroup per row then builds the
     // pool and takes the top-k from the stored scores of its first kb blocks
-    e = csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, sc, bmax,
+    float* sc = scores ? scores : reinterpret_cast<float*>(ws + w.scores);
+    hipError_t e = csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, sc, bmax,
                                            nblk, smax, nsup, s);
     if (e != hipSuccess) return CSA2_ERR_HIP;
     // every block in the pool: the top-k straight from the score rows

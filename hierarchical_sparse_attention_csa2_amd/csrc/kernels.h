@@ -53,18 +53,6 @@ hipError_t launch_select_topk(const float* bmax, int64_t stride, const float* su
 hipError_t launch_select_short(const float* scores, int64_t n_max, const int32_t* n_visible, int R, int n_pool,
                                int32_t* pool_out, int k, int32_t* idx, hipStream_t stream);
 
-// The Full-layer indexer in one launch for decode rows (M = 1, k >= 1) of at
-// most 16,384 positions whose every block fits in the pool (ceil(N_max/8) <=
-// n_pool), B <= kShortCounterRows: the last workgroup of a row to finish its
-// scan takes the row's top-k.  scores: R x N_max (required); block_max
-// optional.  counters: kShortCounterRows words, zero on entry, left zero.
-// hipErrorNotSupported (nothing launched) outside those shapes.
-constexpr int kShortCounterRows = 16384;
-hipError_t launch_index_full_short(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
-                                   const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
-                                   int n_pool, int k, int32_t* pool_out, int32_t* idx, float* scores,
-                                   float* block_max, uint32_t* counters, hipStream_t stream);
-
 // Cache write: ratio-m weighted merge of fp32 token rows (D a power of two,
 // >= 32) quantized to MXFP4 codes and E8M0 scales; and fp32 -> FP8 E4M3 of n
 // elements (n % 4 == 0).

@@ -76,8 +76,7 @@ class Step:
         self.pool_scores = torch.empty((R, 8 * n_pool), dtype=torch.float32, device=dev)
         self.idx = [torch.empty((R, k), dtype=torch.int32, device=dev) for _ in self.modes]
         self.out = [torch.empty((R, H, 512), dtype=torch.float32, device=dev) for _ in self.modes]
-        # zeroed once: its row counters must start at zero (every call leaves them so)
-        self.ws_full = torch.zeros(max(1, csa2_workspace_bytes(CSA2_OP_INDEX_FULL, B, M, N, 0, k)),
+        self.ws_full = torch.empty(max(1, csa2_workspace_bytes(CSA2_OP_INDEX_FULL, B, M, N, 0, k)),
                                    dtype=torch.uint8, device=dev)
         self.ws_attn = torch.empty(max(1, csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, M, 0, H, k + win_max)),
                                    dtype=torch.uint8, device=dev)

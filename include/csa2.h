@@ -173,18 +173,11 @@ int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, c
  * those are rescored.  With fewer than 16 queries per sequence (decode) the scan
  * stores every score instead (into `scores`, else the workspace) and one
  * workgroup per row builds the pool and ranks the stored scores of its first kb
- * blocks; with one query per sequence, k >= 1, at most 16,384 rows and rows of
- * at most 16,384 entries whose every block fits in the pool, a single launch
- * does it all: the last workgroup to finish scanning a row (a per-row counter
- * in the workspace) ranks that row.  The results are the same on every route.
+ * blocks; the results are the same.
  *   scores, block_max  optional outputs (NULL to skip; block_max then lives in
  *                      the workspace).
  *   pool_blocks  i32[R][n_pool] required;  idx i32[R][k] or NULL (k = 0 skips).
- *   workspace    device memory of csa2_workspace_bytes(CSA2_OP_INDEX_FULL, ...).
- *                Its first 64 KiB are row counters: they must be zero before
- *                the first call that uses this workspace (clear it once after
- *                allocating it) and every call leaves them zero, so one
- *                workspace serves calls of any shape in stream order.
+ *   workspace    device memory of csa2_workspace_bytes(CSA2_OP_INDEX_FULL, ...)
  * Returns CSA2_OK, CSA2_ERR_INVALID, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP.
  */
 int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales,

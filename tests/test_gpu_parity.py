@@ -177,13 +177,12 @@ def test_index_full_short_context(kind, N, M, k, nv):
 
 
 def test_index_full_short_rows_reuse_one_workspace():
-    """The one-launch short-row indexer counts workgroups per row in the
-    workspace's first 64 KiB: every call leaves them zero, so one workspace
-    serves calls of different shapes in a row, each bit-exact."""
+    """One workspace serves short-row decode calls of different shapes in a row
+    (what a call leaves in it never leaks into the next), each bit-exact."""
     shapes = [(3, 4096, [4096, 4000, 1]), (7, 16384, [16384, 9001, 0, 5, 16383, 8192, 1024]),
               (2, 100, [100, 37]), (5, 8193, [8193, 8192, 1, 4096, 777])]
     need = max(csa2.csa2_workspace_bytes(csa2.CSA2_OP_INDEX_FULL, B, 1, N, 0, 512) for B, N, _ in shapes)
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
     for i, (B, N, nv) in enumerate(shapes):
         w = Workload("small", 500 + i, B=B, N=N, k=512)
         cache, (lay,) = host_inputs(w, kind="ties" if i % 2 else "normal")
@@ -198,7 +197,6 @@ def test_index_full_short_rows_reuse_one_workspace():
         torch.cuda.synchronize()
         assert np.array_equal(pool.cpu().numpy(), ref["pool_blocks"])
         assert np.array_equal(idx.cpu().numpy(), ref["idx"])
-        assert int(ws[:65536].abs().sum()) == 0   # the row counters are back at zero
 
 
 @pytest.mark.parametrize("kind", ["normal", "ties"])
