@@ -17,8 +17,7 @@ MEASURE_LIB = os.path.join(HERE, "libcsa2_measure.so")
 MEASURE_SOURCES = ["measure.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["scan.hip", "prefill_scan.hip", "prefill_select.hip", "select.hip", "attn.hip", "cache_write.hip",
-           "csa2_abi.hip"]
+SOURCES = ["scan.hip", "prefill_scan.hip", "select.hip", "attn.hip", "cache_write.hip", "csa2_abi.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -39,46 +39,6 @@ inline FullWs full_ws(int64_t R, int M, int64_t N_max, int k) {
   return w;
 }
 
-// The fused prefill selection (many queries per sequence, rows of at most
-// 1,048,576 entries, kb <= 2048, neither scores nor block maxima asked for):
-// chunk summaries, thresholds, chunk offsets and the candidate lists, sized for
-// the worst case (every slot of every chunk a candidate).  It shares the
-// workspace with the staged route; one call uses one of them.
-inline int64_t fused_nsub(int64_t N_max) { return (N_max + csa2::kPfSubKeys - 1) / csa2::kPfSubKeys; }
-
-inline bool fused_prefill_shape(int M, int64_t N_max) {
-  return M >= kStoreScoresBelowM && 4 * fused_nsub(N_max) <= csa2::kPfSummaryCap;
-}
-
-struct FusedWs {
-  size_t summ, thr, offp, offk, pool_key, pool_id, kb_key, kb_id, kb_sc, kbslot, total;
-};
-
-inline FusedWs fused_ws(int64_t R, int64_t N_max, int k) {
-  FusedWs f;
-  const int64_t nsub = fused_nsub(N_max);
-  const size_t cap = (size_t)csa2::kPfSubBlocks * nsub;
-  f.summ = 0;
-  f.thr = align_up((size_t)R * nsub * 4 * sizeof(uint32_t));
-  f.offp = align_up(f.thr + (size_t)R * 4 * sizeof(uint32_t));
-  f.offk = align_up(f.offp + (size_t)R * nsub * sizeof(uint32_t));
-  f.pool_key = align_up(f.offk + (size_t)R * nsub * sizeof(uint32_t));
-  f.pool_id = align_up(f.pool_key + (size_t)R * cap * sizeof(float));
-  f.kb_key = align_up(f.pool_id + (size_t)R * cap * sizeof(int32_t));
-  f.kb_id = align_up(f.kb_key + (size_t)R * cap * sizeof(float));
-  f.kb_sc = align_up(f.kb_id + (size_t)R * cap * sizeof(int32_t));
-  f.kbslot = align_up(f.kb_sc + (size_t)R * cap * 8 * sizeof(float));
-  f.total = align_up(f.kbslot + (size_t)R * (k > 0 ? k : 0) * sizeof(int32_t));
-  return f;
-}
-
-// bytes csa2_index_full needs: the larger of the two routes' layouts
-inline size_t index_full_ws_bytes(int64_t R, int M, int64_t N_max, int k) {
-  const size_t a = full_ws(R, M, N_max, k).total;
-  const size_t b = fused_prefill_shape(M, N_max) ? fused_ws(R, N_max, k).total : 0;
-  return a > b ? a : b;
-}
-
 // Every tensor pointer the caller passes must be 16-byte aligned (NULL passes).
 inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 template <typename... P>
@@ -180,36 +140,8 @@ int index_full_args(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
   return CSA2_OK;
 }
 
-// The fused prefill selection's five launches.
-int fused_prefill_run(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
-                      const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max, int n_pool,
-                      int kb, int k, int32_t* pool_blocks, int32_t* idx, char* ws, hipStream_t s) {
-  const int64_t R = (int64_t)B * M;
-  const FusedWs fw = fused_ws(R, N_max, k);
-  csa2::PfFused f;
-  f.summ = reinterpret_cast<uint32_t*>(ws + fw.summ);
-  f.thr = reinterpret_cast<uint32_t*>(ws + fw.thr);
-  f.offp = reinterpret_cast<uint32_t*>(ws + fw.offp);
-  f.offk = reinterpret_cast<uint32_t*>(ws + fw.offk);
-  f.nsub = fused_nsub(N_max);
-  f.cap = (int64_t)csa2::kPfSubBlocks * f.nsub;
-  f.pool_key = reinterpret_cast<float*>(ws + fw.pool_key);
-  f.pool_id = reinterpret_cast<int32_t*>(ws + fw.pool_id);
-  f.kb_key = reinterpret_cast<float*>(ws + fw.kb_key);
-  f.kb_id = reinterpret_cast<int32_t*>(ws + fw.kb_id);
-  f.kb_sc = reinterpret_cast<float*>(ws + fw.kb_sc);
-  f.kbslot = reinterpret_cast<int32_t*>(ws + fw.kbslot);
-  if (csa2::launch_prefill_summary(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, f, s) != hipSuccess)
-    return CSA2_ERR_HIP;
-  if (csa2::launch_prefill_thresholds(f, (int)R, n_pool, kb, s) != hipSuccess) return CSA2_ERR_HIP;
-  if (csa2::launch_prefill_emit(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, f, s) != hipSuccess)
-    return CSA2_ERR_HIP;
-  if (csa2::launch_select_list_mem(f, (int)R, n_pool, pool_blocks, kb, s) != hipSuccess) return CSA2_ERR_HIP;
-  return hip_status(csa2::launch_prefill_final(f, n_visible, N_max, (int)R, n_pool, pool_blocks, kb, k, idx, s));
-}
-
 // The Full-layer indexer's launches, with the arguments checked and `ws`
-// holding at least index_full_ws_bytes(...) bytes.
+// holding at least full_ws(...).total bytes.
 int index_full_run(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes, const uint8_t* k_scales,
                    const int32_t* n_visible, int B, int M, int64_t N_max, int n_pool, int k, float* scores,
                    float* block_max, int32_t* pool_blocks, int32_t* idx, char* ws, hipStream_t s) {
@@ -239,11 +171,6 @@ int index_full_run(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
     // shapes the fused kernel does not cover: the staged selection below (the
     // scan's outputs are in place)
   } else {
-    // prefill: the fused selection when the caller asks for neither scores nor
-    // block maxima
-    if (!scores && !block_max && kb <= 2048 && fused_prefill_shape(M, N_max))
-      return fused_prefill_run(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool, kb, k,
-                               pool_blocks, idx, ws, s);
     const hipError_t e = csa2::launch_index_scan(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max,
                                                  scores, bmax, nblk, smax, nsup, s);
     if (e != hipSuccess) return CSA2_ERR_HIP;
@@ -308,7 +235,8 @@ int csa2_index_full(const uint8_t* q_codes, const uint8_t* q_scales, const uint8
                                  block_max, pool_blocks, idx);
   if (st != CSA2_OK) return st;
   if (misaligned(workspace)) return CSA2_ERR_INVALID;
-  if (!workspace || workspace_bytes < index_full_ws_bytes((int64_t)B * M, M, N_max, k)) return CSA2_ERR_WORKSPACE;
+  const FullWs w = full_ws((int64_t)B * M, M, N_max, k);
+  if (!workspace || workspace_bytes < w.total) return CSA2_ERR_WORKSPACE;
   return index_full_run(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool, k, scores, block_max,
                         pool_blocks, idx, static_cast<char*>(workspace), as_stream(stream));
 }
@@ -320,7 +248,7 @@ int csa2_index_full_static(const uint8_t* q_codes, const uint8_t* q_scales, cons
   const int st = index_full_args(q_codes, q_scales, k_codes, k_scales, n_visible, B, M, N_max, n_pool, k, scores,
                                  block_max, pool_blocks, idx);
   if (st != CSA2_OK) return st;
-  if (index_full_ws_bytes((int64_t)B * M, M, N_max, k) > (size_t)CSA2_STATIC_SCRATCH_BYTES) return CSA2_ERR_TOO_LARGE;
+  if (full_ws((int64_t)B * M, M, N_max, k).total > (size_t)CSA2_STATIC_SCRATCH_BYTES) return CSA2_ERR_TOO_LARGE;
   hipStream_t s = as_stream(stream);
   char* ws = nullptr;
   const int got = scratch_for(s, &ws);
@@ -397,7 +325,7 @@ size_t csa2_workspace_bytes(int op, int B, int M, int64_t N_max, int H, int k) {
   const int64_t R = (int64_t)B * M;
   if (op == CSA2_OP_INDEX_FULL) {
     if (N_max < 1) return 0;
-    return index_full_ws_bytes(R, M, N_max, k);
+    return full_ws(R, M, N_max, k).total;
   }
   if (op == CSA2_OP_SPARSE_ATTN) {
     if (H != 16 && H != 32 && H != 64) return 0;

@@ -17,47 +17,6 @@ hipError_t launch_prefill_scan(const uint8_t* q_codes, const uint8_t* q_scales, 
                                float* scores, float* block_max, int64_t nblk_stride, float* super_max,
                                int64_t nsup_stride, hipStream_t stream);
 
-// The fused prefill selection (many queries per sequence): the Full layer's
-// pool and top-k without storing every query's block maxima.  Its buffers, for
-// R = B*M query rows, nsub = ceil(N_max / 128) sub-chunks of 16 blocks and
-// cap = 16 * nsub slots per list and row:
-struct PfFused {
-  uint32_t* summ;      // [R][nsub][4] the sub-chunk's four largest block keys, descending (0 = none)
-  uint32_t* thr;       // [R][4] T_pool, T_kb, pool-list length, kb-list length
-  uint32_t* offp;      // [R][nsub] the sub-chunk's first pool-list slot
-  uint32_t* offk;      // [R][nsub] its first kb-list slot
-  int64_t nsub, cap;
-  float* pool_key;     // [R][cap] pool list: block maximum of each candidate
-  int32_t* pool_id;    //          its block id; -1 marks an empty slot
-  float* kb_key;       // [R][cap] kb list (candidates for the first kb blocks), likewise
-  int32_t* kb_id;
-  float* kb_sc;        // [R][cap][8] the eight position scores of each kb-list block
-  int32_t* kbslot;     // [R][kb] kb-list slots of the first kb blocks (rows the memory path ranks)
-};
-constexpr int kPfChunkKeys = 256;                  // keys per prefill-scan workgroup
-constexpr int kPfSubKeys = 128;                    // keys per summarised sub-chunk
-constexpr int kPfSubBlocks = kPfSubKeys / 8;
-constexpr int kPfSummaryCap = 16384;               // stored keys per row the thresholds hold (rows <= 524,288)
-constexpr int kPfListRegCap = 8192;                // list slots the register ranking holds
-// Pass 1: the prefill scan storing summ.
-hipError_t launch_prefill_summary(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
-                                  const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
-                                  const PfFused& f, hipStream_t stream);
-// Per row: T_pool (the n_pool-th largest stored key, 1 when fewer), T_kb (the
-// kb-th, 0xFFFFFFFF for kb = 0), the chunks' slot counts and offsets.
-// Rows of at most kPfSummaryCap / 4 sub-chunks.
-hipError_t launch_prefill_thresholds(const PfFused& f, int R, int n_pool, int kb, hipStream_t stream);
-// Pass 2: the prefill scan again, writing the candidate lists.
-hipError_t launch_prefill_emit(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
-                               const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
-                               const PfFused& f, hipStream_t stream);
-// Rows whose lists exceed kPfListRegCap: pool and first-kb slots from memory.
-hipError_t launch_select_list_mem(const PfFused& f, int R, int n_pool, int32_t* pool_out, int kb, hipStream_t stream);
-// The pool (ids ascending, -1 padded) and the top-k (ids ascending, -1 padded)
-// of every row from its list.
-hipError_t launch_prefill_final(const PfFused& f, const int32_t* n_visible, int64_t N_max, int R, int n_pool,
-                                int32_t* pool_out, int kb, int k, int32_t* idx, hipStream_t stream);
-
 hipError_t launch_pool_scan(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                             const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool,
                             const int32_t* n_visible, int B, int M, int64_t N_max, float* pool_scores,
@@ -66,7 +25,7 @@ hipError_t launch_pool_scan(const uint8_t* q_codes, const uint8_t* q_scales, con
 // Ranked selection.  layout 0: block maxima (row length ceil(n_visible/8),
 // stride `stride`); 1: pool slots (8*n_pool per row, positions through
 // pool_blocks); 2: full score rows (length min(n_visible, stride)).
-enum SelectLayout { kSelBlocks = 0, kSelPool = 1, kSelFull = 2, kSelList = 3 };
+enum SelectLayout { kSelBlocks = 0, kSelPool = 1, kSelFull = 2 };
 
 // super_max (blocks layout only, may be null): maxima of 8 consecutive blocks,
 // row stride nsup_stride, as written by the indexer scan.

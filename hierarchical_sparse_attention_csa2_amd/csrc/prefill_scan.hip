@@ -55,36 +55,6 @@ struct PfStage {
   float bm[kPfQueriesPerWave][kPfBmLd];
 };
 
-// The second pass's kb-list position scores, staged per wave in the key loop:
-// entries (row, block) in the order found; each row's kb-list slot layout per
-// sub-chunk (first slot; kb mask | 16-slot flag << 16 | packed count << 20).
-constexpr int kPfRing = 64;
-struct PfRing {
-  float sc[kPfRing][8];
-  int rb[kPfRing];
-  uint32_t kinfo[kPfQueriesPerWave][2][2];
-};
-
-// Output of the prefill scan: block maxima (and super-block maxima, scores),
-// the sub-chunk summaries of the fused selection, or its candidate lists.
-enum { kPfOutMaxima = 0, kPfOutSummary = 1, kPfOutEmit = 2 };
-static_assert(kPfKeyChunk == kPfChunkKeys && kPfKeyChunk == 2 * kPfSubKeys,
-              "a workgroup's chunk is two sub-chunks: one per half-wave in the summary");
-
-// u32 insertion into a descending top-4
-__device__ __forceinline__ void top4_insert(uint32_t x, uint32_t& t0, uint32_t& t1, uint32_t& t2, uint32_t& t3) {
-  uint32_t m = t0 > x ? t0 : x;
-  x = t0 > x ? x : t0;
-  t0 = m;
-  m = t1 > x ? t1 : x;
-  x = t1 > x ? x : t1;
-  t1 = m;
-  m = t2 > x ? t2 : x;
-  x = t2 > x ? x : t2;
-  t2 = m;
-  t3 = t3 > x ? t3 : x;
-}
-
 // Workgroup-wide: the query scale statistics of each wave and the chunk's
 // tiles that need the VALU path.
 struct PfShared {
@@ -122,15 +92,13 @@ __device__ __noinline__ float pair_score_valu(const uint8_t* qc, const uint8_t* 
   return canonical_nan(s);
 }
 
-template <bool kScores, bool kSuper, int kOut>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(kOut == kPfOutEmit ? 5 : 1))) void
-prefill_scan_kernel(
+template <bool kScores, bool kSuper>
+__global__ __launch_bounds__(kPfThreads) void prefill_scan_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     const int32_t* __restrict__ n_visible, int M, int64_t N_max, int64_t nblk_stride, int64_t nsup_stride,
-    float* __restrict__ scores, float* __restrict__ block_max, float* __restrict__ super_max, PfFused fz) {
+    float* __restrict__ scores, float* __restrict__ block_max, float* __restrict__ super_max) {
   __shared__ PfShared sh;
-  __shared__ PfRing ring_all[kOut == kPfOutEmit ? kPfWaves : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   PfStage& st = sh.stage[wave];
   const int64_t seq = blockIdx.z;
@@ -160,23 +128,6 @@ prefill_scan_kernel(
   nv = nv < 0 ? 0 : (nv > N ? N : nv);
   const int nv_max = (int)wave_max_u32((uint32_t)nv);
   const int nv_min = (int)wave_min_u32(q_ok ? (uint32_t)nv : 0x7FFFFFFFu);
-  // second pass of the fused selection: this row's thresholds and, for this
-  // lane's sub-chunk (its half-wave's 16 blocks), the stored keys and each
-  // list's first slot (loaded now, used after the key loop)
-  uint32_t Tp = 0xFFFFFFFFu, Tk = 0xFFFFFFFFu;
-  u32x4_t xs = {0u, 0u, 0u, 0u};
-  uint32_t opl = 0u, okl = 0u;
-  const int64_t sub = 2 * (int64_t)blockIdx.y + half;
-  if (kOut == kPfOutEmit && q_ok) {   // both lanes of a row hold its thresholds
-    const u32x4_t t = *reinterpret_cast<const u32x4_t*>(fz.thr + 4 * r);
-    if (sub < fz.nsub) {
-      xs = *reinterpret_cast<const u32x4_t*>(fz.summ + 4 * (r * fz.nsub + sub));
-      opl = fz.offp[r * fz.nsub + sub];
-      okl = fz.offk[r * fz.nsub + sub];
-    }
-    Tp = t[0];
-    Tk = t[1];
-  }
   // the query scale statistics: smallest and largest byte, widest spread
   const uint32_t e0 = qsc & 0xFF, e1 = (qsc >> 8) & 0xFF, e2 = (qsc >> 16) & 0xFF, e3 = qsc >> 24;
   const uint32_t qmn = min(min(e0, e1), min(e2, e3)), qmx = max(max(e0, e1), max(e2, e3));
@@ -215,28 +166,6 @@ prefill_scan_kernel(
   __syncthreads();
   const uint32_t bad_tiles = sh.bad_tiles;
   if (qbase >= M) return;   // no barriers below: waves leave independently, each with its own staging
-  if (kOut == kPfOutEmit && __ballot(xs[0] >= Tp) == 0ull) return;   // no row of the wave has a candidate here
-  // kb-list position scores of the blocks at or above T_kb, staged in the
-  // wave's ring during the key loop (no global store in the loop); blocks
-  // found after the ring is full are rescored after the loop
-  PfRing& ring = ring_all[kOut == kPfOutEmit ? wave : 0];
-  int nring = 0;       // entries found so far (wave-uniform)
-  uint32_t ovf = 0u;   // this row's blocks past the ring
-  auto kb_stage = [&](int b, uint32_t kk, float f0, float f1, float f2, float f3) {
-    const bool qk = kk != 0u && kk >= Tk;
-    const uint32_t lo = (uint32_t)__ballot(qk);   // rows (low half-wave lanes) with block b at or above T_kb
-    if (lo == 0u) return;
-    const int e = nring + __builtin_popcount(lo & ((1u << col) - 1u));
-    if (qk) {
-      if (e < kPfRing) {
-        *reinterpret_cast<float4*>(&ring.sc[e][4 * half]) = make_float4(f0, f1, f2, f3);
-        if (half == 0) ring.rb[e] = (col << 8) | b;
-      } else {
-        ovf |= 1u << b;
-      }
-    }
-    nring += __builtin_popcount(lo);
-  };
 
   // A operands (keys): lane l is key k0 + l%32, K group l/32
   const uint8_t* kc = k_codes + seq * N_max * 64;
@@ -305,14 +234,6 @@ prefill_scan_kernel(
     // lanes of the low half stage blocks 0, 1, the high half blocks 2, 3
     st.bm[col][4 * ti + 2 * half] = half ? bm[2] : bm[0];
     st.bm[col][4 * ti + 2 * half + 1] = half ? bm[3] : bm[1];
-    if (kOut == kPfOutEmit) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t kk = 8 * ((kbeg >> 3) + 4 * ti + j) < nv ? order_key(bm[j]) : 0u;
-        kb_stage(4 * ti + j, kk, acc[4 * j] + 0.0f, acc[4 * j + 1] + 0.0f, acc[4 * j + 2] + 0.0f,
-                 acc[4 * j + 3] + 0.0f);
-      }
-    }
   };
 
   KeyTile cur[kPfPrefetch];
@@ -334,12 +255,10 @@ prefill_scan_kernel(
     unsafe_tiles &= unsafe_tiles - 1;
     const int k0 = kbeg + kPfTileKeys * ti;
     uint32_t mk[4] = {0u, 0u, 0u, 0u};
-    float vs[16];
     for (int i = 0; i < 16; ++i) {
       const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
       const int kk = key < N ? key : N - 1;
       const float v = pair_score_valu(q_codes + r * 64, q_scales + r * 4, kc + (int64_t)kk * 64, ks + (int64_t)kk * 4);
-      vs[i] = v;
       if (key < nv) {
         if (kScores) scores[r * N_max + key] = v;
         const uint32_t k = order_key(v);
@@ -358,139 +277,13 @@ prefill_scan_kernel(
     }
     st.bm[col][4 * ti + 2 * half] = half ? bm[2] : bm[0];
     st.bm[col][4 * ti + 2 * half + 1] = half ? bm[3] : bm[1];
-    if (kOut == kPfOutEmit) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t kk = 8 * ((kbeg >> 3) + 4 * ti + j) < nv ? order_key(bm[j]) : 0u;
-        kb_stage(4 * ti + j, kk, vs[4 * j], vs[4 * j + 1], vs[4 * j + 2], vs[4 * j + 3]);
-      }
-    }
   }
   __builtin_amdgcn_wave_barrier();   // the wave's own staging writes precede these reads
-
-  const int nblk_here = (ntiles * kPfTileKeys) >> 3;
-  // this lane's row, blocks [16 half, 16 half + 16) of the chunk: their keys
-  // (0 past the row's visible range)
-  auto block_key = [&](int b) -> uint32_t {
-    return (b < nblk_here && 8 * ((kbeg >> 3) + b) < nv) ? order_key(st.bm[col][b]) : 0u;
-  };
-  if (kOut == kPfOutSummary) {
-    // this lane's sub-chunk: the half-wave's 16 blocks
-    uint32_t t0 = 0u, t1 = 0u, t2 = 0u, t3 = 0u;
-#pragma unroll
-    for (int e = 0; e < kPfSubBlocks; ++e) top4_insert(block_key(kPfSubBlocks * half + e), t0, t1, t2, t3);
-    const int64_t sub = 2 * (int64_t)blockIdx.y + half;
-    if (q_ok && sub < fz.nsub) *reinterpret_cast<u32x4_t*>(fz.summ + 4 * (r * fz.nsub + sub)) = u32x4_t{t0, t1, t2, t3};
-    return;
-  }
-  if (kOut == kPfOutEmit) {
-    // this lane's sub-chunk: each list's layout (all 16 blocks, or the npl /
-    // nkl candidates packed in block order), then its entries from the staged
-    // block maxima (a lane past the rows holds Tp = Tk = max; one past the
-    // sub-chunks holds xs = 0 and no visible block)
-    const bool fpl = xs[3] >= Tp, fkl = xs[3] >= Tk;
-    const int npl = (int)(xs[0] >= Tp) + (int)(xs[1] >= Tp) + (int)(xs[2] >= Tp);
-    const int nkl = (int)(xs[0] >= Tk) + (int)(xs[1] >= Tk) + (int)(xs[2] >= Tk);
-    uint32_t pm = 0u, km = 0u;
-#pragma unroll
-    for (int e = 0; e < kPfSubBlocks; ++e) {
-      const uint32_t kk = block_key(kPfSubBlocks * half + e);
-      pm |= (kk != 0u && kk >= Tp) ? 1u << e : 0u;
-      km |= (kk != 0u && kk >= Tk) ? 1u << e : 0u;
-    }
-    {
-      const int32_t blk0 = (kbeg >> 3) + kPfSubBlocks * half;
-      const float* bmr = &st.bm[col][kPfSubBlocks * half];
-      // packed sub-chunks: each lane its own candidates
-      uint32_t bits = q_ok && !fpl ? pm : 0u;
-      while (bits) {
-        const int e = __builtin_ctz(bits);
-        bits &= bits - 1u;
-        const int rp = __builtin_popcount(pm & ((1u << e) - 1u));
-        if (rp < npl) {   // always: the slots reserved for the sub-chunk
-          fz.pool_key[r * fz.cap + opl + rp] = bmr[e];
-          fz.pool_id[r * fz.cap + opl + rp] = blk0 + e;
-        }
-      }
-      bits = q_ok && !fkl ? km : 0u;
-      while (bits) {
-        const int e = __builtin_ctz(bits);
-        bits &= bits - 1u;
-        const int rk = __builtin_popcount(km & ((1u << e) - 1u));
-        if (rk < nkl) {
-          fz.kb_key[r * fz.cap + okl + rk] = bmr[e];
-          fz.kb_id[r * fz.cap + okl + rk] = blk0 + e;
-        }
-      }
-      // 16-slot sub-chunks: the wave writes each one's slots together, lanes
-      // 0-15 the block maxima and 16-31 the ids of the pool list, lanes 32-63
-      // the same in the kb list
-      for (int t = 0; t < 2; ++t) {
-        uint64_t fm = __ballot(q_ok && (t ? fkl : fpl));
-        while (fm) {
-          const int L = __builtin_ctzll(fm);
-          fm &= fm - 1ull;
-          const int c = L & 31, h = L >> 5, e = lane & 15;
-          const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(t ? okl : opl), L);
-          const uint32_t mask = (uint32_t)__builtin_amdgcn_readlane((int)(t ? km : pm), L);
-          const int64_t rr = seq * M + qbase + c;
-          if ((lane >> 5) == 0) {   // the t-th list, one half-wave
-            if (lane < 16) (t ? fz.kb_key : fz.pool_key)[rr * fz.cap + base + e] = st.bm[c][kPfSubBlocks * h + e];
-            else (t ? fz.kb_id : fz.pool_id)[rr * fz.cap + base + e] =
-                (mask >> e) & 1u ? (kbeg >> 3) + kPfSubBlocks * h + e : -1;
-          }
-        }
-      }
-    }
-    ring.kinfo[col][half][0] = okl;
-    ring.kinfo[col][half][1] = km | (fkl ? 0x10000u : 0u) | ((uint32_t)nkl << 20);
-    __builtin_amdgcn_wave_barrier();
-    // the kb-list slot of block b of a row, from that row's sub-chunk record
-    auto kb_slot = [&](int c, int b, uint32_t& slot) -> bool {
-      const uint32_t base = ring.kinfo[c][b >> 4][0], inf = ring.kinfo[c][b >> 4][1];
-      const int eb = b & 15;
-      if (inf & 0x10000u) {
-        slot = base + eb;
-        return true;
-      }
-      const int rk = __builtin_popcount(inf & 0xFFFFu & ((1u << eb) - 1u));
-      slot = base + rk;
-      return rk < (int)(inf >> 20);   // always: the slots reserved for the sub-chunk
-    };
-    // staged position scores to their slots, one entry a lane
-    const int nst = nring < kPfRing ? nring : kPfRing;
-    for (int e = lane; e < nst; e += 64) {
-      const int rb = ring.rb[e];
-      const int c = rb >> 8, b = rb & 31;
-      uint32_t slot;
-      if (kb_slot(c, b, slot)) {
-        float4* dst = reinterpret_cast<float4*>(fz.kb_sc + ((seq * M + qbase + c) * fz.cap + slot) * 8);
-        dst[0] = *reinterpret_cast<const float4*>(&ring.sc[e][0]);
-        dst[1] = *reinterpret_cast<const float4*>(&ring.sc[e][4]);
-      }
-    }
-    // blocks found after the ring filled: rescored on the VALU (the fixed-order
-    // sum, which the matrix cores' result equals), this lane's four positions
-    while (ovf) {
-      const int b = __builtin_ctz(ovf);
-      ovf &= ovf - 1u;
-      uint32_t slot;
-      if (!kb_slot(col, b, slot)) continue;
-      float v[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        int key = kbeg + 8 * b + 4 * half + t;
-        key = key < N ? key : N - 1;
-        v[t] = pair_score_valu(q_codes + r * 64, q_scales + r * 4, kc + (int64_t)key * 64, ks + (int64_t)key * 4);
-      }
-      *reinterpret_cast<float4*>(fz.kb_sc + ((r * fz.cap + slot) * 8 + 4 * half)) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-    return;
-  }
 
   // block maxima out: each store instruction covers whole rows of the chunk's
   // blocks (several rows when a row has fewer than 64); blocks past a row's
   // visible range are not written
+  const int nblk_here = (ntiles * kPfTileKeys) >> 3;
   {
     constexpr int kRowsPer = kPfBlocks >= 64 ? 1 : 64 / kPfBlocks;
     constexpr int kStoresPerRow = kPfBlocks >= 64 ? kPfBlocks / 64 : 1;
@@ -547,35 +340,14 @@ hipError_t launch_prefill_scan(const uint8_t* q_codes, const uint8_t* q_scales, 
                                int64_t nsup_stride, hipStream_t stream) {
   dim3 grid((unsigned)((M + kPfQueriesPerWG - 1) / kPfQueriesPerWG), (unsigned)((N_max + kPfKeyChunk - 1) / kPfKeyChunk),
             (unsigned)B);
-#define CSA2_PF(S, P)                                                                                        \
-  hipLaunchKernelGGL((prefill_scan_kernel<S, P, kPfOutMaxima>), grid, dim3(kPfThreads), 0, stream, q_codes,   \
-                     q_scales, k_codes, k_scales, n_visible, M, N_max, nblk_stride, nsup_stride, scores,      \
-                     block_max, super_max, PfFused{})
+#define CSA2_PF(S, P)                                                                                            \
+  hipLaunchKernelGGL((prefill_scan_kernel<S, P>), grid, dim3(kPfThreads), 0, stream, q_codes, q_scales, k_codes, \
+                     k_scales, n_visible, M, N_max, nblk_stride, nsup_stride, scores, block_max, super_max)
   if (scores && super_max) CSA2_PF(true, true);
   else if (scores) CSA2_PF(true, false);
   else if (super_max) CSA2_PF(false, true);
   else CSA2_PF(false, false);
 #undef CSA2_PF
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill_summary(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
-                                  const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
-                                  const PfFused& f, hipStream_t stream) {
-  dim3 grid((unsigned)((M + kPfQueriesPerWG - 1) / kPfQueriesPerWG), (unsigned)((f.nsub + 1) / 2), (unsigned)B);
-  hipLaunchKernelGGL((prefill_scan_kernel<false, false, kPfOutSummary>), grid, dim3(kPfThreads), 0, stream, q_codes,
-                     q_scales, k_codes, k_scales, n_visible, M, N_max, (int64_t)0, (int64_t)0, nullptr, nullptr,
-                     nullptr, f);
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill_emit(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
-                               const uint8_t* k_scales, const int32_t* n_visible, int B, int M, int64_t N_max,
-                               const PfFused& f, hipStream_t stream) {
-  dim3 grid((unsigned)((M + kPfQueriesPerWG - 1) / kPfQueriesPerWG), (unsigned)((f.nsub + 1) / 2), (unsigned)B);
-  hipLaunchKernelGGL((prefill_scan_kernel<false, false, kPfOutEmit>), grid, dim3(kPfThreads), 0, stream, q_codes,
-                     q_scales, k_codes, k_scales, n_visible, M, N_max, (int64_t)0, (int64_t)0, nullptr, nullptr,
-                     nullptr, f);
   return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ struct SelShared {
 struct RowView {
   int layout;
   const float* s;          // row base
-  const int32_t* pb;       // pool layout: this row's pool block ids; list layout: item ids (-1 = empty)
+  const int32_t* pb;       // pool layout: this row's pool block ids
   int64_t n;               // elements in the row
   int64_t nv;              // visible positions
   __device__ __forceinline__ uint32_t key_mem(int64_t i) const {
@@ -71,14 +71,11 @@ struct RowView {
       const int64_t blk = pb[i >> 3];
       const int64_t p = 8 * blk + (i & 7);
       if (blk < 0 || p >= nv) return 0u;
-    } else if (layout == kSelList) {
-      if (pb[i] < 0) return 0u;
     }
     return order_key(s[i]);
   }
   __device__ __forceinline__ int32_t id_mem(int64_t i) const {
     if (layout == kSelPool) return (int32_t)(8 * (int64_t)pb[i >> 3] + (i & 7));
-    if (layout == kSelList) return pb[i];
     return (int32_t)i;
   }
 };
@@ -962,50 +959,6 @@ __global__ __launch_bounds__(kSelThreads) void select_mem_kernel(int layout, con
   }
   reduce_stats(sh, st);
   select_targets<kSrcMem, kIdRow, false, false>(sh, row, row.n, k1, o1, k2, o2);
-}
-
-// The fused prefill selection's candidate lists that exceed what the register
-// ranking holds (many equal block maxima), ranked with the list in memory: the
-// pool from the pool list (ids) and the first kb blocks from the kb list (list
-// slots).  Grid 2R: workgroup t*R + r takes list t of row r; short lists exit.
-__global__ __launch_bounds__(kSelThreads) void select_list_mem_kernel(PfFused f, int n_pool,
-                                                                      int32_t* __restrict__ pool_out, int kb) {
-  __shared__ SelShared sh;
-  const int R = (int)(gridDim.x >> 1);
-  const int t = (int)blockIdx.x >= R ? 1 : 0;
-  const int r = (int)blockIdx.x - t * R;
-  if (t == 1 && kb <= 0) return;
-  const int64_t U = f.thr[4 * (int64_t)r + 2 + t];
-  if (U <= kPfListRegCap) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  RowView row;
-  row.layout = kSelList;
-  row.s = (t ? f.kb_key : f.pool_key) + (int64_t)r * f.cap;
-  row.pb = (t ? f.kb_id : f.pool_id) + (int64_t)r * f.cap;
-  row.n = U;
-  row.nv = 0;
-  {
-    KeyStats st;
-    for (int64_t base = 0; base < row.n; base += kSelCap) {
-#pragma unroll 10
-      for (int j = 0; j < kSegIters; ++j) {
-        const int64_t i = base + (int64_t)w * kSegItems + 64 * j + lane;
-        st.add(i < row.n ? row.key_mem(i) : 0u);
-      }
-    }
-    reduce_stats(sh, st);
-    if (t == 0)
-      select_targets<kSrcMem, kIdRow, false, false>(sh, row, row.n, n_pool, pool_out + (int64_t)r * n_pool, 0,
-                                                    nullptr);
-    else
-      select_targets<kSrcMem, kIdIndex, false, false>(sh, row, row.n, kb, f.kbslot + (int64_t)r * kb, 0, nullptr);
-  }
-}
-
-hipError_t launch_select_list_mem(const PfFused& f, int R, int n_pool, int32_t* pool_out, int kb, hipStream_t stream) {
-  hipLaunchKernelGGL(select_list_mem_kernel, dim3(2u * (unsigned)R), dim3(kSelThreads), 0, stream, f, n_pool,
-                     pool_out, kb);
-  return hipGetLastError();
 }
 
 hipError_t launch_select(int layout, const float* scores, int64_t stride, const int32_t* pool_blocks,

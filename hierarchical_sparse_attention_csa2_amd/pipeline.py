@@ -85,11 +85,9 @@ class Step:
     def full_index(self, cache: Cache, li: LayerInputs, idx: torch.Tensor):
         B, M, N = self.B, self.M, self.N
         if not self.staged:
-            # block maxima come out only beside kept scores (asking for them
-            # rules out the fused prefill selection)
             csa2_index_full(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, B, M, N,
                             self.n_pool, self.k, self.pool, idx, self.ws_full, scores=self.scores,
-                            block_max=self.block_max if self.scores is not None else None)
+                            block_max=self.block_max)
             return
         csa2_index_scan(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, B, M, N,
                         self.block_max, scores=self.scores, super_max=self.super_max)

@@ -206,13 +206,11 @@ def test_index_full_short_rows_reuse_one_workspace():
     (20000, 16, 64, 512, "random"),      # pool below k (kb = 64); rows of 0 .. N visible entries
     (70000, 33, 2048, 1000, "random"),   # the wide top-k
     (300, 20, 8, 0, "causal"),           # k = 0: the pool alone
-    (140000, 16, 2048, 512, "causal"),   # more than 16,384 blocks: tied rows take the memory path
+    (140000, 16, 2048, 512, "causal"),   # more than 16,384 blocks a row
 ])
-def test_index_full_prefill_fused(kind, N, M, n_pool, k, nv):
-    """Many queries per sequence through csa2_index_full without block maxima
-    or scores asked for (the fused prefill selection: chunk summaries,
-    thresholds, candidate lists): pool and top-k bit-exact against the oracle,
-    and equal to the staged route's."""
+def test_index_full_prefill(kind, N, M, n_pool, k, nv):
+    """Many queries per sequence through csa2_index_full: pool and top-k
+    bit-exact against the oracle, with and without block maxima asked for."""
     B = 2
     w = Workload("pff", 3 + N + M + k, B=B, N=N, M=M, n_pool=n_pool, k=max(k, 1), prefill_base=N - M)
     cache, (lay,) = host_inputs(w, kind=kind)
@@ -222,7 +220,7 @@ def test_index_full_prefill_fused(kind, N, M, n_pool, k, nv):
         v[0], v[1], v[-1] = 0, N, 1
         lay["n_visible"] = v
     c, l = dev(cache), dev(lay)
-    say(f"index_full fused prefill N={N} M={M} pool={n_pool} k={k} nv={nv} kind={kind}")
+    say(f"index_full prefill N={N} M={M} pool={n_pool} k={k} nv={nv} kind={kind}")
     ref = oracle.index_full(lay["q_codes"], lay["q_scales"], cache["k_codes"], cache["k_scales"], lay["n_visible"],
                             B, M, N, n_pool=n_pool, k=k)
     pool = torch.full((w.R, n_pool), -7, dtype=torch.int32, device="cuda")
@@ -233,7 +231,6 @@ def test_index_full_prefill_fused(kind, N, M, n_pool, k, nv):
     assert np.array_equal(pool.cpu().numpy(), ref["pool_blocks"])
     if k:
         assert np.array_equal(idx.cpu().numpy(), ref["idx"])
-    # the staged route (asked for block maxima) gives the same
     pool2 = torch.empty_like(pool)
     idx2 = torch.empty_like(idx) if k else None
     bmax = torch.empty((w.R, (N + 7) // 8), dtype=torch.float32, device="cuda")
