@@ -280,56 +280,50 @@ __global__ __launch_bounds__(kPfThreads) void prefill_scan_kernel(
   }
   __builtin_amdgcn_wave_barrier();   // the wave's own staging writes precede these reads
 
-  // block maxima out: each store instruction covers whole rows of the chunk's
-  // blocks (several rows when a row has fewer than 64); blocks past a row's
-  // visible range are not written
+  // block maxima out, 8 query rows a pass: lane l takes row row0 + l/8 and the
+  // chunk's blocks 4(l%8) .. 4(l%8)+3, so a row's 32 blocks are 128 contiguous
+  // bytes in 8 lanes (one 16-byte store each when rows are 16-byte aligned);
+  // blocks past a row's visible range are not written.  A super-block (8
+  // blocks) is a lane pair, whose maxima meet in one lane exchange.
   const int nblk_here = (ntiles * kPfTileKeys) >> 3;
+  static_assert(kPfBlocks == 32, "a row's blocks in 8 lanes of 4");
   {
-    constexpr int kRowsPer = kPfBlocks >= 64 ? 1 : 64 / kPfBlocks;
-    constexpr int kStoresPerRow = kPfBlocks >= 64 ? kPfBlocks / 64 : 1;
-    const int rsub = kRowsPer > 1 ? lane / kPfBlocks : 0;
-    for (int row0 = 0; row0 < kPfQueriesPerWave; row0 += kRowsPer) {
+    const int sub = lane >> 3, q4 = lane & 7;
+    const int b0 = 4 * q4;
+    const int blk0 = (kbeg >> 3) + b0;
+    const bool vec = (nblk_stride & 3) == 0;   // blk0 is a multiple of 4
+    for (int row0 = 0; row0 < kPfQueriesPerWave; row0 += 8) {
       if (qbase + row0 >= M) break;
-      const int row = row0 + rsub;
-      int nvr = 0;
-#pragma unroll
-      for (int j = 0; j < kRowsPer; ++j) {
-        const int v = __builtin_amdgcn_readlane(nv, row0 + j);
-        nvr = rsub == j ? v : nvr;
-      }
-#pragma unroll
-      for (int h = 0; h < kStoresPerRow; ++h) {
-        const int b = kRowsPer > 1 ? lane % kPfBlocks : 64 * h + lane;
-        const int blk = (kbeg >> 3) + b;
-        if (qbase + row < M && b < nblk_here && 8 * blk < nvr)
-          block_max[(seq * M + qbase + row) * nblk_stride + blk] = st.bm[row][b];
-      }
-    }
-  }
-  if (kSuper) {
-    // super-block maxima from the staged block maxima (total order of the keys):
-    // 64 / (chunk/64) query rows per store instruction
-    constexpr int kSupers = kPfKeyChunk / 64;
-    constexpr int kRowsPer = 64 / kSupers;
-    const int sidx = lane % kSupers, sp = (kbeg >> 6) + sidx;
-    for (int row0 = 0; row0 < kPfQueriesPerWave; row0 += kRowsPer) {
-      if (qbase + row0 >= M) break;
-      const int row = row0 + lane / kSupers;
-      int nvr = 0;
-#pragma unroll
-      for (int j = 0; j < kRowsPer; ++j) {
-        const int v = __builtin_amdgcn_readlane(nv, row0 + j);
-        nvr = lane / kSupers == j ? v : nvr;
-      }
+      const int row = row0 + sub;
+      const int nvr = __shfl(nv, row);   // lane `row` holds that row's visible count
+      const bool rok = qbase + row < M;
+      float v[4];
+      bool vis[4];
       uint32_t m = 0u;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int b = 8 * sidx + e;
-        const uint32_t k = (b < nblk_here && 8 * ((kbeg >> 3) + b) < nvr) ? order_key(st.bm[row][b]) : 0u;
+      for (int t = 0; t < 4; ++t) {
+        v[t] = st.bm[row][b0 + t];
+        vis[t] = b0 + t < nblk_here && 8 * (blk0 + t) < nvr;
+        const uint32_t k = vis[t] ? order_key(v[t]) : 0u;
         m = k > m ? k : m;
       }
-      if (qbase + row < M && 8 * sidx < nblk_here && 64 * sp < nvr)
-        super_max[(seq * M + qbase + row) * nsup_stride + sp] = key_to_float(m);
+      float* dst = block_max + (seq * M + qbase + row) * nblk_stride + blk0;
+      if (rok) {
+        if (vec && vis[3]) {   // vis[3]: all four visible
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (vis[t]) dst[t] = v[t];
+        }
+      }
+      if (kSuper) {
+        const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false);   // lane l ^ 1
+        m = o > m ? o : m;
+        const int sidx = q4 >> 1, sp = (kbeg >> 6) + sidx;
+        if ((q4 & 1) == 0 && rok && 8 * sidx < nblk_here && 64 * sp < nvr)
+          super_max[(seq * M + qbase + row) * nsup_stride + sp] = key_to_float(m);
+      }
     }
   }
 }
