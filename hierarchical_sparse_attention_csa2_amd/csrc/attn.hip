@@ -365,12 +365,15 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
       for (int m = 0; m < kM; ++m) oacc[m] *= alpha;
       m_run = m_new;
     }
+    // v_exp_f32 directly: arguments lie in [-inf, kLazyRescale], and a result
+    // below 2^-126 (flushed to zero here) is below any weight that can move
+    // the output
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < kT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sacc[t][i] - m_run);
+        const float p = __builtin_amdgcn_exp2f(sacc[t][i] - m_run);
         sacc[t][i] = p;
         psum += p;
       }
