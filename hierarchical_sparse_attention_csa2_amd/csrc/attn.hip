@@ -185,11 +185,14 @@ __device__ __forceinline__ bf16x4_t lds_read_tr4(const __bf16* p) {
 }
 
 // NP head groups of 16 per workgroup, ND waves per head group (each 512/ND
-// dims), CH entries per chunk
-template <int NP, int ND, int CH>
+// dims), CH entries per chunk.  NH = 2: two halves of NP * ND waves each take
+// alternate chunks of the split (their own LDS copies, the same barriers) and
+// merge their softmax states at the end, so a grid of one workgroup per CU
+// keeps two chunks in flight.
+template <int NP, int ND, int CH, int NH>
 __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   constexpr int kChunk = CH;
-  constexpr int NT = NP * ND * 64;
+  constexpr int NT = NP * ND * 64;    // threads of one half
   constexpr int kDims = 512 / ND;     // dims per wave
   constexpr int kS = kDims / 32;      // K steps of S^T
   constexpr int kM = kDims / 16;      // dim tiles of O^T
@@ -197,16 +200,21 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   constexpr int kJ = CH / 32;         // K steps of O^T
   constexpr uint64_t kChunkBits = CH == 64 ? ~0ull : ((1ull << CH) - 1ull);
   static_assert(CH == 32 || CH == 64, "chunk of 32 or 64 entries");
-  __shared__ __attribute__((aligned(16))) __bf16 sK[kChunk * kKLd];
-  __shared__ f32x4 sX[NP * ND * 64 * kT];   // partial S^T tiles of the ND waves of each head group
-  __shared__ int32_t sIdx[kIdxCap];         // the split's selected indices after its first chunk
+  static_assert(NH == 1 || NH == 2, "one or two halves");
+  __shared__ __attribute__((aligned(16))) __bf16 sKh[NH][kChunk * kKLd];
+  __shared__ f32x4 sXh[NH][NP * ND * 64 * kT];   // partial S^T tiles of the ND waves of each head group
+  __shared__ int32_t sIdx[kIdxCap];              // the split's selected indices after each half's first chunk
 
   const int split = blockIdx.x;
   const int r = blockIdx.y;
   const int64_t seq = r / a.M;
   const int tid = threadIdx.x;
+  const int hf = NH > 1 ? __builtin_amdgcn_readfirstlane(tid / NT) : 0;   // half
+  const int tidh = tid - hf * NT;
+  __bf16* sK = sKh[hf];
+  f32x4* sX = sXh[hf];
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tidh >> 6);
   const int pr = w % NP;       // head group of 16
   const int part = w / NP;     // dims [kDims * part, kDims * (part + 1))
   const int dbase = kDims * part;
@@ -224,34 +232,40 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   int c_end = c_begin + a.chunks_per_split;
   c_end = c_end < a.n_chunks ? c_end : a.n_chunks;
 
-  // The first chunk's indices load first and its rows are gathered as soon as
-  // they arrive; later chunks' indices are staged in LDS (visible after the
-  // first chunk's decode barrier), so no chunk waits on a global index load in
-  // the loop.  The query loads after the first gathers.
+  // Half hf takes chunks c_begin + hf, c_begin + hf + NH, ...: n_iter rounds
+  // for both halves (a round past the split is empty for that half).
+  const int n_iter = c_end > c_begin ? (c_end - c_begin + NH - 1) / NH : 0;
+  const int c_first = c_begin + hf;
+
+  // Each half's first chunk's indices load first and its rows are gathered as
+  // soon as they arrive; later chunks' indices are staged in LDS (visible after
+  // the first round's decode barrier), so no chunk waits on a global index load
+  // in the loop.  The query loads after the first gathers.
   Gathered<CH, NT> gr;
   uint64_t mask = 0ull;   // validity of the gathered chunk's entries (uniform)
-  const int staged0 = (c_begin + 1) * kChunk;                         // first staged entry
-  int n_staged = (c_end - c_begin - 1) * kChunk;
+  const int staged0 = (c_begin + NH) * kChunk;                        // first staged entry
+  int n_staged = (c_end - c_begin - NH) * kChunk;
   n_staged = n_staged < a.k - staged0 ? n_staged : a.k - staged0;     // latent entries only
   n_staged = n_staged < kIdxCap ? n_staged : kIdxCap;                 // (a longer split loads the rest)
   {
-    const int e0 = c_begin * kChunk + le;
-    const int32_t p0 = (c_begin < c_end && e0 < a.k) ? a.idx[(int64_t)r * a.k + e0] : -1;
-    int32_t st[kIdxCap / NT];
+    constexpr int kStage = (kIdxCap + NH * NT - 1) / (NH * NT);
+    const int e0 = c_first * kChunk + le;
+    const int32_t p0 = (c_first < c_end && e0 < a.k) ? a.idx[(int64_t)r * a.k + e0] : -1;
+    int32_t st[kStage];
 #pragma unroll
-    for (int j = 0; j < kIdxCap / NT; ++j) {
-      const int t = tid + j * NT;
+    for (int j = 0; j < kStage; ++j) {
+      const int t = tid + j * NH * NT;
       st[j] = t < n_staged ? a.idx[(int64_t)r * a.k + staged0 + t] : -1;
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (c_begin < c_end) {
+    if (c_first < c_end) {
       const EntryRow x = entry_row(a, seq, ws0, E, e0, p0);
       mask = __ballot(x.valid) & kChunkBits;
-      gather_chunk<CH, NT>(a, x.off, mask, c_begin * kChunk, w, lane, gr);
+      gather_chunk<CH, NT>(a, x.off, mask, c_first * kChunk, w, lane, gr);
     }
 #pragma unroll
-    for (int j = 0; j < kIdxCap / NT; ++j) {
-      const int t = tid + j * NT;
+    for (int j = 0; j < kStage; ++j) {
+      const int t = tid + j * NH * NT;
       if (t < n_staged) sIdx[t] = st[j];
     }
   }
@@ -281,21 +295,20 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  for (int c = c_begin; c < c_end; ++c) {
+  for (int it = 0; it < n_iter; ++it) {
+    // Three barriers a round whatever the chunk holds, the same for both
+    // halves; a chunk with no valid entry (past E, past the split) does no work.
+    const int c = c_first + NH * it;
     const int ebase = c * kChunk;
-    if (ebase >= E) break;
     const uint64_t cm = mask;   // this chunk's validity
-    if (cm != 0ull) {
-      __syncthreads();   // previous chunk's LDS reads are done
-      store_chunk<CH, NT>(a, gr, cm, ebase, w, lane, sK);
-      __syncthreads();
-    } else if (c == c_begin) {
-      __syncthreads();   // the staged indices are visible
-    }
-    // the next chunk's rows: in flight during this chunk's products
+    __syncthreads();   // the previous round's LDS reads are done
+    if (cm != 0ull) store_chunk<CH, NT>(a, gr, cm, ebase, w, lane, sK);
+    __syncthreads();   // decoded rows (and, in the first round, the staged indices) visible
+    // this half's next chunk's rows: in flight during this chunk's products
     mask = 0ull;
-    if (c + 1 < c_end && ebase + kChunk < E) {
-      const int e = ebase + kChunk + le;
+    const int cn = c + NH;
+    if (cn < c_end && cn * kChunk < E) {
+      const int e = cn * kChunk + le;
       const int t = e - staged0;
       int32_t p = -1;
       if (t >= n_staged && e < a.k) p = a.idx[(int64_t)r * a.k + e];
@@ -303,9 +316,8 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
       p = t < n_staged ? ps : p;
       const EntryRow x = entry_row(a, seq, ws0, E, e, p);
       mask = __ballot(x.valid) & kChunkBits;
-      gather_chunk<CH, NT>(a, x.off, mask, ebase + kChunk, w, lane, gr);
+      gather_chunk<CH, NT>(a, x.off, mask, cn * kChunk, w, lane, gr);
     }
-    if (cm == 0ull) continue;
 
     // 3. partial S^T[CH entries x 16 heads] over this wave's kDims dims
     // (row 16t + hl, dims dbase + 32s + 8g .. +8: chunk g of K step s, stored at chunk g ^ x)
@@ -313,6 +325,7 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
     f32x4 sacc[kT];
 #pragma unroll
     for (int t = 0; t < kT; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (cm != 0ull) {
 #pragma unroll
     for (int s = 0; s < kS; ++s) {
 #pragma unroll
@@ -329,7 +342,9 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
 #pragma unroll
       for (int t = 0; t < kT; ++t) mine[64 * t] = sacc[t];
     }
+    }   // cm != 0
     __syncthreads();
+    if (cm == 0ull) continue;
 #pragma unroll
     for (int t = 0; t < kT; ++t) {
       f32x4 acc = sX[((pr * ND + 0) * kT + t) * 64 + lane];
@@ -415,6 +430,31 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
     }
   }
 
+  if constexpr (NH > 1) {
+    // the halves' states meet: thread t of half 1 holds the same heads and
+    // dims as thread t of half 0, over the other chunks of the split
+    __syncthreads();   // every chunk's LDS reads are done
+    float* po = reinterpret_cast<float*>(&sKh[0][0]);   // kM x 4 floats a thread
+    float* pml = reinterpret_cast<float*>(&sXh[0][0]);  // m and l a thread
+    static_assert(NT * kM * 4 * sizeof(float) <= sizeof(sKh) && 2 * NT * sizeof(float) <= sizeof(sXh),
+                  "the merge fits the chunk buffers");
+    if (hf == 1) {
+#pragma unroll
+      for (int m = 0; m < kM; ++m) *reinterpret_cast<f32x4*>(po + (m * NT + tidh) * 4) = oacc[m];
+      pml[tidh] = m_run;
+      pml[NT + tidh] = l_run;
+    }
+    __syncthreads();
+    if (hf == 1) return;   // no barrier follows
+    const float m1 = pml[tidh], l1 = pml[NT + tidh];
+    const float M = fmaxf(m_run, m1);
+    const float a0 = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - M);
+    const float a1 = m1 == -__builtin_inff() ? 0.f : exp2f(m1 - M);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) oacc[m] = oacc[m] * a0 + *reinterpret_cast<const f32x4*>(po + (m * NT + tidh) * 4) * a1;
+    m_run = M;
+  }
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot = l_tot + __shfl_xor(l_tot, 32, 64);
   if (a.splits == 1) {
@@ -441,12 +481,17 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
 // several workgroups per compute unit, worse for a grid that does not.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void sparse_attn_kernel_h32c32_2wg(
     AttnParams a) {
-  sparse_attn_body<2, 4, 32>(a);
+  sparse_attn_body<2, 4, 32, 1>(a);
 }
-__global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h32c32(AttnParams a) { sparse_attn_body<2, 4, 32>(a); }
-__global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h32c64(AttnParams a) { sparse_attn_body<2, 4, 64>(a); }
-__global__ __launch_bounds__(256) void sparse_attn_kernel_h16c32(AttnParams a) { sparse_attn_body<1, 4, 32>(a); }
-__global__ __launch_bounds__(256, 1) void sparse_attn_kernel_h16c64(AttnParams a) { sparse_attn_body<1, 4, 64>(a); }
+__global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h32c32(AttnParams a) { sparse_attn_body<2, 4, 32, 1>(a); }
+// One workgroup per CU over splits of several chunks: 16 waves, two halves on
+// alternate chunks.
+__global__ __launch_bounds__(1024, 1) void sparse_attn_kernel_h32c32_halves(AttnParams a) {
+  sparse_attn_body<2, 4, 32, 2>(a);
+}
+__global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h32c64(AttnParams a) { sparse_attn_body<2, 4, 64, 1>(a); }
+__global__ __launch_bounds__(256) void sparse_attn_kernel_h16c32(AttnParams a) { sparse_attn_body<1, 4, 32, 1>(a); }
+__global__ __launch_bounds__(256, 1) void sparse_attn_kernel_h16c64(AttnParams a) { sparse_attn_body<1, 4, 64, 1>(a); }
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // One workgroup per (row, head), V consecutive output dims per thread (512 / V
@@ -582,22 +627,29 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
     a.splits = 1;
     a.chunks_per_split = 0;
   }
-  a.part_o = nullptr;
-  a.part_ml = nullptr;
-  if (a.splits > 1) {
-    a.part_o = static_cast<float*>(L.workspace);
-    a.part_ml = a.part_o + (size_t)R * a.splits * L.H * 512;
-  }
   // Workgroups of 32 heads (8 waves); more heads split over blockIdx.z.  Four
   // waves of 128 dims per 16-head group keep every wave's chain of products
   // short and leave two waves per SIMD to overlap LDS and matrix-core work.
   if (L.H % 16 != 0 || L.H < 16) return hipErrorInvalidValue;
   const int NP = attn_group_heads(L.H) / 16;
   if (L.H % (16 * NP) != 0) return hipErrorInvalidValue;
+  const int64_t n_wg = (int64_t)a.splits * R * (L.H / (16 * NP));
+  const bool many = n_wg > 4 * kAttnTargetWorkgroups;
+  // a grid of one workgroup per CU whose splits hold several chunks runs
+  // 16-wave workgroups whose halves take alternate chunks (c4: 47 -> 41 us per
+  // layer); splits of one chunk keep the 8-wave kernel (more workgroups)
+  const bool halves = NP == 2 && ch == 32 && !many && a.chunks_per_split >= 2;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (a.splits > 1) {
+    a.part_o = static_cast<float*>(L.workspace);
+    a.part_ml = a.part_o + (size_t)R * a.splits * L.H * 512;
+  }
   dim3 grid((unsigned)a.splits, (unsigned)R, (unsigned)(L.H / (16 * NP)));
-  const bool many = (int64_t)grid.x * grid.y * grid.z > 4 * kAttnTargetWorkgroups;
   if (NP == 2 && ch == 32 && many)
     hipLaunchKernelGGL(sparse_attn_kernel_h32c32_2wg, grid, dim3(512), 0, stream, a);
+  else if (halves)
+    hipLaunchKernelGGL(sparse_attn_kernel_h32c32_halves, grid, dim3(1024), 0, stream, a);
   else if (NP == 2 && ch == 32)
     hipLaunchKernelGGL(sparse_attn_kernel_h32c32, grid, dim3(512), 0, stream, a);
   else if (NP == 2)
