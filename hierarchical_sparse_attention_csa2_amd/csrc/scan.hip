@@ -202,22 +202,24 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(7,
 // Pool scan: one wave scores 8 pool blocks (64 positions) with the decode scan's
 // lane layout (group u = pool blocks 2u and 2u + 1; lane 16g + c holds block g
 // of position c & 7 of pool block 2u + (c >> 3)); lane l's result is slot l of
-// the wave's 64 output slots.  Grid (ceil(n_pool / 8), M, B), one wave per
-// workgroup.
+// the wave's 64 output slots.  Grid (ceil(n_pool / 32), M, B), four waves (32
+// pool blocks of one row) per workgroup.
 constexpr int kPoolWaveBlocks = 8;
+constexpr int kPoolWaves = 4;
 
-__global__ __launch_bounds__(64) void pool_scan_kernel(
+__global__ __launch_bounds__(64 * kPoolWaves) void pool_scan_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     const int32_t* __restrict__ pool_blocks, int n_pool, const int32_t* __restrict__ n_visible, int M,
     int64_t N_max, float* __restrict__ pool_scores) {
   const int64_t seq = blockIdx.z;
   const int r = (int)seq * M + (int)blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
+  const int base = ((int)blockIdx.x * kPoolWaves + (int)(threadIdx.x >> 6)) * kPoolWaveBlocks;
+  if (base >= n_pool) return;   // no barriers: waves leave independently
   int64_t nv = n_visible[r];
   nv = nv < 0 ? 0 : (nv > N_max ? N_max : nv);
-  const int base = (int)blockIdx.x * kPoolWaveBlocks;
   const int32_t* pb = pool_blocks + (int64_t)r * n_pool;
   // pool block of group u for this lane's column: base + 2u + (c >> 3); loads at
   // clamped indices, all issued together; ids past the pool are -1
@@ -290,9 +292,10 @@ hipError_t launch_pool_scan(const uint8_t* q_codes, const uint8_t* q_scales, con
                             const int32_t* n_visible, int B, int M, int64_t N_max, float* pool_scores,
                             hipStream_t stream) {
   if (M > 65535 || B > 65535) return hipErrorInvalidConfiguration;
-  dim3 grid((unsigned)((n_pool + kPoolWaveBlocks - 1) / kPoolWaveBlocks), (unsigned)M, (unsigned)B);
-  hipLaunchKernelGGL(pool_scan_kernel, grid, dim3(64), 0, stream, q_codes, q_scales, k_codes, k_scales,
-                     pool_blocks, n_pool, n_visible, M, N_max, pool_scores);
+  constexpr int kPer = kPoolWaveBlocks * kPoolWaves;
+  dim3 grid((unsigned)((n_pool + kPer - 1) / kPer), (unsigned)M, (unsigned)B);
+  hipLaunchKernelGGL(pool_scan_kernel, grid, dim3(64 * kPoolWaves), 0, stream, q_codes, q_scales, k_codes,
+                     k_scales, pool_blocks, n_pool, n_visible, M, N_max, pool_scores);
   return hipGetLastError();
 }
 
