@@ -217,11 +217,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_scan_kernel(
     // exact sum gives.
     float bm[4];
     if (k0 + kPfTileKeys <= nv_min) {
+      // the halves meet in block pairs (0, 2) and (1, 3): one swap each leaves
+      // the low half blocks 0 and 1 and the high half blocks 2 and 3, the two
+      // it stages
+      float m4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float m = fmaximum(fmaximum(acc[4 * j], acc[4 * j + 1]), fmaximum(acc[4 * j + 2], acc[4 * j + 3]));
-        bm[j] = fmaximum_halves(m) + 0.0f;
-      }
+      for (int j = 0; j < 4; ++j)
+        m4[j] = fmaximum(fmaximum(acc[4 * j], acc[4 * j + 1]), fmaximum(acc[4 * j + 2], acc[4 * j + 3]));
+      const auto pa = __builtin_amdgcn_permlane32_swap(__float_as_uint(m4[0]), __float_as_uint(m4[2]), false, false);
+      const auto pb = __builtin_amdgcn_permlane32_swap(__float_as_uint(m4[1]), __float_as_uint(m4[3]), false, false);
+      const float b0 = fmaximum(__uint_as_float(pa[0]), __uint_as_float(pa[1])) + 0.0f;   // block 0 / block 2
+      const float b1 = fmaximum(__uint_as_float(pb[0]), __uint_as_float(pb[1])) + 0.0f;   // block 1 / block 3
+      st.bm[col][4 * ti + 2 * half] = b0;
+      st.bm[col][4 * ti + 2 * half + 1] = b1;
+      return;
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
