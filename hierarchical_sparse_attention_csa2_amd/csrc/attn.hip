@@ -89,22 +89,22 @@ __device__ __forceinline__ bf16x8_t decode_fp8x8(uint32_t w0, uint32_t w1) {
 }
 
 // Entry rows of a chunk: lane l of every wave resolves entry l % CH (its row
-// offset and validity), so a ballot gives the chunk's validity mask and any
-// wave can read an entry's row offset from that lane.
+// within the sequence and its validity), so a ballot gives the chunk's
+// validity mask and any wave can read an entry's row from that lane.
 struct EntryRow {
-  int64_t off;   // latent row seq*N_max + p, or window row seq*Tw + t
+  int32_t row;   // latent row p in [0, N_max), or window row t in [0, Tw); 0 when invalid
   bool valid;
 };
 
-__device__ __forceinline__ EntryRow entry_row(const AttnParams& a, int64_t seq, int ws0, int E, int e, int32_t p) {
+__device__ __forceinline__ EntryRow entry_row(const AttnParams& a, int ws0, int E, int e, int32_t p) {
   EntryRow x;
   if (e < a.k) {
     x.valid = p >= 0 && p < a.N_max;
-    x.off = seq * a.N_max + (x.valid ? p : 0);
+    x.row = x.valid ? p : 0;
   } else {
     const int64_t t = (int64_t)ws0 + (e - a.k);
     x.valid = e < E && t >= 0 && t < a.Tw;
-    x.off = seq * a.Tw + (x.valid ? t : 0);
+    x.row = x.valid ? (int32_t)t : 0;
   }
   return x;
 }
@@ -123,36 +123,87 @@ struct Gathered {
 // its byte length), read at the lane's 32-bit offset: the per-lane address
 // needs no 64-bit register pair, and a read past the row returns zero.
 constexpr int kBufferConfig = 0x00020000;   // gfx9 buffer descriptor word 3 for raw dword loads
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* row, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(row), 0, bytes, kBufferConfig);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* row, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(row), 0, (int)bytes, kBufferConfig);
+}
+
+// One sequence's latent codes, latent scales and window as buffer resources:
+// a row is then one scalar offset away (row * row bytes), which fits 32 bits
+// while the sequence has fewer than 2^24 latent rows.
+struct SeqRows {
+  __amdgpu_buffer_rsrc_t codes, scales, win;
+};
+constexpr int64_t kFastRows = 1 << 24;
+
+__device__ __forceinline__ SeqRows seq_rows(const AttnParams& a, int64_t seq) {
+  SeqRows s;
+  const bool fit = a.N_max < kFastRows;
+  s.codes = row_rsrc(a.c_codes + seq * a.N_max * 256, fit ? (uint32_t)(a.N_max * 256) : 0u);
+  s.scales = row_rsrc(a.c_scales + seq * a.N_max * 16, fit ? (uint32_t)(a.N_max * 16) : 0u);
+  s.win = row_rsrc(a.win + seq * a.Tw * 512, (uint32_t)(a.Tw * 512));
+  return s;
+}
+
+// Chunks whose entries are all valid and all latent (or all window) take one
+// branch per chunk; any other chunk (invalid entries, the latent / window
+// boundary, rows past 32-bit offsets) goes entry by entry.
+enum ChunkKind { kMixed = 0, kLatent = 1, kWindow = 2 };
+
+template <int CH>
+__device__ __forceinline__ int chunk_kind(const AttnParams& a, uint64_t mask, int ebase) {
+  constexpr uint64_t kChunkBits = CH == 64 ? ~0ull : ((1ull << CH) - 1ull);
+  if (mask != kChunkBits) return kMixed;
+  if (ebase + CH <= a.k) return a.N_max < kFastRows ? kLatent : kMixed;
+  return ebase >= a.k && a.Tw < (1 << 23) ? kWindow : kMixed;
 }
 
 template <int CH, int NT>
-__device__ __forceinline__ void gather_chunk(const AttnParams& a, int64_t off, uint64_t mask, int ebase, int w,
-                                             int lane, Gathered<CH, NT>& g) {
-  const int off_lo = (int)(uint32_t)off, off_hi = (int)(off >> 32);
+__device__ __forceinline__ void gather_chunk(const AttnParams& a, const SeqRows& sr, int64_t seq, int32_t row,
+                                             uint64_t mask, int ebase, int w, int lane, Gathered<CH, NT>& g) {
+  constexpr int kTPT = Gathered<CH, NT>::kTPT;
+  const int kind = chunk_kind<CH>(a, mask, ebase);
+  if (kind == kLatent) {
 #pragma unroll
-  for (int j = 0; j < Gathered<CH, NT>::kTPT; ++j) {
-    const int eg = w + j * (NT / 64);
+    for (int j = 0; j < kTPT; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * eg + i;
-      const int64_t o = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(off_hi, e) << 32) |
-                                  (uint32_t)__builtin_amdgcn_readlane(off_lo, e));
-      uint32_t x0 = 0u, x1 = 0u;
-      if ((mask >> e) & 1ull) {
-        if (ebase + e < a.k) {
-          x0 = __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(a.c_codes + o * 256, 256), 4 * lane, 0, 0);
-          x1 = __builtin_amdgcn_raw_buffer_load_b8(row_rsrc(a.c_scales + o * 16, 16), lane >> 2, 0, 0);
-        } else {
-          const u32x2_t wb = __builtin_amdgcn_raw_buffer_load_b64(row_rsrc(a.win + o * 512, 512), 8 * lane, 0, 0);
-          x0 = wb[0];
-          x1 = wb[1];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t re = (uint32_t)__builtin_amdgcn_readlane(row, 4 * (w + j * (NT / 64)) + i);
+        g.w0[j][i] = __builtin_amdgcn_raw_buffer_load_b32(sr.codes, 4 * lane, re << 8, 0);
+        g.w1[j][i] = __builtin_amdgcn_raw_buffer_load_b8(sr.scales, lane >> 2, re << 4, 0);
       }
-      g.w0[j][i] = x0;
-      g.w1[j][i] = x1;
-    }
+  } else if (kind == kWindow) {
+#pragma unroll
+    for (int j = 0; j < kTPT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t re = (uint32_t)__builtin_amdgcn_readlane(row, 4 * (w + j * (NT / 64)) + i);
+        const u32x2_t wb = __builtin_amdgcn_raw_buffer_load_b64(sr.win, 8 * lane, re << 9, 0);
+        g.w0[j][i] = wb[0];
+        g.w1[j][i] = wb[1];
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTPT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * (w + j * (NT / 64)) + i;
+        const uint32_t re = (uint32_t)__builtin_amdgcn_readlane(row, e);
+        uint32_t x0 = 0u, x1 = 0u;
+        if ((mask >> e) & 1ull) {
+          if (ebase + e < a.k) {
+            const int64_t o = seq * a.N_max + re;
+            x0 = __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(a.c_codes + o * 256, 256), 4 * lane, 0, 0);
+            x1 = __builtin_amdgcn_raw_buffer_load_b8(row_rsrc(a.c_scales + o * 16, 16), lane >> 2, 0, 0);
+          } else {
+            const int64_t o = seq * a.Tw + re;
+            const u32x2_t wb = __builtin_amdgcn_raw_buffer_load_b64(row_rsrc(a.win + o * 512, 512), 8 * lane, 0, 0);
+            x0 = wb[0];
+            x1 = wb[1];
+          }
+        }
+        g.w0[j][i] = x0;
+        g.w1[j][i] = x1;
+      }
   }
 }
 
@@ -161,18 +212,54 @@ __device__ __forceinline__ void gather_chunk(const AttnParams& a, int64_t off, u
 template <int CH, int NT>
 __device__ __forceinline__ void store_chunk(const AttnParams& a, const Gathered<CH, NT>& g, uint64_t mask,
                                             int ebase, int w, int lane, __bf16* sK) {
+  constexpr int kTPT = Gathered<CH, NT>::kTPT;
+  const int kind = chunk_kind<CH>(a, mask, ebase);
+  if (kind == kLatent) {
 #pragma unroll
-  for (int j = 0; j < Gathered<CH, NT>::kTPT; ++j) {
-    const int eg = w + j * (NT / 64);
+    for (int j = 0; j < kTPT; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * eg + i;
-      bf16x8_t v = zero_bf16x8();
-      if ((mask >> e) & 1ull)
-        v = ebase + e < a.k ? decode_latent8(g.w0[j][i], g.w1[j][i]) : decode_fp8x8(g.w0[j][i], g.w1[j][i]);
-      *reinterpret_cast<bf16x8_t*>(&sK[kofs(e, 8 * lane, (e >> 2) & 1)]) = v;
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * (w + j * (NT / 64)) + i;
+        *reinterpret_cast<bf16x8_t*>(&sK[kofs(e, 8 * lane, (e >> 2) & 1)]) = decode_latent8(g.w0[j][i], g.w1[j][i]);
+      }
+  } else if (kind == kWindow) {
+#pragma unroll
+    for (int j = 0; j < kTPT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * (w + j * (NT / 64)) + i;
+        *reinterpret_cast<bf16x8_t*>(&sK[kofs(e, 8 * lane, (e >> 2) & 1)]) = decode_fp8x8(g.w0[j][i], g.w1[j][i]);
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTPT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * (w + j * (NT / 64)) + i;
+        bf16x8_t v = zero_bf16x8();
+        if ((mask >> e) & 1ull)
+          v = ebase + e < a.k ? decode_latent8(g.w0[j][i], g.w1[j][i]) : decode_fp8x8(g.w0[j][i], g.w1[j][i]);
+        *reinterpret_cast<bf16x8_t*>(&sK[kofs(e, 8 * lane, (e >> 2) & 1)]) = v;
+      }
   }
+}
+
+// Two floats rounded to bf16 (round to nearest even), packed low to high.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2v));
+}
+
+// max of x over lanes l and l ^ 16 (kHalf: l ^ 32).  v_permlane16_swap
+// exchanges the odd 16-lane rows of one register with the even rows of the
+// other (v_permlane32_swap: the upper 32 lanes with the lower), so with both
+// operands x every lane receives both values of its pair.
+template <bool kHalf>
+__device__ __forceinline__ float max_lanes(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto p = kHalf ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                       : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
 // Four bf16 of a transposed 16x4 tile: in each 16-lane group, lane i receives
@@ -227,6 +314,7 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   wl = wl < 0 ? 0 : (wl > a.win_max ? a.win_max : wl);
   const int E = a.k + wl;
   const int ws0 = a.win_max > 0 ? a.win_start[r] : 0;
+  const SeqRows sr = seq_rows(a, seq);
 
   const int c_begin = split * a.chunks_per_split;
   int c_end = c_begin + a.chunks_per_split;
@@ -259,9 +347,9 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     if (c_first < c_end) {
-      const EntryRow x = entry_row(a, seq, ws0, E, e0, p0);
+      const EntryRow x = entry_row(a, ws0, E, e0, p0);
       mask = __ballot(x.valid) & kChunkBits;
-      gather_chunk<CH, NT>(a, x.off, mask, c_first * kChunk, w, lane, gr);
+      gather_chunk<CH, NT>(a, sr, seq, x.row, mask, c_first * kChunk, w, lane, gr);
     }
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
@@ -314,9 +402,9 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
       if (t >= n_staged && e < a.k) p = a.idx[(int64_t)r * a.k + e];
       const int32_t ps = t < n_staged ? sIdx[t < kIdxCap ? t : 0] : -1;
       p = t < n_staged ? ps : p;
-      const EntryRow x = entry_row(a, seq, ws0, E, e, p);
+      const EntryRow x = entry_row(a, ws0, E, e, p);
       mask = __ballot(x.valid) & kChunkBits;
-      gather_chunk<CH, NT>(a, x.off, mask, cn * kChunk, w, lane, gr);
+      gather_chunk<CH, NT>(a, sr, seq, x.row, mask, cn * kChunk, w, lane, gr);
     }
 
     // 3. partial S^T[CH entries x 16 heads] over this wave's kDims dims
@@ -359,19 +447,20 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
     // probabilities stay below 2^kLazyRescale, and l and the partials carry
     // the same m_run, so the result is the same softmax.
     if (cm != kChunkBits) {
+      const uint64_t mine = cm >> (4 * g);   // bit 16t + i: entry 16t + 4g + i
 #pragma unroll
       for (int t = 0; t < kT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (!((cm >> (16 * t + 4 * g + i)) & 1ull)) sacc[t][i] = -__builtin_inff();
+          if (!((mine >> (16 * t + i)) & 1ull)) sacc[t][i] = -__builtin_inff();
     }
     float mloc = -__builtin_inff();
 #pragma unroll
     for (int t = 0; t < kT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sacc[t][i]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    mloc = max_lanes<false>(mloc);   // lanes l ^ 16
+    mloc = max_lanes<true>(mloc);    // lanes l ^ 32
     if (__ballot(mloc > m_run + kLazyRescale) != 0ull) {
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = exp2f(m_run - m_new);
@@ -401,14 +490,18 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
     // probabilities it holds.
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      bf16x8_t bhi, blo;
+      // hi = bf16(p) two at a time, lo = bf16(p - hi)
+      u32x4_t bh, bl;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = i < 4 ? sacc[2 * j][i] : sacc[2 * j + 1][i - 4];
-        const __bf16 hi = (__bf16)p;
-        bhi[i] = hi;
-        blo[i] = (__bf16)(p - (float)hi);
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = i < 2 ? sacc[2 * j][2 * i] : sacc[2 * j + 1][2 * i - 4];
+        const float p1 = i < 2 ? sacc[2 * j][2 * i + 1] : sacc[2 * j + 1][2 * i - 3];
+        const uint32_t h = pack_bf16(p0, p1);
+        bh[i] = h;
+        bl[i] = pack_bf16(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xffff0000u));
       }
+      const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, bh);
+      const bf16x8_t blo = __builtin_bit_cast(bf16x8_t, bl);
       // rows e0 and e0 + 16 (both with (e >> 2) & 1 = g & 1), dims dbase + 16m +
       // 4 (hl & 3) .. +4: chunk 2m + ((hl & 3) >> 1), stored at that chunk ^ (g & 1)
       const int e0 = 32 * j + 4 * g + (hl >> 2);
