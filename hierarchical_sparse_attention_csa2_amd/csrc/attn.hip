@@ -71,7 +71,8 @@ __device__ __forceinline__ bf16x8_t zero_bf16x8() {
 }
 
 __device__ __forceinline__ bf16x8_t decode_latent8(uint32_t wcode, uint32_t scale_byte) {
-  const float sc = e8m0_to_f32(scale_byte);
+  // 2^(e-127): e << 23 for e >= 1, the subnormal 2^-127 = 0x00400000 for e = 0
+  const float sc = __uint_as_float(max(scale_byte << 23, 0x00400000u));
   const bf16x2_t p0 = fp4x2_to_bf16<0>(wcode, sc);
   const bf16x2_t p1 = fp4x2_to_bf16<1>(wcode, sc);
   const bf16x2_t p2 = fp4x2_to_bf16<2>(wcode, sc);
@@ -159,9 +160,9 @@ __device__ __forceinline__ int chunk_kind(const AttnParams& a, uint64_t mask, in
 
 template <int CH, int NT>
 __device__ __forceinline__ void gather_chunk(const AttnParams& a, const SeqRows& sr, int64_t seq, int32_t row,
-                                             uint64_t mask, int ebase, int w, int lane, Gathered<CH, NT>& g) {
+                                             uint64_t mask, int kind, int ebase, int w, int lane,
+                                             Gathered<CH, NT>& g) {
   constexpr int kTPT = Gathered<CH, NT>::kTPT;
-  const int kind = chunk_kind<CH>(a, mask, ebase);
   if (kind == kLatent) {
 #pragma unroll
     for (int j = 0; j < kTPT; ++j)
@@ -210,10 +211,9 @@ __device__ __forceinline__ void gather_chunk(const AttnParams& a, const SeqRows&
 // Decode the gathered bytes (zeros for invalid entries) into the row-major
 // LDS copy: lane l writes dims 8l .. 8l+7 of each of its entries.
 template <int CH, int NT>
-__device__ __forceinline__ void store_chunk(const AttnParams& a, const Gathered<CH, NT>& g, uint64_t mask,
+__device__ __forceinline__ void store_chunk(const AttnParams& a, const Gathered<CH, NT>& g, uint64_t mask, int kind,
                                             int ebase, int w, int lane, __bf16* sK) {
   constexpr int kTPT = Gathered<CH, NT>::kTPT;
-  const int kind = chunk_kind<CH>(a, mask, ebase);
   if (kind == kLatent) {
 #pragma unroll
     for (int j = 0; j < kTPT; ++j)
@@ -290,7 +290,7 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   static_assert(NH == 1 || NH == 2, "one or two halves");
   __shared__ __attribute__((aligned(16))) __bf16 sKh[NH][kChunk * kKLd];
   __shared__ f32x4 sXh[NH][NP * ND * 64 * kT];   // partial S^T tiles of the ND waves of each head group
-  __shared__ int32_t sIdx[kIdxCap];              // the split's selected indices after each half's first chunk
+  __shared__ int32_t sIdx[kIdxCap];              // rows of the split's entries after each half's first chunk
 
   const int split = blockIdx.x;
   const int r = blockIdx.y;
@@ -326,15 +326,20 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   const int c_first = c_begin + hf;
 
   // Each half's first chunk's indices load first and its rows are gathered as
-  // soon as they arrive; later chunks' indices are staged in LDS (visible after
-  // the first round's decode barrier), so no chunk waits on a global index load
-  // in the loop.  The query loads after the first gathers.
+  // soon as they arrive; the rows of the split's later chunks (-1 for an
+  // invalid entry) are resolved once into LDS (visible after the first round's
+  // decode barrier), so no chunk waits on a global index load or re-checks its
+  // entries in the loop.  The query loads after the first gathers.
   Gathered<CH, NT> gr;
   uint64_t mask = 0ull;   // validity of the gathered chunk's entries (uniform)
-  const int staged0 = (c_begin + NH) * kChunk;                        // first staged entry
-  int n_staged = (c_end - c_begin - NH) * kChunk;
-  n_staged = n_staged < a.k - staged0 ? n_staged : a.k - staged0;     // latent entries only
-  n_staged = n_staged < kIdxCap ? n_staged : kIdxCap;                 // (a longer split loads the rest)
+  int kind = kMixed;      // and its kind
+  const int staged_c0 = c_begin + NH;                                 // first staged chunk
+  int n_staged_ch = c_end - staged_c0;
+  const int e_chunks = (E + kChunk - 1) / kChunk;                     // chunks holding entries
+  n_staged_ch = n_staged_ch < e_chunks - staged_c0 ? n_staged_ch : e_chunks - staged_c0;
+  n_staged_ch = n_staged_ch < kIdxCap / kChunk ? n_staged_ch : kIdxCap / kChunk;   // (a longer split loads the rest)
+  n_staged_ch = n_staged_ch > 0 ? n_staged_ch : 0;
+  const int n_staged = n_staged_ch * kChunk;
   {
     constexpr int kStage = (kIdxCap + NH * NT - 1) / (NH * NT);
     const int e0 = c_first * kChunk + le;
@@ -342,19 +347,23 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
     int32_t st[kStage];
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
-      const int t = tid + j * NH * NT;
-      st[j] = t < n_staged ? a.idx[(int64_t)r * a.k + staged0 + t] : -1;
+      const int e = staged_c0 * kChunk + tid + j * NH * NT;
+      st[j] = tid + j * NH * NT < n_staged && e < a.k ? a.idx[(int64_t)r * a.k + e] : -1;
     }
     __builtin_amdgcn_sched_barrier(0);
     if (c_first < c_end) {
       const EntryRow x = entry_row(a, ws0, E, e0, p0);
       mask = __ballot(x.valid) & kChunkBits;
-      gather_chunk<CH, NT>(a, sr, seq, x.row, mask, c_first * kChunk, w, lane, gr);
+      kind = chunk_kind<CH>(a, mask, c_first * kChunk);
+      gather_chunk<CH, NT>(a, sr, seq, x.row, mask, kind, c_first * kChunk, w, lane, gr);
     }
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
       const int t = tid + j * NH * NT;
-      if (t < n_staged) sIdx[t] = st[j];
+      if (t < n_staged) {
+        const EntryRow x = entry_row(a, ws0, E, staged_c0 * kChunk + t, st[j]);
+        sIdx[t] = x.valid ? x.row : -1;
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -389,22 +398,26 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
     const int c = c_first + NH * it;
     const int ebase = c * kChunk;
     const uint64_t cm = mask;   // this chunk's validity
+    const int ck = kind;
     __syncthreads();   // the previous round's LDS reads are done
-    if (cm != 0ull) store_chunk<CH, NT>(a, gr, cm, ebase, w, lane, sK);
+    if (cm != 0ull) store_chunk<CH, NT>(a, gr, cm, ck, ebase, w, lane, sK);
     __syncthreads();   // decoded rows (and, in the first round, the staged indices) visible
     // this half's next chunk's rows: in flight during this chunk's products
     mask = 0ull;
+    kind = kMixed;
     const int cn = c + NH;
     if (cn < c_end && cn * kChunk < E) {
-      const int e = cn * kChunk + le;
-      const int t = e - staged0;
-      int32_t p = -1;
-      if (t >= n_staged && e < a.k) p = a.idx[(int64_t)r * a.k + e];
-      const int32_t ps = t < n_staged ? sIdx[t < kIdxCap ? t : 0] : -1;
-      p = t < n_staged ? ps : p;
-      const EntryRow x = entry_row(a, ws0, E, e, p);
-      mask = __ballot(x.valid) & kChunkBits;
-      gather_chunk<CH, NT>(a, sr, seq, x.row, mask, cn * kChunk, w, lane, gr);
+      int32_t row;
+      if (cn - staged_c0 < n_staged_ch) {
+        row = sIdx[(cn - staged_c0) * kChunk + le];
+      } else {
+        const int e = cn * kChunk + le;
+        const EntryRow x = entry_row(a, ws0, E, e, e < a.k ? a.idx[(int64_t)r * a.k + e] : -1);
+        row = x.valid ? x.row : -1;
+      }
+      mask = __ballot(row >= 0) & kChunkBits;
+      kind = chunk_kind<CH>(a, mask, cn * kChunk);
+      gather_chunk<CH, NT>(a, sr, seq, row, mask, kind, cn * kChunk, w, lane, gr);
     }
 
     // 3. partial S^T[CH entries x 16 heads] over this wave's kDims dims

@@ -362,6 +362,7 @@ def test_sparse_attn_vs_oracle(H, k, win_lens):
     (2, 64, 1500, 64),    # one split per row, over 1,024 later-chunk indices (the rest load directly)
     (4, 130, 200, 64),    # more than 1,024 workgroups (two per compute unit), a chunk mixing both row kinds
     (1, 700, 96, 32),     # 700 workgroups of 32 heads
+    (1, 1100, 1100, 32),  # more than 1,024 workgroups, over 1,024 later-chunk indices
 ])
 def test_sparse_attn_many_rows_long_rows(B, M, k, H):
     w = Workload("attnR", 1000 + B * M + k, B=B, M=M, N=2500, H=H, k=k)
