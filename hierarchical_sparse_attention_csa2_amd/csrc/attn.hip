@@ -595,6 +595,9 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h32c32(AttnParams a
 __global__ __launch_bounds__(1024, 1) void sparse_attn_kernel_h32c32_halves(AttnParams a) {
   sparse_attn_body<2, 4, 32, 2>(a);
 }
+__global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h16c32_halves(AttnParams a) {
+  sparse_attn_body<1, 4, 32, 2>(a);
+}
 __global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h32c64(AttnParams a) { sparse_attn_body<2, 4, 64, 1>(a); }
 __global__ __launch_bounds__(256) void sparse_attn_kernel_h16c32(AttnParams a) { sparse_attn_body<1, 4, 32, 1>(a); }
 __global__ __launch_bounds__(256, 1) void sparse_attn_kernel_h16c64(AttnParams a) { sparse_attn_body<1, 4, 64, 1>(a); }
@@ -675,7 +678,13 @@ __global__ __launch_bounds__(512 / V) void attn_combine_kernel(const float* __re
 }
 
 // Head groups of 16 heads per workgroup (32 when H allows).
-static int attn_group_heads(int H) { return H >= 32 ? 32 : 16; }
+// (16 when groups of 16 heads alone give every compute unit a workgroup with
+// one split per row: two halves then share the row's chunks and no combine runs)
+static int attn_group_heads(int R, int H) {
+  if (H < 32) return 16;
+  const int64_t g16 = (int64_t)R * (H / 16), g32 = (int64_t)R * (H / 32);
+  return H % 16 == 0 && g16 >= kAttnTargetWorkgroups && g32 < kAttnTargetWorkgroups ? 16 : 32;
+}
 
 // Entries per chunk: 32 keeps a workgroup's LDS at 54 KB, so two workgroups
 // share a compute unit and one's loads overlap the other's products.
@@ -693,7 +702,8 @@ int attn_splits(int R, int H, int k_plus_win) {
   const int ch = attn_chunk(R, H, k_plus_win);
   const int n_chunks = (k_plus_win + ch - 1) / ch;
   if (n_chunks <= 1) return 1;
-  const int64_t groups = (int64_t)R * (H > 0 ? (H + attn_group_heads(H) - 1) / attn_group_heads(H) : 1);
+  const int gh = attn_group_heads(R, H);
+  const int64_t groups = (int64_t)R * (H > 0 ? (H + gh - 1) / gh : 1);
   int64_t want = (kAttnTargetWorkgroups + groups - 1) / groups;
   if (want < 1) want = 1;
   if (want > n_chunks) want = n_chunks;
@@ -737,14 +747,14 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
   // waves of 128 dims per 16-head group keep every wave's chain of products
   // short and leave two waves per SIMD to overlap LDS and matrix-core work.
   if (L.H % 16 != 0 || L.H < 16) return hipErrorInvalidValue;
-  const int NP = attn_group_heads(L.H) / 16;
+  const int NP = attn_group_heads(R, L.H) / 16;
   if (L.H % (16 * NP) != 0) return hipErrorInvalidValue;
   const int64_t n_wg = (int64_t)a.splits * R * (L.H / (16 * NP));
   const bool many = n_wg > 4 * kAttnTargetWorkgroups;
   // a grid of one workgroup per CU whose splits hold several chunks runs
   // 16-wave workgroups whose halves take alternate chunks (c4: 47 -> 41 us per
   // layer); splits of one chunk keep the 8-wave kernel (more workgroups)
-  const bool halves = NP == 2 && ch == 32 && !many && a.chunks_per_split >= 2;
+  const bool halves = ch == 32 && !many && a.chunks_per_split >= 2;
   a.part_o = nullptr;
   a.part_ml = nullptr;
   if (a.splits > 1) {
@@ -754,8 +764,10 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
   dim3 grid((unsigned)a.splits, (unsigned)R, (unsigned)(L.H / (16 * NP)));
   if (NP == 2 && ch == 32 && many)
     hipLaunchKernelGGL(sparse_attn_kernel_h32c32_2wg, grid, dim3(512), 0, stream, a);
-  else if (halves)
+  else if (halves && NP == 2)
     hipLaunchKernelGGL(sparse_attn_kernel_h32c32_halves, grid, dim3(1024), 0, stream, a);
+  else if (halves)
+    hipLaunchKernelGGL(sparse_attn_kernel_h16c32_halves, grid, dim3(512), 0, stream, a);
   else if (NP == 2 && ch == 32)
     hipLaunchKernelGGL(sparse_attn_kernel_h32c32, grid, dim3(512), 0, stream, a);
   else if (NP == 2)

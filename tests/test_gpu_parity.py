@@ -207,6 +207,8 @@ def test_index_full_short_rows_reuse_one_workspace():
     (70000, 33, 2048, 1000, "random"),   # the wide top-k
     (300, 20, 8, 0, "causal"),           # k = 0: the pool alone
     (140000, 16, 2048, 512, "causal"),   # more than 16,384 blocks a row
+    (140000, 130, 2048, 512, "causal"),  # and 260 rows: the one-wave-per-row block filter
+    (200000, 128, 1000, 300, "random"),  # the same with a smaller pool and k, rows of 0 .. N visible
 ])
 def test_index_full_prefill(kind, N, M, n_pool, k, nv):
     """Many queries per sequence through csa2_index_full: pool and top-k
