@@ -185,6 +185,10 @@ int index_full_run(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
                           kb, k > 0 ? topk_blocks : nullptr, smax, nsup, s, nullptr, key_floor);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   if (k == 0) return CSA2_OK;
+  // rescoring and top-k in one kernel where it covers the shape
+  e = csa2::launch_pool_topk(q_codes, q_scales, k_codes, k_scales, topk_blocks, kb, n_visible, B, M, N_max,
+                             kb == k ? key_floor : nullptr, k, idx, s);
+  if (e != hipErrorNotSupported) return hip_status(e);
   e = csa2::launch_pool_scan(q_codes, q_scales, k_codes, k_scales, topk_blocks, kb, n_visible, B, M, N_max,
                              topk_scores, s);
   if (e != hipSuccess) return CSA2_ERR_HIP;

@@ -21,6 +21,13 @@ hipError_t launch_pool_scan(const uint8_t* q_codes, const uint8_t* q_scales, con
                             const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool,
                             const int32_t* n_visible, int B, int M, int64_t N_max, float* pool_scores,
                             hipStream_t stream);
+// Pool rescoring and top-k in one workgroup per row: pool_blocks [B*M][n_pool]
+// (ids ascending, -1 padded), idx [B*M][k]; hipErrorNotSupported when
+// 8 * n_pool > 16384 or k <= 0 (nothing launched).
+hipError_t launch_pool_topk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                            const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool,
+                            const int32_t* n_visible, int B, int M, int64_t N_max, const uint32_t* floor_in, int k,
+                            int32_t* idx, hipStream_t stream);
 
 // Ranked selection.  layout 0: block maxima (row length ceil(n_visible/8),
 // stride `stride`); 1: pool slots (8*n_pool per row, positions through

@@ -34,6 +34,7 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "select_core.h"
+#include "score_core.h"
 
 namespace csa2 {
 
@@ -959,6 +960,140 @@ __global__ __launch_bounds__(kSelThreads) void select_mem_kernel(int layout, con
   }
   reduce_stats(sh, st);
   select_targets<kSrcMem, kIdRow, false, false>(sh, row, row.n, k1, o1, k2, o2);
+}
+
+// ---------------------------------------------------------------------------
+// Pool rescoring and top-k in one workgroup per row (many queries per
+// sequence).  In round j wave w scores the row's pool blocks [8 (w Jp + j), +8)
+// with the pool scan's lane layout (lane 16g + c holds block g of position
+// c & 7 of pool block 2u + (c >> 3) in group u), so lane l's score is item
+// (w, j, l) of the register-resident selection: slot order is position order
+// (the pool blocks are listed by id).  Keys, validity and floor as
+// pool_scan_kernel followed by select_reg_kernel<J, kSelPool>, with no round
+// trip of the scores through memory.
+// ---------------------------------------------------------------------------
+template <int J>
+__device__ __forceinline__ void pool_topk_row(RegShared& sh, int r, const uint8_t* __restrict__ q_codes,
+                                              const uint8_t* __restrict__ q_scales,
+                                              const uint8_t* __restrict__ k_codes,
+                                              const uint8_t* __restrict__ k_scales,
+                                              const int32_t* __restrict__ pool_blocks, int n_pool,
+                                              const int32_t* __restrict__ n_visible, int M, int64_t N_max,
+                                              const uint32_t* __restrict__ floor_in, int k,
+                                              int32_t* __restrict__ idx) {
+  const int64_t seq = r / M;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int cap = 8 * n_pool;
+  const int Jp = (cap + 1023) >> 10;
+  const int32_t* pb = pool_blocks + (int64_t)r * n_pool;
+  int64_t nv_sel = n_visible[r];
+  nv_sel = nv_sel < 0 ? 0 : nv_sel;                          // the selection's bound
+  const int64_t nv = nv_sel > N_max ? N_max : nv_sel;        // the scan's bound
+  const uint8_t* kc = k_codes + seq * N_max * 64;
+  const uint8_t* ks = k_scales + seq * N_max * 4;
+  half2_t qh[16];
+  load_query_block(q_codes + (int64_t)r * 64 + 16 * g, qh);
+  const int eq = q_scales[(int64_t)r * 4 + g];
+  const uint32_t fl = floor_in ? floor_in[r] : 1u;
+  uint32_t key[J];
+  int32_t pbv[J];   // pool block of this lane's item in round j
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    key[j] = 0u;
+    pbv[j] = -1;
+    const int base = (w * Jp + j) * 8;
+    if (j < Jp && base < n_pool) {   // uniform over the wave
+      int32_t blk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + 2 * u + (c >> 3);
+        const int32_t v = pb[i < n_pool ? i : n_pool - 1];
+        blk[u] = i < n_pool ? v : -1;
+      }
+      u32x4_t kb[4];
+      uint32_t ek[4];
+      bool ok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int32_t b = blk[u];
+        int64_t p = 8 * (int64_t)b + (c & 7);
+        ok[u] = b >= 0 && p < nv;
+        p = ok[u] ? p : 0;   // masked lanes read position 0 (in bounds)
+        kb[u] = load_codes16(kc + p * 64 + 16 * g);
+        ek[u] = ks[p * 4 + g];
+      }
+      const float sc = score_groups_valu(qh, eq, kb, ek);
+      // this lane's item: pool block base + 2g + (c >> 3) (group u = g), position c & 7
+      const bool mine_ok = (g & 2) ? ((g & 1) ? ok[3] : ok[2]) : ((g & 1) ? ok[1] : ok[0]);
+      const int32_t bm = (g & 2) ? ((g & 1) ? blk[3] : blk[2]) : ((g & 1) ? blk[1] : blk[0]);
+      const int i = base * 8 + lane;
+      if (i < cap) {
+        pbv[j] = bm;
+        const uint32_t kk = order_key(mine_ok ? sc : -__builtin_inff());
+        const bool okk = bm >= 0 && 8 * (int64_t)bm + (c & 7) < nv_sel;
+        key[j] = okk && kk >= fl ? kk : 0u;
+      }
+    }
+  }
+  hist_zero(sh.c);
+  if (threadIdx.x == 0) {
+    sh.s.cnt[0] = 0;
+    sh.s.cnt[1] = 0;
+  }
+  int valid;
+  uint32_t kmin, kmax;
+  key_range(sh.s, key, Jp, valid, kmin, kmax);
+  Thr th0, th1;
+  select_thresholds(sh.c, sh.s, key, Jp, valid, kmin, kmax, k, 0, 0, th0, th1);
+  int32_t* out = idx + (int64_t)r * k;
+  emit_sel(
+      sh.s, key, Jp, th0, th1, [&](int, int pos, int j, int i) { out[pos] = 8 * pbv[j] + (i & 7); },
+      [&](int, int p) { out[p] = -1; });
+}
+
+#define CSA2_POOL_TOPK_ARGS                                                                                     \
+  const uint8_t *__restrict__ q_codes, const uint8_t *__restrict__ q_scales, const uint8_t *__restrict__ k_codes, \
+      const uint8_t *__restrict__ k_scales, const int32_t *__restrict__ pool_blocks, int n_pool,                 \
+      const int32_t *__restrict__ n_visible, int M, int64_t N_max, const uint32_t *__restrict__ floor_in, int k,  \
+      int32_t *__restrict__ idx
+// pools of up to 512 blocks: two workgroups a compute unit (64 registers)
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void pool_topk_kernel4(
+    CSA2_POOL_TOPK_ARGS) {
+  __shared__ RegShared sh;
+  pool_topk_row<4>(sh, blockIdx.x, q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, M, N_max,
+                   floor_in, k, idx);
+}
+template <int J>
+__global__ __launch_bounds__(kSelThreads) void pool_topk_kernel(CSA2_POOL_TOPK_ARGS) {
+  __shared__ RegShared sh;
+  pool_topk_row<J>(sh, blockIdx.x, q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, M, N_max,
+                   floor_in, k, idx);
+}
+#undef CSA2_POOL_TOPK_ARGS
+
+hipError_t launch_pool_topk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                            const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool,
+                            const int32_t* n_visible, int B, int M, int64_t N_max, const uint32_t* floor_in, int k,
+                            int32_t* idx, hipStream_t stream) {
+  const int64_t R = (int64_t)B * M;
+  if (k <= 0 || n_pool <= 0 || R <= 0 || R > 0x7FFFFFFF) return hipErrorNotSupported;
+  const int cap = 8 * n_pool;
+  const dim3 grid((unsigned)R), block(kSelThreads);
+#define CSA2_PT(J)                                                                                                   \
+  hipLaunchKernelGGL((pool_topk_kernel<J>), grid, block, 0, stream, q_codes, q_scales, k_codes, k_scales, pool_blocks, \
+                     n_pool, n_visible, M, N_max, floor_in, k, idx)
+  if (cap <= 4096)
+    hipLaunchKernelGGL(pool_topk_kernel4, grid, block, 0, stream, q_codes, q_scales, k_codes, k_scales, pool_blocks,
+                       n_pool, n_visible, M, N_max, floor_in, k, idx);
+  else if (cap <= 8192)
+    CSA2_PT(8);
+  else if (cap <= 16384)
+    CSA2_PT(16);
+  else
+    return hipErrorNotSupported;
+#undef CSA2_PT
+  return hipGetLastError();
 }
 
 hipError_t launch_select(int layout, const float* scores, int64_t stride, const int32_t* pool_blocks,

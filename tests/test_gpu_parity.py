@@ -205,6 +205,7 @@ def test_index_full_short_rows_reuse_one_workspace():
     (40000, 130, 2048, 512, "causal"),   # pool below the block count; two query groups and a tail
     (20000, 16, 64, 512, "random"),      # pool below k (kb = 64); rows of 0 .. N visible entries
     (70000, 33, 2048, 1000, "random"),   # the wide top-k
+    (30000, 20, 2048, 1500, "causal"),   # a top-k over more than 8,192 pool positions
     (300, 20, 8, 0, "causal"),           # k = 0: the pool alone
     (140000, 16, 2048, 512, "causal"),   # more than 16,384 blocks a row
     (140000, 130, 2048, 512, "causal"),  # and 260 rows: the one-wave-per-row block filter
