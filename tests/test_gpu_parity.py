@@ -123,6 +123,14 @@ def test_index_full_bitexact(kind, N, n_pool, k, nv):
     torch.cuda.synchronize()
     assert np.array_equal(pool.cpu().numpy(), ref["pool_blocks"])
     assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    # with the scores asked for (written to the caller's rows instead of the
+    # workspace): the same pool and top-k
+    scores = torch.empty((w.R, N), dtype=torch.float32, device="cuda")
+    pool3, idx3 = torch.empty_like(pool), torch.empty_like(idx)
+    csa2.csa2_index_full(l["q_codes"], l["q_scales"], c["k_codes"], c["k_scales"], l["n_visible"], w.B, 1, N,
+                         n_pool, k, pool3, idx3, scores=scores)
+    torch.cuda.synchronize()
+    assert torch.equal(pool3, pool) and torch.equal(idx3, idx)
     # staged calls (scan, block select, pool scan, top-k as separate entry points)
     st = pipeline.Step(("full",), w.B, 1, N, H=64, n_pool=n_pool, k=k, staged=True)
     st.full_index(pipeline.cache_from(c), pipeline.layer_from(l), st.idx[0])
