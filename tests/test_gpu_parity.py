@@ -72,7 +72,7 @@ def _same_f32(a, b):
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed", "overflow"])
 @pytest.mark.parametrize("B,M,N", [(1, 40, 3000), (2, 33, 2100), (1, 130, 5000), (3, 5, 2500), (2, 15, 700),
-                                   (2, 16, 1900)])
+                                   (2, 16, 1900), (1, 2, 1800), (2, 8, 1300)])
 def test_prefill_scan_bitexact(kind, B, M, N):
     """Several queries per sequence: scores, block maxima and super-block maxima
     bit-exact for ragged visibility, partial query groups, several key chunks,
