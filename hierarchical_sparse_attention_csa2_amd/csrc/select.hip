@@ -973,7 +973,7 @@ __global__ __launch_bounds__(kSelThreads) void select_mem_kernel(int layout, con
 // trip of the scores through memory.
 // ---------------------------------------------------------------------------
 template <int J>
-__device__ __forceinline__ void pool_topk_row(RegShared& sh, int r, const uint8_t* __restrict__ q_codes,
+__device__ __forceinline__ void pool_topk_row(RegShared& sh, int32_t* sblk, int r, const uint8_t* __restrict__ q_codes,
                                               const uint8_t* __restrict__ q_scales,
                                               const uint8_t* __restrict__ k_codes,
                                               const uint8_t* __restrict__ k_scales,
@@ -986,7 +986,9 @@ __device__ __forceinline__ void pool_topk_row(RegShared& sh, int r, const uint8_
   const int c = lane & 15, g = lane >> 4;
   const int cap = 8 * n_pool;
   const int Jp = (cap + 1023) >> 10;
+  // the row's pool block ids, staged in LDS with one coalesced pass
   const int32_t* pb = pool_blocks + (int64_t)r * n_pool;
+  for (int t = threadIdx.x; t < n_pool; t += kSelThreads) sblk[t] = pb[t];
   int64_t nv_sel = n_visible[r];
   nv_sel = nv_sel < 0 ? 0 : nv_sel;                          // the selection's bound
   const int64_t nv = nv_sel > N_max ? N_max : nv_sel;        // the scan's bound
@@ -996,6 +998,7 @@ __device__ __forceinline__ void pool_topk_row(RegShared& sh, int r, const uint8_
   load_query_block(q_codes + (int64_t)r * 64 + 16 * g, qh);
   const int eq = q_scales[(int64_t)r * 4 + g];
   const uint32_t fl = floor_in ? floor_in[r] : 1u;
+  __syncthreads();   // the staged ids visible
   uint32_t key[J];
   int32_t pbv[J];   // pool block of this lane's item in round j
 #pragma unroll
@@ -1008,7 +1011,7 @@ __device__ __forceinline__ void pool_topk_row(RegShared& sh, int r, const uint8_
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = base + 2 * u + (c >> 3);
-        const int32_t v = pb[i < n_pool ? i : n_pool - 1];
+        const int32_t v = sblk[i < n_pool ? i : n_pool - 1];
         blk[u] = i < n_pool ? v : -1;
       }
       u32x4_t kb[4];
@@ -1061,13 +1064,15 @@ __device__ __forceinline__ void pool_topk_row(RegShared& sh, int r, const uint8_
 __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void pool_topk_kernel4(
     CSA2_POOL_TOPK_ARGS) {
   __shared__ RegShared sh;
-  pool_topk_row<4>(sh, blockIdx.x, q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, M, N_max,
+  __shared__ int32_t sblk[512];
+  pool_topk_row<4>(sh, sblk, blockIdx.x, q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, M, N_max,
                    floor_in, k, idx);
 }
 template <int J>
 __global__ __launch_bounds__(kSelThreads) void pool_topk_kernel(CSA2_POOL_TOPK_ARGS) {
   __shared__ RegShared sh;
-  pool_topk_row<J>(sh, blockIdx.x, q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, M, N_max,
+  __shared__ int32_t sblk[128 * J];   // n_pool <= 1024 J / 8
+  pool_topk_row<J>(sh, sblk, blockIdx.x, q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, M, N_max,
                    floor_in, k, idx);
 }
 #undef CSA2_POOL_TOPK_ARGS
