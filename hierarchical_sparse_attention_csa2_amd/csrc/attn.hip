@@ -437,6 +437,14 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
         sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qlo[s], sacc[t], 0, 0, 0);
       }
     }
+    // one operand read ahead of each pair of products
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < kS * kT - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // the ND waves of a head group add their partial sums in part order
     {
       f32x4* mine = sX + (pr * ND + part) * kT * 64 + lane;
@@ -527,12 +535,15 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
         oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bhi, oacc[m], 0, 0, 0);
         oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, blo, oacc[m], 0, 0, 0);
       }
-      // two transposing reads ahead of each pair of products, no further
+      // the next dim tile's two transposing reads in flight during each pair of
+      // products
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int m = 0; m < kM; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int m = 0; m < kM - 1; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
   }
 
