@@ -253,13 +253,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // max of x over lanes l and l ^ 16 (kHalf: l ^ 32).  v_permlane16_swap
 // exchanges the odd 16-lane rows of one register with the even rows of the
 // other (v_permlane32_swap: the upper 32 lanes with the lower), so with both
-// operands x every lane receives both values of its pair.
+// operands x every lane receives both values of its pair.  The maximum is one
+// v_max_f32, where fmaxf would first quiet both operands: a NaN here can only
+// come from a NaN score, which makes the row's output NaN whatever this
+// maximum is.
 template <bool kHalf>
 __device__ __forceinline__ float max_lanes(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto p = kHalf ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
                        : __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  float m;
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(p[0]), "v"(p[1]));
+  return m;
 }
 
 // Four bf16 of a transposed 16x4 tile: in each 16-lane group, lane i receives
@@ -493,14 +498,14 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
     // v_exp_f32 directly: arguments lie in [-inf, kLazyRescale], and a result
     // below 2^-126 (flushed to zero here) is below any weight that can move
     // the output
-    float psum = 0.f;
+    float psum;
 #pragma unroll
     for (int t = 0; t < kT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = __builtin_amdgcn_exp2f(sacc[t][i] - m_run);
         sacc[t][i] = p;
-        psum += p;
+        psum = t == 0 && i == 0 ? p : psum + p;
       }
     l_run += psum;
 

@@ -24,10 +24,14 @@ struct FullWs {
   size_t block_max, super_max, topk_blocks, topk_scores, key_floor, scores, total;
 };
 
+// Super-block maxima per row in the workspace: ceil(N_max / 64) rounded up to
+// a multiple of 4, so that each row is 16-byte aligned for the block filter.
+inline int64_t super_stride(int64_t N_max) { return ((N_max + 63) / 64 + 3) / 4 * 4; }
+
 inline FullWs full_ws(int64_t R, int M, int64_t N_max, int k) {
   FullWs w;
   const int64_t nblk = (N_max + 7) / 8;
-  const int64_t nsup = (N_max + 63) / 64;
+  const int64_t nsup = super_stride(N_max);
   w.block_max = 0;
   w.super_max = align_up(w.block_max + (size_t)R * nblk * sizeof(float));
   w.topk_blocks = align_up(w.super_max + (size_t)R * nsup * sizeof(float));
@@ -152,7 +156,7 @@ int index_full_run(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
   int32_t* topk_blocks = reinterpret_cast<int32_t*>(ws + w.topk_blocks);
   float* topk_scores = reinterpret_cast<float*>(ws + w.topk_scores);
   float* smax = reinterpret_cast<float*>(ws + w.super_max);
-  const int64_t nsup = (N_max + 63) / 64;
+  const int64_t nsup = super_stride(N_max);
   // the pool's top-k lies in the pool's first min(k, n_pool) blocks
   const int kb = k < n_pool ? k : n_pool;
   if (M < kStoreScoresBelowM && k > 0) {

@@ -85,9 +85,12 @@ class Step:
     def full_index(self, cache: Cache, li: LayerInputs, idx: torch.Tensor):
         B, M, N = self.B, self.M, self.N
         if not self.staged:
+            # the block maxima are exported only by a step that keeps its
+            # intermediates (keep_scores); otherwise they stay in the workspace,
+            # in whichever layout the library's block filter reads fastest
             csa2_index_full(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, B, M, N,
                             self.n_pool, self.k, self.pool, idx, self.ws_full, scores=self.scores,
-                            block_max=self.block_max)
+                            block_max=self.block_max if self.scores is not None else None)
             return
         csa2_index_scan(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, li.n_visible, B, M, N,
                         self.block_max, scores=self.scores, super_max=self.super_max)

@@ -98,6 +98,43 @@ def test_prefill_scan_bitexact(kind, B, M, N):
         assert _same_f32(smax[r, :ns], np.array(want, np.float32)), r
 
 
+@pytest.mark.parametrize("kind", ["normal", "spread", "mixed", "overflow"])
+@pytest.mark.parametrize("B,M,N", [(1, 64, 4100), (2, 130, 3000), (1, 32, 1024), (2, 96, 2600), (2, 130, 8192),
+                                   (2, 64, 5000)])
+def test_prefill_scan_bitexact_causal(kind, B, M, N):
+    """A causal prefill chunk (query i of M sees the first N - M + i + 1
+    entries): whole half-rounds of 128 keys seen by every query of a wave (the
+    many-query scan's common case, stored 16 bytes a lane when the block rows
+    are 16-byte aligned: N = 1024, 8192, 5000), next to ragged last rounds,
+    partial query groups and tiles on the VALU path inside otherwise whole
+    rounds."""
+    w = Workload("pfc", 4242 + N + M, B=B, N=N, M=M, prefill_base=N - M)
+    cache, (lay,) = host_inputs(w, kind=kind)
+    nv = lay["n_visible"]
+    say(f"prefill scan causal B={B} M={M} N={N} kind={kind}")
+    c, l = dev(cache), dev(lay)
+    scores, bmax, smax = _run_scan(w, c, l, want_super=True)
+    # the maxima alone (no scores stored), as a Full-layer prefill asks for them
+    bmax2 = torch.full((w.R, (N + 7) // 8), float("nan"), device="cuda")
+    smax2 = torch.full((w.R, (N + 63) // 64), float("nan"), device="cuda")
+    csa2.csa2_index_scan(l["q_codes"], l["q_scales"], c["k_codes"], c["k_scales"], l["n_visible"], w.B, w.M, w.N,
+                         bmax2, super_max=smax2)
+    torch.cuda.synchronize()
+    bmax2, smax2 = bmax2.cpu().numpy(), smax2.cpu().numpy()
+    ref = oracle_full(w, cache, lay, want_scores=True, want_block_max=True)
+    for r in range(w.R):
+        n = nv[r]
+        assert n == N - M + r % M + 1
+        assert _same_f32(scores[r, :n], ref["scores"][r, :n]), r
+        nb = (n + 7) // 8
+        assert _same_f32(bmax[r, :nb], ref["block_max"][r, :nb]), r
+        ns = (n + 63) // 64
+        want = [np.max(ref["block_max"][r, 8 * s:min(8 * s + 8, nb)]) for s in range(ns)]
+        assert _same_f32(smax[r, :ns], np.array(want, np.float32)), r
+        assert _same_f32(bmax2[r, :nb], ref["block_max"][r, :nb]), r
+        assert _same_f32(smax2[r, :ns], np.array(want, np.float32)), r
+
+
 @pytest.mark.parametrize("kind", ["normal", "ties", "spread", "mixed", "overflow"])
 @pytest.mark.parametrize("N,n_pool,k,nv", [
     (4096, 2048, 512, [4096, 4000, 3333]),      # pool covers all blocks
