@@ -297,8 +297,21 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   __shared__ f32x4 sXh[NH][NP * ND * 64 * kT];   // partial S^T tiles of the ND waves of each head group
   __shared__ int32_t sIdx[kIdxCap];              // rows of the split's entries after each half's first chunk
 
-  const int split = blockIdx.x;
-  const int r = blockIdx.y;
+  // Workgroups reach the 8 XCDs round-robin by linear id; renumbered so that
+  // XCD x runs linear ids [x T/8, (x+1) T/8) in order, head group fastest, then
+  // split, then row: neighbouring rows, whose selections overlap in a prefill
+  // chunk, gather through one L2.  Grids of a size not divisible by 8 keep
+  // their order.
+  int split, r, hgrp;
+  {
+    const unsigned gx = gridDim.x, gy = gridDim.y, gz = gridDim.z, T = gx * gy * gz;
+    unsigned b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    if (T % 8u == 0u) b = (b % 8u) * (T / 8u) + b / 8u;
+    hgrp = (int)(b % gz);
+    b /= gz;
+    split = (int)(b % gx);
+    r = (int)(b / gx);
+  }
   const int64_t seq = r / a.M;
   const int tid = threadIdx.x;
   const int hf = NH > 1 ? __builtin_amdgcn_readfirstlane(tid / NT) : 0;   // half
@@ -312,7 +325,7 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   const int dbase = kDims * part;
   const int g = lane >> 4;     // lane group 0..3
   const int hl = lane & 15;
-  const int h = 16 * NP * blockIdx.z + 16 * pr + hl;   // head groups of 16*NP heads across blockIdx.z
+  const int h = 16 * NP * hgrp + 16 * pr + hl;   // head groups of 16*NP heads
   const int le = lane % kChunk;                          // this lane's entry of a chunk
 
   int wl = a.win_max > 0 ? a.win_len[r] : 0;

@@ -1055,6 +1055,15 @@ __device__ __forceinline__ void pool_topk_row(RegShared& sh, int32_t* sblk, int 
       [&](int, int p) { out[p] = -1; });
 }
 
+// Row of a one-dimensional grid of workgroups, renumbered so that each of the
+// 8 XCDs (which take linear workgroup ids round-robin) runs a contiguous run of
+// rows: neighbouring rows of a prefill chunk, whose pools overlap, rescore
+// through one L2.  Grids of a size not divisible by 8 keep their order.
+__device__ __forceinline__ int xcd_row() {
+  const unsigned b = blockIdx.x, T = gridDim.x;
+  return (int)(T % 8u == 0u ? (b % 8u) * (T / 8u) + b / 8u : b);
+}
+
 #define CSA2_POOL_TOPK_ARGS                                                                                     \
   const uint8_t *__restrict__ q_codes, const uint8_t *__restrict__ q_scales, const uint8_t *__restrict__ k_codes, \
       const uint8_t *__restrict__ k_scales, const int32_t *__restrict__ pool_blocks, int n_pool,                 \
@@ -1065,14 +1074,14 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8, 
     CSA2_POOL_TOPK_ARGS) {
   __shared__ RegShared sh;
   __shared__ int32_t sblk[512];
-  pool_topk_row<4>(sh, sblk, blockIdx.x, q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, M, N_max,
+  pool_topk_row<4>(sh, sblk, xcd_row(), q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, M, N_max,
                    floor_in, k, idx);
 }
 template <int J>
 __global__ __launch_bounds__(kSelThreads) void pool_topk_kernel(CSA2_POOL_TOPK_ARGS) {
   __shared__ RegShared sh;
   __shared__ int32_t sblk[128 * J];   // n_pool <= 1024 J / 8
-  pool_topk_row<J>(sh, sblk, blockIdx.x, q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, M, N_max,
+  pool_topk_row<J>(sh, sblk, xcd_row(), q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, M, N_max,
                    floor_in, k, idx);
 }
 #undef CSA2_POOL_TOPK_ARGS
