@@ -100,14 +100,15 @@ def test_prefill_scan_bitexact(kind, B, M, N):
 
 @pytest.mark.parametrize("kind", ["normal", "spread", "mixed", "overflow"])
 @pytest.mark.parametrize("B,M,N", [(1, 64, 4100), (2, 130, 3000), (1, 32, 1024), (2, 96, 2600), (2, 130, 8192),
-                                   (2, 64, 5000)])
+                                   (2, 64, 5000), (1, 64, 8190), (2, 33, 4096)])
 def test_prefill_scan_bitexact_causal(kind, B, M, N):
     """A causal prefill chunk (query i of M sees the first N - M + i + 1
-    entries): whole half-rounds of 128 keys seen by every query of a wave (the
+    entries): whole 256-key rounds seen by every query of a wave (the
     many-query scan's common case, stored 16 bytes a lane when the block rows
-    are 16-byte aligned: N = 1024, 8192, 5000), next to ragged last rounds,
-    partial query groups and tiles on the VALU path inside otherwise whole
-    rounds."""
+    are 16-byte aligned: N = 1024, 4096, 8190, 8192), next to ragged last
+    rounds, partial query groups and tiles on the VALU path inside otherwise
+    whole rounds.  N = 8190 ends in a tile two keys short of 32 behind 16-byte
+    rows; M = 33 leaves a last query group of one row."""
     w = Workload("pfc", 4242 + N + M, B=B, N=N, M=M, prefill_base=N - M)
     cache, (lay,) = host_inputs(w, kind=kind)
     nv = lay["n_visible"]
