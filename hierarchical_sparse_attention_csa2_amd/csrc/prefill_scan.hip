@@ -28,8 +28,8 @@
 // scalar tile offsets (the cache's own block layout), two MFMAs whose key scale
 // bytes are picked by operand select, then per 8-key block in-lane maxima and one
 // exchange between the half-waves.  Block maxima are staged in LDS and leave in
-// row segments after every 256 keys, so the tile loop holds no global stores and
-// its key loads stay in flight across tiles; the query operands, visibility
+// row lines after every 256 keys, so a round's tiles issue no global stores and
+// the key loads stay in flight across tiles; the query operands, visibility
 // bounds and exactness test are set up once per span.
 #include "device_common.h"
 #include "kernels.h"
@@ -56,14 +56,14 @@ constexpr int kPfBlocks = kPfKeyChunk / 8;                      // 32 block maxi
 constexpr int kPfBmLd = kPfBlocks + 1;                          // padded row: conflict-free column writes
 constexpr int kPfBufferConfig = 0x00020000;                     // gfx9 buffer descriptor word 3, raw dwords
 
-// Per-wave staging of the chunk's block maxima, written back in row segments
-// after the key loop (which then holds no global stores).
+// Per-wave staging of a 256-key round's block maxima, written back in row lines
+// at the end of the round.
 struct PfStage {
   float bm[kPfQueriesPerWave][kPfBmLd];
 };
 
-// Workgroup-wide: the query scale statistics of each wave and the chunk's
-// tiles that need the VALU path.
+// Workgroup-wide: the staging, the span's key scales, the query scale
+// statistics of each wave and the span's tiles that need the VALU path.
 struct PfShared {
   PfStage stage[kPfWaves];
   uint32_t kscale[kPfSpan];   // the span's key scale words (zero past the cache)
@@ -87,7 +87,7 @@ __device__ __forceinline__ float fmaximum_halves(float x) {
 // Exact score of one (query row, key) pair on the VALU, for tiles outside the
 // matrix cores' exact range.
 __device__ __forceinline__ float pair_score_valu(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
-                                              const uint8_t* ks) {
+                                                 const uint8_t* ks) {
   float s = 0.0f;
 #pragma unroll 1
   for (int b = 0; b < 4; ++b) {
