@@ -130,8 +130,8 @@ int csa2_select_blocks(const float* block_max, const float* super_max, int64_t n
  * csa2_index_pool - score only inside a pool (Reindex layers, and the Full
  * layer's own top-k; defined by: fupanwang.com article, section
  * "三个方向一起压小缓存" - later layers score only inside the first Full layer's
- * candidate pool; dreamax.pages.dev notes, CSA2 paragraph - the Reindex mode)
- * layer's own top-k): for row r, pool block i and t = 0..7 the score of position
+ * candidate pool; dreamax.pages.dev notes, CSA2 paragraph - the Reindex mode):
+ * for row r, pool block i and t = 0..7 the score of position
  * j = 8*pool_blocks[r][i] + t against the row's own index query, written to
  * pool_scores[r][8i+t]; slots with pool_blocks < 0 or j >= n_visible[r] are
  * written as -inf.  Same score definition as csa2_index_scan.
