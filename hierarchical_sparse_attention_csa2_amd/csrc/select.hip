@@ -518,12 +518,26 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
 // super-blocks.
 //
 // Thread t owns super-blocks 8t..8t+7 at level 1; the kept super-blocks are
-// listed in id order with one workgroup prefix sum, and thread t then gathers a
-// contiguous run of at most three of them.  Its blocks >= T1 (the survivors)
-// are written to LDS in id order at positions from a second prefix sum, and
-// counted into level 2's histogram on the way.
-constexpr int kB3Items = 8;                        // super-blocks per thread at level 1
-constexpr int kB3Gather = kKeepCap / kSelThreads;  // kept super-blocks per thread (3)
+// listed in id order with one workgroup prefix sum.  The gather then reads each
+// kept super-block's 8 block maxima as two 16-byte halves, six halves per
+// thread, in one of two layouts:
+//  - runs (kPairs false): thread t takes kept super-blocks [G t, G t + G),
+//    G = ceil(nkept / 1024) <= 3, so its survivors are contiguous in id order
+//    and one prefix sum places them;
+//  - pairs (kPairs true): in pass p, lanes 2i and 2i+1 take the two halves of
+//    kept super-block 512p + i, so a load instruction covers 32 consecutive
+//    entries of the kept list, one run of rows when most super-blocks are kept
+//    (a prefill row: three quarters pass level 1) instead of 64 lines; id order
+//    is then (pass, thread, element) order, placed by per-pass prefix sums.
+// The stand-alone filter takes pairs; the fused decode selection keeps runs
+// (its top-k side keeps a few percent of a long row's super-blocks, far apart,
+// where pairs gain nothing and their extra placement work cost 0.4 us a row).
+// The blocks >= T1 (the survivors) are written to LDS in id order and counted
+// into level 2's histogram on the way.
+constexpr int kB3Items = 8;                          // super-blocks per thread at level 1
+constexpr int kB3Pass = 2 * kKeepCap / kSelThreads;  // half super-blocks gathered per thread (6)
+static_assert(kB3Pass * kSelThreads / 2 == kKeepCap, "gather passes cover the kept-list capacity");
+static_assert(kB3Pass == 6, "three packed prefix sums of two passes each");
 
 struct Blocks3Shared {
   int32_t cids[kCompCap];       // survivors' block ids, id order
@@ -547,6 +561,28 @@ __device__ __forceinline__ int block_excl_scan(int* buf, int x, int& total) {
   const int wi = row_incl_scan(wt);
   total = __builtin_amdgcn_readlane(wi, kSelWaves - 1);
   return __builtin_amdgcn_readlane(wi, w) - __builtin_amdgcn_readlane(wt, w) + incl - x;
+}
+
+// Exclusive prefix sums of three values over the workgroup in thread order,
+// and their totals, with one barrier.  buf: 3 x 16 ints, as block_excl_scan's.
+__device__ __forceinline__ void block_excl_scan3(int (*buf)[kSelWaves], const int (&x)[3], int (&excl)[3],
+                                                 int (&total)[3]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) incl[i] = wave_incl_scan(x[i]);
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) buf[i][w] = incl[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int wt = lane < kSelWaves ? buf[i][lane] : 0;
+    const int wi = row_incl_scan(wt);
+    total[i] = __builtin_amdgcn_readlane(wi, kSelWaves - 1);
+    excl[i] = __builtin_amdgcn_readlane(wi, w) - __builtin_amdgcn_readlane(wt, w) + incl[i] - x[i];
+  }
 }
 
 // Level 2 of the block filter: exact selection among the m2 <= 1024*J
@@ -578,7 +614,7 @@ __device__ __forceinline__ void blocks_level2(Blocks3Shared& sh, int m2, uint32_
 // loads each.
 // Row r of the two-level block filter.  o0 / o1: this row's outputs (may be
 // null); floor_out: this row's floor slot (may be null).
-template <bool kHaveSuper, bool kVec>
+template <bool kHaveSuper, bool kVec, bool kPairs>
 __device__ __forceinline__ void select_blocks3_row(Blocks3Shared& sh, int r, const float* __restrict__ bmax,
                                                    int64_t stride, const float* __restrict__ super_max,
                                                    int64_t nsup_stride, const int32_t* __restrict__ n_visible,
@@ -648,9 +684,11 @@ __device__ __forceinline__ void select_blocks3_row(Blocks3Shared& sh, int r, con
 
   int approx = kKeepCap;
   uint32_t T1 = 1u;
-  int nkept = 0, m2 = 0, cpos = 0;
-  int sbq[kB3Gather];
-  uint32_t ck[kB3Gather * 8];   // survivors (>= T1) of this thread's run, 0 elsewhere
+  int nkept = 0, m2 = 0;
+  uint32_t ck[kB3Pass * 4];      // survivors (>= T1) of this thread's gathered blocks, 0 elsewhere
+  int cpos2[kB3Pass / 2];        // pairs: LDS positions of passes 2i, 2i+1's first survivors (16 bits each)
+  int sbq[kB3Pass / 2];          // runs: this thread's kept super-blocks, -1 when none
+  int cpos = 0;                  // runs: LDS position of this thread's first survivor
   for (;;) {
     Thr a0, a1;
     select_thresholds(sh.c, sh.s, k1, kB3Items, valid1, kmin1, kmax1, kmaxK, 0, approx, a0, a1);
@@ -691,43 +729,94 @@ __device__ __forceinline__ void select_blocks3_row(Blocks3Shared& sh, int r, con
       sh.s.cnt[0] = 0;
       sh.s.cnt[1] = 0;
     }
-    // gather: thread t takes kept super-blocks [G t, G t + G), G = ceil(nkept / 1024)
-    const int G = (nkept + kSelThreads - 1) / kSelThreads;   // <= 3
-    float gv[kB3Gather * 8];
+    if constexpr (kPairs) {
+      // pass p: lanes 2i, 2i+1 take the halves of kept super-block 512p + i
+      float gv[kB3Pass * 4];
+      int b0p[kB3Pass];   // first block of this lane's half, -1 when none
 #pragma unroll
-    for (int q = 0; q < kB3Gather; ++q) {
-      const int u = G * t + q;
-      const bool on = q < G && u < nkept;
-      sbq[q] = on ? sh.sbsel[u] : -1;
-      const int sb = on ? sbq[q] : 0;
-      if constexpr (kVec) {
-        // 8 sb + 7 < stride: stride is a multiple of 8 here
+      for (int p = 0; p < kB3Pass; ++p) {
+        const int u = (kSelThreads / 2) * p + (t >> 1);
+        const bool on = u < nkept;
+        const int b0 = 8 * (on ? sh.sbsel[u] : 0) + 4 * (t & 1);
+        b0p[p] = on ? b0 : -1;
+        if constexpr (kVec) {
+          // b0 + 3 < stride: stride is a multiple of 8 here
+          const f32x4_t v = on ? *reinterpret_cast<const f32x4_t*>(row + b0) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4_t v =
-              on ? *reinterpret_cast<const f32x4_t*>(row + 8 * sb + 4 * h) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int e = 0; e < 4; ++e) gv[4 * p + e] = v[e];
+        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) gv[8 * q + 4 * h + e] = v[e];
+          for (int e = 0; e < 4; ++e) gv[4 * p + e] = (on && b0 + e < nblk) ? row[b0 + e] : 0.0f;
         }
-      } else {
+      }
+      int nc[kB3Pass];
+#pragma unroll
+      for (int p = 0; p < kB3Pass; ++p) {
+        nc[p] = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = (b0p[p] >= 0 && b0p[p] + e < nblk) ? order_key(gv[4 * p + e]) : 0u;
+          ck[4 * p + e] = key >= T1 ? key : 0u;
+          nc[p] += ck[4 * p + e] != 0u ? 1 : 0;
+        }
+      }
+      // positions in (pass, thread) order: two passes per scan, 16 bits each
+      // (a pass holds at most 4 * 1024 survivors)
+      const int x[3] = {nc[0] | (nc[1] << 16), nc[2] | (nc[3] << 16), nc[4] | (nc[5] << 16)};
+      int ex[3], tot[3];
+      // wsum rows 0-2: their last reads (the tie and kept-list sums) precede the
+      // barrier after the kept list
+      block_excl_scan3(sh.wsum, x, ex, tot);
+      int base = 0;
+#pragma unroll
+      for (int i = 0; i < kB3Pass / 2; ++i) {
+        // m2 <= 24 * 1024 < 2^16
+        const int lo = base + (ex[i] & 0xFFFF);
+        base += tot[i] & 0xFFFF;
+        const int hi = base + (ex[i] >> 16);
+        base += tot[i] >> 16;
+        cpos2[i] = lo | (hi << 16);
+      }
+      m2 = base;
+    } else {
+      // thread t takes kept super-blocks [G t, G t + G), G = ceil(nkept / 1024)
+      const int G = (nkept + kSelThreads - 1) / kSelThreads;   // <= 3
+      float gv[kB3Pass * 4];
+#pragma unroll
+      for (int q = 0; q < kB3Pass / 2; ++q) {
+        const int u = G * t + q;
+        const bool on = q < G && u < nkept;
+        sbq[q] = on ? sh.sbsel[u] : -1;
+        const int sb = on ? sbq[q] : 0;
+        if constexpr (kVec) {
+          // 8 sb + 7 < stride: stride is a multiple of 8 here
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const f32x4_t v =
+                on ? *reinterpret_cast<const f32x4_t*>(row + 8 * sb + 4 * h) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gv[8 * q + 4 * h + e] = v[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int b = 8 * sb + e;
+            gv[8 * q + e] = (on && b < nblk) ? row[b] : 0.0f;
+          }
+        }
+      }
+      int nc = 0;
+#pragma unroll
+      for (int q = 0; q < kB3Pass / 2; ++q) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int b = 8 * sb + e;
-          gv[8 * q + e] = (on && b < nblk) ? row[b] : 0.0f;
+          const uint32_t key = (sbq[q] >= 0 && 8 * sbq[q] + e < nblk) ? order_key(gv[8 * q + e]) : 0u;
+          ck[8 * q + e] = key >= T1 ? key : 0u;
+          nc += ck[8 * q + e] != 0u ? 1 : 0;
         }
       }
+      cpos = block_excl_scan(sh.wsum[2], nc, m2);
     }
-    int nc = 0;
-#pragma unroll
-    for (int q = 0; q < kB3Gather; ++q) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t key = (sbq[q] >= 0 && 8 * sbq[q] + e < nblk) ? order_key(gv[8 * q + e]) : 0u;
-        ck[8 * q + e] = key >= T1 ? key : 0u;
-        nc += ck[8 * q + e] != 0u ? 1 : 0;
-      }
-    }
-    cpos = block_excl_scan(sh.wsum[2], nc, m2);
     if (m2 > kCompCap && approx > 0) {
       // too many survivors for LDS: redo level 1 exactly (at most 8 * 2048)
       approx = 0;
@@ -738,14 +827,33 @@ __device__ __forceinline__ void select_blocks3_row(Blocks3Shared& sh, int r, con
   // survivors to LDS in id order, counted into level 2's first-digit histogram
   {
     const int s2 = first_digit_shift(T1, kmax1);
-    int pos = cpos;
+    if constexpr (kPairs) {
 #pragma unroll
-    for (int j = 0; j < kB3Gather * 8; ++j) {
-      if (ck[j] != 0u) {
-        sh.ckeys[pos] = ck[j];
-        sh.cids[pos] = 8 * sbq[j >> 3] + (j & 7);
-        atomicAdd(&sh.c.hist[((ck[j] - T1) >> s2) & (kBins - 1)], 1u);
-        ++pos;
+      for (int p = 0; p < kB3Pass; ++p) {
+        int pos = (cpos2[p >> 1] >> ((p & 1) ? 16 : 0)) & 0xFFFF;
+        // the kept list is intact until level 2 emits
+        const int b0 = 8 * sh.sbsel[(kSelThreads / 2) * p + (t >> 1)] + 4 * (t & 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = ck[4 * p + e];
+          if (key != 0u) {
+            sh.ckeys[pos] = key;
+            sh.cids[pos] = b0 + e;
+            atomicAdd(&sh.c.hist[((key - T1) >> s2) & (kBins - 1)], 1u);
+            ++pos;
+          }
+        }
+      }
+    } else {
+      int pos = cpos;
+#pragma unroll
+      for (int j = 0; j < kB3Pass * 4; ++j) {
+        if (ck[j] != 0u) {
+          sh.ckeys[pos] = ck[j];
+          sh.cids[pos] = 8 * sbq[j >> 3] + (j & 7);
+          atomicAdd(&sh.c.hist[((ck[j] - T1) >> s2) & (kBins - 1)], 1u);
+          ++pos;
+        }
       }
     }
   }
@@ -768,7 +876,7 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks3_kernel(const float
                                                                      uint32_t* __restrict__ floor_out) {
   __shared__ Blocks3Shared sh;
   const int r = blockIdx.x;
-  select_blocks3_row<kHaveSuper, kVec>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, K0,
+  select_blocks3_row<kHaveSuper, kVec, true>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, K0,
                                        out0 ? out0 + (int64_t)r * K0 : nullptr, K1,
                                        out1 ? out1 + (int64_t)r * K1 : nullptr, floor_out ? floor_out + r : nullptr);
 }
@@ -871,12 +979,12 @@ __global__ __launch_bounds__(kSelThreads) void select_blocks3_topk_kernel(
   const int R = (int)(gridDim.x >> 1);
   if ((int)blockIdx.x >= R) {
     const int r = (int)blockIdx.x - R;
-    select_blocks3_row<true, kVec>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, n_pool,
+    select_blocks3_row<true, kVec, false>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, n_pool,
                                    pool_out + (int64_t)r * n_pool, 0, nullptr, nullptr);
     return;
   }
   const int r = blockIdx.x;
-  select_blocks3_row<true, kVec>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, 0, nullptr, kb, sh.sbsel,
+  select_blocks3_row<true, kVec, false>(sh, r, bmax, stride, super_max, nsup_stride, n_visible, 0, nullptr, kb, sh.sbsel,
                                  &sh.floor);
   __syncthreads();
   int64_t nv = n_visible[r];
