@@ -43,6 +43,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kAttnTargetWorkgroups = 256;   // one per compute unit
 constexpr int kAttnChunk = 32;
 constexpr int kIdxCap = 1024;                 // staged indices per workgroup (splits keep within it)
+constexpr int kAttnThirdsMinChunks = 16;      // chunks a split needs before three streams share it
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -292,7 +293,7 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   constexpr int kJ = CH / 32;         // K steps of O^T
   constexpr uint64_t kChunkBits = CH == 64 ? ~0ull : ((1ull << CH) - 1ull);
   static_assert(CH == 32 || CH == 64, "chunk of 32 or 64 entries");
-  static_assert(NH == 1 || NH == 2, "one or two halves");
+  static_assert(NH >= 1 && NH <= 3, "one to three chunk streams");
   __shared__ __attribute__((aligned(16))) __bf16 sKh[NH][kChunk * kKLd];
   __shared__ f32x4 sXh[NH][NP * ND * 64 * kT];   // partial S^T tiles of the ND waves of each head group
   __shared__ int32_t sIdx[kIdxCap];              // rows of the split's entries after each half's first chunk
@@ -566,28 +567,41 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& a) {
   }
 
   if constexpr (NH > 1) {
-    // the halves' states meet: thread t of half 1 holds the same heads and
-    // dims as thread t of half 0, over the other chunks of the split
+    // the streams' states meet: thread t of stream q holds the same heads and
+    // dims as thread t of stream 0, over the other chunks of the split;
+    // streams 1 .. NH-1 leave theirs in the chunk buffers, stream 0 adds them
+    // in stream order
     __syncthreads();   // every chunk's LDS reads are done
-    float* po = reinterpret_cast<float*>(&sKh[0][0]);   // kM x 4 floats a thread
-    float* pml = reinterpret_cast<float*>(&sXh[0][0]);  // m and l a thread
-    static_assert(NT * kM * 4 * sizeof(float) <= sizeof(sKh) && 2 * NT * sizeof(float) <= sizeof(sXh),
+    float* po = reinterpret_cast<float*>(&sKh[0][0]);   // per stream q >= 1: kM x 4 floats a thread
+    float* pml = reinterpret_cast<float*>(&sXh[0][0]);  // per stream q >= 1: m and l a thread
+    static_assert((NH - 1) * NT * kM * 4 * sizeof(float) <= sizeof(sKh) &&
+                      2 * (NH - 1) * NT * sizeof(float) <= sizeof(sXh),
                   "the merge fits the chunk buffers");
-    if (hf == 1) {
+    if (hf >= 1) {
+      float* pq = po + (hf - 1) * NT * kM * 4;
 #pragma unroll
-      for (int m = 0; m < kM; ++m) *reinterpret_cast<f32x4*>(po + (m * NT + tidh) * 4) = oacc[m];
-      pml[tidh] = m_run;
-      pml[NT + tidh] = l_run;
+      for (int m = 0; m < kM; ++m) *reinterpret_cast<f32x4*>(pq + (m * NT + tidh) * 4) = oacc[m];
+      pml[2 * (hf - 1) * NT + tidh] = m_run;
+      pml[(2 * (hf - 1) + 1) * NT + tidh] = l_run;
     }
     __syncthreads();
-    if (hf == 1) return;   // no barrier follows
-    const float m1 = pml[tidh], l1 = pml[NT + tidh];
-    const float M = fmaxf(m_run, m1);
-    const float a0 = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - M);
-    const float a1 = m1 == -__builtin_inff() ? 0.f : exp2f(m1 - M);
-    l_run = l_run * a0 + l1 * a1;
+    if (hf >= 1) return;   // no barrier follows
+    float M = m_run;
 #pragma unroll
-    for (int m = 0; m < kM; ++m) oacc[m] = oacc[m] * a0 + *reinterpret_cast<const f32x4*>(po + (m * NT + tidh) * 4) * a1;
+    for (int q = 1; q < NH; ++q) M = fmaxf(M, pml[2 * (q - 1) * NT + tidh]);
+    const float a0 = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - M);
+    l_run = l_run * a0;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) oacc[m] = oacc[m] * a0;
+#pragma unroll
+    for (int q = 1; q < NH; ++q) {
+      const float mq = pml[2 * (q - 1) * NT + tidh], lq = pml[(2 * (q - 1) + 1) * NT + tidh];
+      const float aq = mq == -__builtin_inff() ? 0.f : exp2f(mq - M);
+      l_run = l_run + lq * aq;
+      const float* pq = po + (q - 1) * NT * kM * 4;
+#pragma unroll
+      for (int m = 0; m < kM; ++m) oacc[m] = oacc[m] + *reinterpret_cast<const f32x4*>(pq + (m * NT + tidh) * 4) * aq;
+    }
     m_run = M;
   }
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
@@ -626,6 +640,14 @@ __global__ __launch_bounds__(1024, 1) void sparse_attn_kernel_h32c32_halves(Attn
 }
 __global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h16c32_halves(AttnParams a) {
   sparse_attn_body<1, 4, 32, 2>(a);
+}
+// Three streams of 4 waves on every third chunk (12 waves, 130 KB of LDS), for
+// 16-head grids of one workgroup per CU with long splits: a third stream makes
+// each round about 40% longer, which pays only where it saves many rounds
+// (64 rows x 20 chunks: 10 -> 7 rounds, 34.0 -> 33.0 us a layer; 10-chunk
+// splits: 27 -> 28.5 us, not taken).
+__global__ __launch_bounds__(768, 1) void sparse_attn_kernel_h16c32_thirds(AttnParams a) {
+  sparse_attn_body<1, 4, 32, 3>(a);
 }
 __global__ __launch_bounds__(512, 1) void sparse_attn_kernel_h32c64(AttnParams a) { sparse_attn_body<2, 4, 64, 1>(a); }
 __global__ __launch_bounds__(256) void sparse_attn_kernel_h16c32(AttnParams a) { sparse_attn_body<1, 4, 32, 1>(a); }
@@ -797,6 +819,8 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
     hipLaunchKernelGGL(sparse_attn_kernel_h32c32_2wg, grid, dim3(512), 0, stream, a);
   else if (halves && NP == 2)
     hipLaunchKernelGGL(sparse_attn_kernel_h32c32_halves, grid, dim3(1024), 0, stream, a);
+  else if (halves && NP == 1 && a.chunks_per_split >= kAttnThirdsMinChunks)
+    hipLaunchKernelGGL(sparse_attn_kernel_h16c32_thirds, grid, dim3(768), 0, stream, a);
   else if (halves)
     hipLaunchKernelGGL(sparse_attn_kernel_h16c32_halves, grid, dim3(512), 0, stream, a);
   else if (NP == 2 && ch == 32)
