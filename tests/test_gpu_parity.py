@@ -429,6 +429,32 @@ def test_sparse_attn_many_rows_long_rows(B, M, k, H):
     assert err <= ATOL
 
 
+@pytest.mark.parametrize("B,M,k,H", [
+    (64, 1, 512, 64),    # 64 rows x 4 groups of 16 heads, one split of 20 chunks: streams of 7, 7, 6
+    (4, 16, 600, 64),    # ragged rows, one split of 23 chunks: 8, 8, 7
+    (2, 16, 2000, 32),   # four splits of 17 chunks (the last 16) and their combine
+])
+def test_sparse_attn_three_streams(B, M, k, H):
+    """Grids of 16-head workgroups, one a compute unit, whose splits hold 16 or
+    more chunks: the workgroup's three streams take every third chunk and merge
+    their softmax states at the end (streams with an empty last round, padded
+    and repeated entries, short windows)."""
+    w = Workload("attn3", 7000 + B * M + k, B=B, M=M, N=2500, H=H, k=k)
+    cache, (lay,) = host_inputs(w)
+    rng = np.random.default_rng(B * M + k + H)
+    lay["win_len"] = rng.integers(0, 129, size=w.R).astype(np.int32)
+    idx = np.sort(rng.choice(w.N, size=(w.R, k), replace=True), axis=1).astype(np.int32)
+    idx[::5, k // 3:] = -1            # padded rows
+    idx[1, :] = idx[1, 0]             # one entry repeated k times
+    say(f"attn three streams B={B} M={M} k={k} H={H}")
+    got = _attn_case(w, cache, lay, idx, 128)
+    ref = oracle_attn(w, cache, lay, idx)
+    err = np.max(np.abs(got - ref))
+    say(f"  max abs err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= ATOL
+
+
 @pytest.mark.parametrize("H", [32, 64])
 def test_sparse_attn_out_of_range_names(H):
     """Indices outside [0, N_max), window rows outside [0, Tw), window lengths
