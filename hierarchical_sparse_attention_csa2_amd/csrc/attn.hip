@@ -729,14 +729,15 @@ __global__ __launch_bounds__(512 / V) void attn_combine_kernel(const float* __re
 }
 
 // Head groups of 16 heads per workgroup (32 when H allows).
-// (16 where 32-head groups leave compute units idle and there are several
-// rows: at 64 rows x 4 groups every compute unit gets a workgroup with one
-// split a row, two halves share the row's chunks and no combine runs; with
-// fewer rows the splits, and the partials the combine reads, halve)
+// (16 where 32-head groups leave compute units idle: at 64 rows x 4 groups
+// every compute unit gets a workgroup with one split a row, two halves share
+// the row's chunks and no combine runs; with fewer rows the splits, and the
+// partials the combine reads, halve; a single row's one-chunk workgroups also
+// finish sooner at 16 heads: 4,096-entry decode step 24.3 -> 22.9 us)
 static int attn_group_heads(int R, int H) {
   if (H < 32) return 16;
   const int64_t g32 = (int64_t)R * (H / 32);
-  return H % 16 == 0 && g32 < kAttnTargetWorkgroups && R >= 2 ? 16 : 32;
+  return H % 16 == 0 && g32 < kAttnTargetWorkgroups ? 16 : 32;
 }
 
 // Entries per chunk: 32 keeps a workgroup's LDS at 54 KB, so two workgroups
