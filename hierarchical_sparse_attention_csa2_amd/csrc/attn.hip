@@ -749,9 +749,18 @@ static int attn_chunk(int R, int H, int k_plus_win) {
   return kAttnChunk;
 }
 
+// 16-head grids with fewer head groups than compute units run independent
+// 4-wave workgroups, two a compute unit (a target of 512), rather than
+// workgroups of two halves: decode at 4 rows x 4 groups 55.4 -> 54.1 us (one
+// chunk a workgroup), 20 rows x 4 groups 82.5 -> 80.6 us, 32 rows x 4 groups
+// unchanged.
+static bool attn_small16(int R, int H) {
+  return attn_group_heads(R, H) == 16 && (int64_t)R * (H / 16) < kAttnTargetWorkgroups;
+}
+
 // Splits of a row's entry chunks: enough workgroups to give every compute unit
-// about one (a workgroup's LDS fills a compute unit), or one chunk each when
-// those workgroups all fit at once, never more splits than chunks, and chunks
+// about one (a workgroup's LDS fills a compute unit), or two for small 16-head
+// grids, never more splits than chunks or than the combine takes, and chunks
 // spread evenly over the splits.
 int attn_splits(int R, int H, int k_plus_win) {
   const int ch = attn_chunk(R, H, k_plus_win);
@@ -759,13 +768,11 @@ int attn_splits(int R, int H, int k_plus_win) {
   if (n_chunks <= 1) return 1;
   const int gh = attn_group_heads(R, H);
   const int64_t groups = (int64_t)R * (H > 0 ? (H + gh - 1) / gh : 1);
-  int64_t want = (kAttnTargetWorkgroups + groups - 1) / groups;
-  // a grid whose one-chunk workgroups are all resident at once (two a compute
-  // unit) takes one chunk a split: short chains beat fewer partials there
-  // (4 rows x 4 head groups x 20 chunks: decode step 55.4 -> 54.1 us)
-  if (groups * n_chunks <= 2 * kAttnTargetWorkgroups) want = n_chunks;
+  const int64_t target = attn_small16(R, H) ? 2 * kAttnTargetWorkgroups : kAttnTargetWorkgroups;
+  int64_t want = (target + groups - 1) / groups;
   if (want < 1) want = 1;
   if (want > n_chunks) want = n_chunks;
+  if (want > kMaxSplits) want = kMaxSplits;
   const int cps = (int)((n_chunks + want - 1) / want);
   return (n_chunks + cps - 1) / cps;
 }
@@ -813,7 +820,7 @@ hipError_t launch_sparse_attn(const AttnLaunch& L, hipStream_t stream) {
   // a grid of one workgroup per CU whose splits hold several chunks runs
   // 16-wave workgroups whose halves take alternate chunks (c4: 47 -> 41 us per
   // layer); splits of one chunk keep the 8-wave kernel (more workgroups)
-  const bool halves = ch == 32 && !many && a.chunks_per_split >= 2;
+  const bool halves = ch == 32 && !many && a.chunks_per_split >= 2 && !attn_small16(R, L.H);
   a.part_o = nullptr;
   a.part_ml = nullptr;
   if (a.splits > 1) {
