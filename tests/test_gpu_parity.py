@@ -455,6 +455,25 @@ def test_sparse_attn_three_streams(B, M, k, H):
     assert err <= ATOL
 
 
+@pytest.mark.parametrize("H,k", [(16, 9000), (32, 16000)])
+def test_sparse_attn_more_chunks_than_splits(H, k):
+    """One row over more than 256 chunks of entries: the splits stop at the 256
+    the combine merges (each split then takes two or more chunks) and every
+    split's partial still reaches the output."""
+    w = Workload("attnS", 9000 + H, B=1, N=k + 100, H=H, k=k)
+    cache, (lay,) = host_inputs(w)
+    rng = np.random.default_rng(H + k)
+    lay["win_len"] = np.array([128], np.int32)
+    idx = np.sort(rng.choice(w.N, size=(w.R, k), replace=False), axis=1).astype(np.int32)
+    say(f"attn one row H={H} k={k}")
+    got = _attn_case(w, cache, lay, idx, 128)
+    ref = oracle_attn(w, cache, lay, idx)
+    err = np.max(np.abs(got - ref))
+    say(f"  max abs err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= ATOL
+
+
 @pytest.mark.parametrize("H", [32, 64])
 def test_sparse_attn_out_of_range_names(H):
     """Indices outside [0, N_max), window rows outside [0, Tw), window lengths
