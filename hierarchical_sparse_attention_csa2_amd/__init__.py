@@ -13,6 +13,7 @@ Full / Reindex / Reuse modes):
     Full    : csa2_index_full (scan -> 8-position block max -> 2048-block pool ->
               top-512) then csa2_sparse_attn
     Reindex : csa2_index_pool over the Full layer's pool -> csa2_topk -> attention
+              (csa2_index_pool_topk, the same in one call, from 256 rows up)
     Reuse   : csa2_sparse_attn with the previous layer's indices
 """
 from __future__ import annotations
@@ -36,7 +37,7 @@ CSA2_OP_INDEX_FULL = 1
 CSA2_OP_SPARSE_ATTN = 2
 
 EXPORTED = (
-    "csa2_index_scan", "csa2_select_blocks", "csa2_index_pool", "csa2_topk", "csa2_index_full",
+    "csa2_index_scan", "csa2_select_blocks", "csa2_index_pool", "csa2_topk", "csa2_index_pool_topk", "csa2_index_full",
     "csa2_index_full_static", "csa2_sparse_attn", "csa2_cache_write_mxfp4", "csa2_cache_write_e4m3",
     "csa2_workspace_bytes", "csa2_status_string",
 )
@@ -64,6 +65,7 @@ def load_library(path: str = LIB_PATH):
     L.csa2_select_blocks.argtypes = [vp, vp, i64, vp, i32, i32, vp, i32, vp, vp]
     L.csa2_index_pool.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i64, vp, vp]
     L.csa2_topk.argtypes = [vp, vp, i64, vp, i32, i32, vp, vp]
+    L.csa2_index_pool_topk.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i64, i32, vp, vp]
     L.csa2_index_full.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.csa2_index_full_static.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp]
     L.csa2_sparse_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i64, i32, i32, f32, vp, vp, sz,
@@ -213,6 +215,17 @@ def csa2_index_pool(q_codes, q_scales, k_codes, k_scales, pool_blocks, n_visible
         _dev(k_codes, "k_codes", U8, numel=B * N_max * 64), _dev(k_scales, "k_scales", U8, numel=B * N_max * 4),
         _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), n_pool, _dev(n_visible, "n_visible", I32, (R,)),
         B, M, N_max, _dev(pool_scores, "pool_scores", F32, (R, 8 * n_pool)), _stream(stream))
+
+
+def csa2_index_pool_topk(q_codes, q_scales, k_codes, k_scales, pool_blocks, n_visible, B, M, N_max, k, idx,
+                         stream=None):
+    R = B * M
+    n_pool = pool_blocks.shape[1]
+    _call("csa2_index_pool_topk",
+        _dev(q_codes, "q_codes", U8, (R, 64)), _dev(q_scales, "q_scales", U8, (R, 4)),
+        _dev(k_codes, "k_codes", U8, numel=B * N_max * 64), _dev(k_scales, "k_scales", U8, numel=B * N_max * 4),
+        _dev(pool_blocks, "pool_blocks", I32, (R, n_pool)), n_pool, _dev(n_visible, "n_visible", I32, (R,)),
+        B, M, N_max, k, _dev(idx, "idx", I32, (R, k)), _stream(stream))
 
 
 def csa2_topk(scores, n_visible, k, idx, pool_blocks=None, stream=None):

@@ -53,6 +53,7 @@ inline bool any_misaligned(const P*... p) {
 constexpr int64_t kMaxRows = 1 << 24;
 constexpr int64_t kMaxN = (int64_t)1 << 30;   // ids are int32; 8*blocks must fit
 constexpr int kMaxPool = 1 << 20;
+constexpr int kMaxFusedPool = 2048;   // pool blocks csa2_index_pool_topk scores in one workgroup
 constexpr int kMaxRatio = 64;                          // tokens merged into one cached entry
 constexpr int kMaxWriteDim = 1 << 14;                  // elements per cached row
 constexpr int64_t kMaxWriteElems = (int64_t)1 << 40;   // fp32 input elements of one write call
@@ -123,6 +124,20 @@ int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, c
   const int layout = pool_blocks ? csa2::kSelPool : csa2::kSelFull;
   return hip_status(csa2::launch_select(layout, scores, pool_blocks ? 8 * n_pool : n_pool, pool_blocks, n_pool,
                                         n_visible, R, k, idx, 0, nullptr, nullptr, 0, as_stream(stream)));
+}
+
+int csa2_index_pool_topk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                         const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool, const int32_t* n_visible,
+                         int B, int M, int64_t N_max, int k, int32_t* idx, void* stream) {
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !pool_blocks || !n_visible || !idx)
+    return CSA2_ERR_INVALID;
+  if (any_misaligned(q_codes, q_scales, k_codes, k_scales, pool_blocks, n_visible, idx)) return CSA2_ERR_INVALID;
+  if (B < 1 || M < 1 || N_max < 1 || N_max > kMaxN || (int64_t)B * M > kMaxRows || n_pool < 1 ||
+      n_pool > kMaxFusedPool || k < 0 || k > kMaxPool)
+    return CSA2_ERR_INVALID;
+  if (k == 0) return CSA2_OK;
+  return hip_status(csa2::launch_pool_topk(q_codes, q_scales, k_codes, k_scales, pool_blocks, n_pool, n_visible, B, M,
+                                           N_max, nullptr, k, idx, as_stream(stream)));
 }
 
 }  // extern "C"

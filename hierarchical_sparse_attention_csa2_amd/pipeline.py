@@ -18,8 +18,14 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (CSA2_OP_INDEX_FULL, CSA2_OP_SPARSE_ATTN, csa2_index_full, csa2_index_pool, csa2_index_scan,
-               csa2_select_blocks, csa2_sparse_attn, csa2_topk, csa2_workspace_bytes, recording)
+from . import (CSA2_OP_INDEX_FULL, CSA2_OP_SPARSE_ATTN, csa2_index_full, csa2_index_pool, csa2_index_pool_topk,
+               csa2_index_scan, csa2_select_blocks, csa2_sparse_attn, csa2_topk, csa2_workspace_bytes, recording)
+
+FUSED_POOL_BLOCKS = 2048   # pools csa2_index_pool_topk takes (one workgroup scores and ranks a row)
+# Rows from which the one-call Reindex beats index_pool + topk (a 2048-block pool
+# over 266,240 entries: 64 rows 49.6 vs 32.8 us, 256 rows 59.8 vs 66.1 us, 4,096
+# rows 813.5 vs 947.1 us): with fewer rows its workgroups leave compute units idle.
+FUSED_MIN_ROWS = 256
 
 
 @dataclass
@@ -116,6 +122,11 @@ class Step:
         self.attend(cache, li, self.idx[0], self.out[0])
 
     def reindex(self, cache: Cache, li: LayerInputs, idx: torch.Tensor):
+        if self.k > 0 and self.pool.shape[1] <= FUSED_POOL_BLOCKS and self.B * self.M >= FUSED_MIN_ROWS:
+            # scoring and top-k in one workgroup per row
+            csa2_index_pool_topk(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, self.pool, li.n_visible,
+                                 self.B, self.M, self.N, self.k, idx)
+            return
         csa2_index_pool(li.q_codes, li.q_scales, cache.k_codes, cache.k_scales, self.pool, li.n_visible,
                         self.B, self.M, self.N, self.pool_scores)
         csa2_topk(self.pool_scores, li.n_visible, self.k, idx, pool_blocks=self.pool)

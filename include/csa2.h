@@ -161,6 +161,28 @@ int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, c
               int R, int k, int32_t* idx, void* stream);
 
 /*
+ * csa2_index_pool_topk - a Reindex layer's indexer in one call (defined by:
+ * fupanwang.com article, section "三个方向一起压小缓存" - a later layer scores
+ * only the first Full layer's candidate pool with its own index query and keeps
+ * its own top 512; dreamax.pages.dev notes, CSA2 paragraph - the Reindex mode).
+ * idx equals csa2_index_pool followed by csa2_topk in the pool layout, bit for
+ * bit, with no pool-score output: each row's pool positions are scored and
+ * ranked in one workgroup, which is faster than the two calls once the rows
+ * give every compute unit a workgroup (about 256 rows and up on MI355X) and
+ * slower below.
+ *   pool_blocks  i32[R][n_pool], 1 <= n_pool <= 2048, ids ascending, -1 padded
+ *                (as csa2_select_blocks writes them)
+ *   idx          i32[R][k]: the first min(k, valid slots) positions by
+ *                (score desc, position asc), ascending, -1 padded; k = 0 writes
+ *                nothing.
+ * Other arguments as csa2_index_pool.  Returns CSA2_OK, CSA2_ERR_INVALID (NULL,
+ * misaligned, B<1, M<1, N_max<1, n_pool outside [1, 2048], k<0), CSA2_ERR_HIP.
+ */
+int csa2_index_pool_topk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                         const uint8_t* k_scales, const int32_t* pool_blocks, int n_pool, const int32_t* n_visible,
+                         int B, int M, int64_t N_max, int k, int32_t* idx, void* stream);
+
+/*
  * csa2_index_full - the whole Full-layer indexer (defined by: fupanwang.com
  * article, section "三个方向一起压小缓存" and its figure caption - the first Full
  * layer scores the whole visible context, builds the pool from the block maxima

@@ -372,6 +372,37 @@ def test_reindex_pool_scores_and_topk(kind):
     assert np.array_equal(f32_bits(ps.cpu().numpy()), f32_bits(ref_ps))
     ref_idx = oracle.topk_pool(ref_ps, pool_np, nv, 512)
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    # the same layer in one call (scores ranked in the scoring workgroup)
+    idx1 = torch.full((w.R, 512), -7, dtype=torch.int32, device="cuda")
+    csa2.csa2_index_pool_topk(l1["q_codes"], l1["q_scales"], c["k_codes"], c["k_scales"], pool, l1["n_visible"],
+                              w.B, 1, w.N, 512, idx1)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx1.cpu().numpy(), ref_idx)
+
+
+@pytest.mark.parametrize("n_pool,k", [(2048, 512), (300, 3000), (1, 5), (2048, 16384)])
+def test_reindex_one_call_edges(n_pool, k):
+    """csa2_index_pool_topk against the oracle's pool scores and top-k: pools
+    with -1 padding and blocks past a row's visible range, k above the valid
+    slots (-1 padding), a one-block pool, a top-k over the whole pool."""
+    w = Workload("reidx1", 4242 + n_pool + k, B=2, M=2, N=30000, n_pool=n_pool, k=k)
+    cache, (lay,) = host_inputs(w)
+    nv = np.array([30000, 29993, 17, 12345], np.int32)
+    lay["n_visible"] = nv
+    rng = np.random.default_rng(n_pool + k)
+    nblk = (w.N + 7) // 8
+    pool_np = np.full((w.R, n_pool), -1, np.int32)
+    for r in range(w.R):
+        m = n_pool if r % 2 == 0 else max(1, n_pool // 3)          # odd rows padded with -1
+        pool_np[r, :m] = np.sort(rng.choice(nblk, size=m, replace=False))   # some blocks past n_visible
+    c, l = dev(cache), dev(lay)
+    idx = torch.full((w.R, k), -7, dtype=torch.int32, device="cuda")
+    csa2.csa2_index_pool_topk(l["q_codes"], l["q_scales"], c["k_codes"], c["k_scales"],
+                              torch.from_numpy(pool_np).cuda(), l["n_visible"], w.B, w.M, w.N, k, idx)
+    torch.cuda.synchronize()
+    ref_ps = oracle.index_pool(lay["q_codes"], lay["q_scales"], cache["k_codes"], cache["k_scales"], pool_np, nv,
+                               w.B, w.M, w.N)
+    assert np.array_equal(idx.cpu().numpy(), oracle.topk_pool(ref_ps, pool_np, nv, k))
 
 
 def _attn_case(w, cache, lay, idx_np, win_max, H=None):
@@ -570,12 +601,13 @@ def test_chain_full_reindex_reindex_reuse():
     assert torch.equal(again, outs[3])
 
 
-@pytest.mark.parametrize("M", [5, 40])
+@pytest.mark.parametrize("M", [5, 40, 130])
 def test_chain_many_queries_per_sequence(M):
     """Full -> Reindex -> Reuse with M causal query rows per sequence: M = 5 is a
     verify step (multi-token decode scan), M = 40 a prefill chunk (the many-query
-    scan); the Reindex layer rescores the Full pool of each row with its own
-    query, the Reuse layer takes the Reindex indices."""
+    scan), M = 130 one whose 260 rows take the one-call Reindex; the Reindex
+    layer rescores the Full pool of each row with its own query, the Reuse
+    layer takes the Reindex indices."""
     N = 20000
     w = Workload("chainM", 97 + M, B=2, N=N, M=M, prefill_base=N - M, layers=("full", "reindex", "reuse"))
     cache, lays = host_inputs(w, layers=3)
