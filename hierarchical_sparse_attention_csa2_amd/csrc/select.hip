@@ -1022,6 +1022,106 @@ __global__ __launch_bounds__(kSelThreads) void select_short_kernel(const float* 
 }
 
 // ---------------------------------------------------------------------------
+// Top-k over a pool's slots (Reindex layers), by the pool lemma: the k best
+// positions of the pool lie in its first kb = min(k, n_pool) blocks ranked by
+// (block maximum desc, block position asc), since every block ranked ahead of a
+// block holding a selected position contributes its own best position ahead of
+// that position.  One workgroup per row ranks the pool's block maxima (taken
+// from the row's slot scores), then the 8 kb slots of its first kb blocks; when
+// kb == k the kb-th block key bounds the k-th position score from below, so
+// slots under it are dropped first.  The result is select_reg_kernel's over
+// every slot.
+// ---------------------------------------------------------------------------
+template <int JT>
+__device__ __forceinline__ void topk_from_pool_blocks(Core& c, Small& s, const int32_t* pidx, int kb,
+                                                      const float* __restrict__ srow,
+                                                      const int32_t* __restrict__ pb, int64_t nv, uint32_t floor,
+                                                      int k, int32_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int cap = 8 * kb;
+  const int Jp = (cap + 1023) >> 10;
+  int32_t pos[JT];
+  uint32_t key[JT];
+#pragma unroll
+  for (int j = 0; j < JT; ++j) {
+    const int i = (w * Jp + j) * 64 + lane;
+    const int32_t pi = (j < Jp && i < cap) ? pidx[i >> 3] : -1;   // pool index of the slot's block
+    const int32_t b = pi >= 0 ? pb[pi] : -1;
+    const int64_t p = 8 * (int64_t)b + (i & 7);
+    pos[j] = (b >= 0 && p < nv) ? (int32_t)p : -1;
+    const float x = pos[j] >= 0 ? srow[8 * pi + (i & 7)] : 0.0f;
+    const uint32_t kk = order_key(x);
+    key[j] = (pos[j] >= 0 && kk >= floor) ? kk : 0u;
+  }
+  hist_zero(c);
+  if (threadIdx.x == 0) {
+    s.cnt[0] = 0;
+    s.cnt[1] = 0;
+  }
+  int valid;
+  uint32_t kmin, kmax;
+  key_range(s, key, Jp, valid, kmin, kmax);
+  Thr th0, th1;
+  select_thresholds(c, s, key, Jp, valid, kmin, kmax, k, 0, 0, th0, th1);
+  emit_sel(
+      s, key, Jp, th0, th1, [&](int, int p, int j, int) { out[p] = pos[j]; }, [&](int, int p) { out[p] = -1; });
+}
+
+// JB: pool blocks per thread (n_pool <= 1024 JB); JT: slots per thread (kb <= 128 JT).
+template <int JB, int JT>
+__global__ __launch_bounds__(kSelThreads) void select_pool_topk_kernel(const float* __restrict__ scores,
+                                                                       const int32_t* __restrict__ pool_blocks,
+                                                                       int n_pool,
+                                                                       const int32_t* __restrict__ n_visible, int k,
+                                                                       int32_t* __restrict__ idx) {
+  __shared__ RegTopkShared sh;
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const float* srow = scores + (int64_t)r * 8 * n_pool;
+  const int32_t* pb = pool_blocks + (int64_t)r * n_pool;
+  int64_t nv = n_visible[r];
+  nv = nv < 0 ? 0 : nv;
+  // block keys, item (w, j, lane) = pool block (w Jp + j) 64 + lane: the
+  // maximum key of its valid slots, 0 when it has none
+  const int Jp = (n_pool + 1023) >> 10;
+  uint32_t bkey[JB];
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int i = (w * Jp + j) * 64 + lane;
+    uint32_t m = 0u;
+    const int32_t b = (j < Jp && i < n_pool) ? pb[i] : -1;
+    if (b >= 0) {
+      // 32-byte aligned: rows of 8 n_pool floats from a 16-byte aligned base
+      const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(srow + 8 * i);
+      const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(srow + 8 * i + 4);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t kk = order_key(t < 4 ? v0[t] : v1[t - 4]);
+        m = (8 * (int64_t)b + t < nv && kk > m) ? kk : m;
+      }
+    }
+    bkey[j] = m;
+  }
+  hist_zero(sh.rs.c);
+  if (threadIdx.x == 0) {
+    sh.rs.s.cnt[0] = 0;
+    sh.rs.s.cnt[1] = 0;
+  }
+  int valid;
+  uint32_t kmin, kmax;
+  key_range(sh.rs.s, bkey, Jp, valid, kmin, kmax);
+  const int kb = k < n_pool ? k : n_pool;
+  Thr th0, th1;
+  select_thresholds(sh.rs.c, sh.rs.s, bkey, Jp, valid, kmin, kmax, 0, kb, 0, th0, th1);
+  const uint32_t floor = (kb == k && th1.keff == kb && valid > kb) ? th1.T : 1u;
+  emit_sel(
+      sh.rs.s, bkey, Jp, th0, th1, [&](int, int p, int, int i) { sh.blk[p] = i; },
+      [&](int, int p) { sh.blk[p] = -1; });
+  __syncthreads();
+  topk_from_pool_blocks<JT>(sh.rs.c, sh.rs.s, sh.blk, kb, srow, pb, nv, floor, k, idx + (int64_t)r * k);
+}
+
+// ---------------------------------------------------------------------------
 // generic selection: the row stays in memory
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSelThreads) void select_mem_kernel(int layout, const float* __restrict__ scores,
@@ -1237,7 +1337,16 @@ hipError_t launch_select(int layout, const float* scores, int64_t stride, const 
     CSA2_REG(J, kSelPool);              \
   else                                  \
     CSA2_REG(J, kSelFull)
-  if (max_n <= 4096) {
+  if (layout == kSelPool && n_pool <= 2048 && out1 && k1 > 0 && !out2 && !floor_in && !floor_out) {
+    // a pool's top-k through its first min(k, n_pool) blocks
+    const int kbk = k1 < n_pool ? k1 : (int)n_pool;
+    if (kbk <= 512)
+      hipLaunchKernelGGL((select_pool_topk_kernel<2, 4>), grid, block, 0, stream, scores, pool_blocks, (int)n_pool,
+                         n_visible, k1, out1);
+    else
+      hipLaunchKernelGGL((select_pool_topk_kernel<2, 16>), grid, block, 0, stream, scores, pool_blocks, (int)n_pool,
+                         n_visible, k1, out1);
+  } else if (max_n <= 4096) {
     CSA2_REG_J(4);
   } else if (max_n <= 8192) {
     CSA2_REG_J(8);
