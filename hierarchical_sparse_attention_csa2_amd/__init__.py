@@ -13,7 +13,7 @@ Full / Reindex / Reuse modes):
     Full    : csa2_index_full (scan -> 8-position block max -> 2048-block pool ->
               top-512) then csa2_sparse_attn
     Reindex : csa2_index_pool over the Full layer's pool -> csa2_topk -> attention
-              (csa2_index_pool_topk, the same in one call, from 256 rows up)
+              (csa2_index_pool_topk, the same in one call, from 1,024 rows up)
     Reuse   : csa2_sparse_attn with the previous layer's indices
 """
 from __future__ import annotations

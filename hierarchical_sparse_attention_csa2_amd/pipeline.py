@@ -23,9 +23,10 @@ from . import (CSA2_OP_INDEX_FULL, CSA2_OP_SPARSE_ATTN, csa2_index_full, csa2_in
 
 FUSED_POOL_BLOCKS = 2048   # pools csa2_index_pool_topk takes (one workgroup scores and ranks a row)
 # Rows from which the one-call Reindex beats index_pool + topk (a 2048-block pool
-# over 266,240 entries: 64 rows 49.6 vs 32.8 us, 256 rows 59.8 vs 66.1 us, 4,096
-# rows 813.5 vs 947.1 us): with fewer rows its workgroups leave compute units idle.
-FUSED_MIN_ROWS = 256
+# over 266,240 entries: 64 rows 50.3 vs 29.6 us, 256 rows 63.7 vs 62.8 us, 1,024
+# rows 211.4 vs 225.2 us, 4,096 rows 812.1 vs 857.7 us): with fewer rows its
+# workgroups leave compute units idle.
+FUSED_MIN_ROWS = 1024
 
 
 @dataclass

@@ -167,9 +167,8 @@ int csa2_topk(const float* scores, const int32_t* pool_blocks, int64_t n_pool, c
  * its own top 512; dreamax.pages.dev notes, CSA2 paragraph - the Reindex mode).
  * idx equals csa2_index_pool followed by csa2_topk in the pool layout, bit for
  * bit, with no pool-score output: each row's pool positions are scored and
- * ranked in one workgroup, which is faster than the two calls once the rows
- * give every compute unit a workgroup (about 256 rows and up on MI355X) and
- * slower below.
+ * ranked in one workgroup, which is faster than the two calls for many rows
+ * (about 1,024 and up on MI355X with a 2048-block pool) and slower for few.
  *   pool_blocks  i32[R][n_pool], 1 <= n_pool <= 2048, ids ascending, -1 padded
  *                (as csa2_select_blocks writes them)
  *   idx          i32[R][k]: the first min(k, valid slots) positions by

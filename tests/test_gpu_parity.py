@@ -601,20 +601,21 @@ def test_chain_full_reindex_reindex_reuse():
     assert torch.equal(again, outs[3])
 
 
-@pytest.mark.parametrize("M", [5, 40, 130])
+@pytest.mark.parametrize("M", [5, 40, 520])
 def test_chain_many_queries_per_sequence(M):
     """Full -> Reindex -> Reuse with M causal query rows per sequence: M = 5 is a
     verify step (multi-token decode scan), M = 40 a prefill chunk (the many-query
-    scan), M = 130 one whose 260 rows take the one-call Reindex; the Reindex
+    scan), M = 520 one whose 1,040 rows take the one-call Reindex; the Reindex
     layer rescores the Full pool of each row with its own query, the Reuse
     layer takes the Reindex indices."""
     N = 20000
-    w = Workload("chainM", 97 + M, B=2, N=N, M=M, prefill_base=N - M, layers=("full", "reindex", "reuse"))
+    w = Workload("chainM", 97 + M, B=2, N=N, M=M, prefill_base=N - M, layers=("full", "reindex", "reuse"),
+                 H=16 if M > 100 else 64)   # 16 heads keep the oracle's attention over 1,040 rows short
     cache, lays = host_inputs(w, layers=3)
     c = dev(cache)
     ls = [dev(d) for d in lays]
     say(f"chain M={M}")
-    st = pipeline.Step(w.layers, w.B, w.M, w.N, win_max=w.win_len)
+    st = pipeline.Step(w.layers, w.B, w.M, w.N, H=w.H, win_max=w.win_len)
     pool, idxs, outs = st.run(pipeline.cache_from(c), [pipeline.layer_from(d) for d in ls])
     torch.cuda.synchronize()
     ref_full = oracle_full(w, cache, lays[0])
